@@ -1,0 +1,194 @@
+"""fp64 CPU oracle for paged decode attention and the paged KV append.
+
+TEST INFRASTRUCTURE ONLY: this package may be imported by ``tests/``, by the
+package's ``smoke()`` check and by the benchmark's CPU-baseline leg, and by
+nothing else.  It shares no code with the HIP library; the only module both
+sides use is the seeded input generator (``workloads``), which holds none of
+the attention arithmetic.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, compiled with
+gcc without fast-math or FMA contraction).  This module only builds that file
+and marshals numpy arrays into it.
+
+Storage convention (identical to the library's documented one, implemented
+independently in ``oracle.c``):
+
+* K cache ``uint16 [num_blocks, num_kv_heads, block_size, head_dim]``
+* V cache ``uint16 [num_blocks, num_kv_heads, head_dim, block_size]``
+* q ``uint16 [num_seqs, num_heads, head_dim]``; k, v ``uint16 [T, num_kv_heads, head_dim]``
+* ``dtype`` 0 = IEEE binary16, 1 = bfloat16 (raw bit patterns).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+F16, BF16 = 0, 1
+_DTYPE = {"f16": F16, "fp16": F16, "float16": F16, "bf16": BF16, "bfloat16": BF16}
+
+ERRORS = {
+    -1: "bad sizes or dtype",
+    -2: "slot out of range or repeated",
+    -3: "block table names a block outside the pool",
+    -4: "context length exceeds the block table's capacity",
+    -5: "normalised weights do not sum to one",
+    -6: "out of memory",
+}
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(src: str = SRC, out: str = LIB) -> str:
+    """Compile oracle.c into liboracle.so (always recompiles)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-o", f"{out}.tmp{os.getpid()}", src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(f"{out}.tmp{os.getpid()}", out)
+    return out
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    override = os.environ.get("PAGED_ORACLE_LIB")  # mutation tests load a planted-mistake build
+    if override:
+        lib = ctypes.CDLL(override)
+    else:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()
+        lib = ctypes.CDLL(LIB)
+    p = ctypes.c_void_p
+    i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f64.restype = dbl
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f64.restype = dbl
+    lib.oracle_kv_write.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i64]
+    lib.oracle_kv_write.restype = i32
+    common = [p, p, p, p, p, dbl, i32, i32, i32, i32, i32, i32, i64, i32]
+    lib.oracle_decode.argtypes = [p] + common
+    lib.oracle_decode.restype = i32
+    lib.oracle_decode_rows.argtypes = [p, p, i32] + common
+    lib.oracle_decode_rows.restype = i32
+    lib.oracle_decode_row_partitioned.argtypes = [p] + common + [i32, i32, i32]
+    lib.oracle_decode_row_partitioned.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise OracleError(f"{what}: {ERRORS.get(rc, rc)}")
+
+
+def dtype_code(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    return _DTYPE[str(dtype)]
+
+
+def f16_to_f64(bits: int) -> float:
+    return _load().oracle_f16_to_f64(int(bits))
+
+
+def bf16_to_f64(bits: int) -> float:
+    return _load().oracle_bf16_to_f64(int(bits))
+
+
+def decode_bits(bits: np.ndarray, dtype) -> np.ndarray:
+    """Element-wise decode of a uint16 array through the oracle's decoders
+    (slow; meant for small arrays in tests)."""
+    fn = f16_to_f64 if dtype_code(dtype) == F16 else bf16_to_f64
+    flat = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
+    return np.array([fn(b) for b in flat], dtype=np.float64).reshape(bits.shape)
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, a.dtype
+    return a
+
+
+def kv_write(k, v, slot_mapping, k_cache, v_cache, block_size: int) -> None:
+    """In-place scatter of k/v [T, Hkv, D] into the caches at slot_mapping."""
+    k, v = _u16(k), _u16(v)
+    slot = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    assert k_cache.dtype == np.uint16 and v_cache.dtype == np.uint16
+    T, hkv, d = k.shape
+    nb = k_cache.shape[0]
+    assert k_cache.shape == (nb, hkv, block_size, d)
+    assert v_cache.shape == (nb, hkv, d, block_size)
+    rc = _load().oracle_kv_write(_ptr(k), _ptr(v), _ptr(slot), _ptr(k_cache),
+                                 _ptr(v_cache), T, hkv, d, block_size, nb)
+    _check(rc, "oracle_kv_write")
+
+
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, scale,
+                 block_size, dtype):
+    q = _u16(q)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    kc, vc = _u16(k_cache), _u16(v_cache)
+    B, hq, d = q.shape
+    nb, hkv = kc.shape[0], kc.shape[1]
+    assert kc.shape == (nb, hkv, block_size, d) and vc.shape == (nb, hkv, d, block_size)
+    assert bt.shape[0] == B and cl.shape == (B,)
+    keep = (q, bt, cl, kc, vc)
+    args = [_ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(cl), float(scale),
+            block_size, hkv, B, hq, d, bt.shape[1], nb, dtype_code(dtype)]
+    return keep, args, (B, hq, d)
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+           dtype) -> np.ndarray:
+    """Full decode attention; returns float64 [B, Hq, D]."""
+    keep, args, (B, hq, d) = _decode_args(q, k_cache, v_cache, block_tables,
+                                          context_lens, scale, block_size, dtype)
+    out = np.zeros((B, hq, d), dtype=np.float64)
+    _check(_load().oracle_decode(_ptr(out), *args), "oracle_decode")
+    del keep
+    return out
+
+
+def decode_rows(rows, q, k_cache, v_cache, block_tables, context_lens, scale,
+                block_size, dtype) -> np.ndarray:
+    """Selected (seq, head) rows; returns float64 [len(rows), D]."""
+    rows = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
+    keep, args, (_, _, d) = _decode_args(q, k_cache, v_cache, block_tables,
+                                         context_lens, scale, block_size, dtype)
+    out = np.zeros((rows.shape[0], d), dtype=np.float64)
+    _check(_load().oracle_decode_rows(_ptr(out), _ptr(rows), rows.shape[0], *args),
+           "oracle_decode_rows")
+    del keep
+    return out
+
+
+def decode_row_partitioned(s, h, part_tokens, q, k_cache, v_cache, block_tables,
+                           context_lens, scale, block_size, dtype) -> np.ndarray:
+    """One row computed partition by partition and merged by log-sum-exp."""
+    keep, args, (_, _, d) = _decode_args(q, k_cache, v_cache, block_tables,
+                                         context_lens, scale, block_size, dtype)
+    out = np.zeros((d,), dtype=np.float64)
+    _check(_load().oracle_decode_row_partitioned(_ptr(out), *args, int(s), int(h),
+                                                 int(part_tokens)),
+           "oracle_decode_row_partitioned")
+    del keep
+    return out

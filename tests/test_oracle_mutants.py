@@ -1,0 +1,88 @@
+"""The oracle's pins catch plausible mistakes (no GPU).
+
+Each case plants one mistake in a copy of oracle/oracle.c (a dropped term, a
+wrong sign, index or layout, a transposed operand), builds it on the CPU into
+a temporary library and runs tests/test_oracle_pins.py against that library
+in a subprocess.  The pin suite must fail for every mutant and pass for the
+unmodified copy.
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+
+# (name, original text, planted text) -- the first occurrence is replaced
+MUTANTS = [
+    ("scale_dropped", "x[t] = scale * dot;", "x[t] = dot;"),
+    ("gqa_modulo", "int kv_head = h / group;", "int kv_head = h % num_kv_heads;"),
+    ("block_index_mod", "int64_t block = table[t / block_size];",
+     "int64_t block = table[(t / block_size) % 2];"),
+    ("max_not_subtracted", "x[t] = exp(x[t] - m);", "x[t] = exp(x[t]);"),
+    ("softmax_sign", "x[t] = exp(x[t] - m);", "x[t] = exp(m - x[t]);"),
+    ("not_normalised", "for (int d = 0; d < head_dim; ++d) out_row[d] /= z;", ""),
+    ("first_token_dropped",
+     "for (int64_t t = 0; t < len; ++t) {\n    int64_t block = table[t / block_size];\n    int offset",
+     "for (int64_t t = 1; t < len; ++t) {\n    int64_t block = table[t / block_size];\n    int offset"),
+    ("v_read_token_major", "return v_cache[base * block_size + offset];",
+     "return v_cache[((block * num_kv_heads + kv_head) * (int64_t)block_size + offset)"
+     " * head_dim + dim];"),
+    ("v_both_token_major",
+     "return v_cache[base * block_size + offset];",
+     "return v_cache[((block * num_kv_heads + kv_head) * (int64_t)block_size + offset)"
+     " * head_dim + dim];"),
+    ("f16_bias", "expo - 25); /* 1.frac", "expo - 24); /* 1.frac"),
+    ("bf16_bias", "expo - 134); /* 1.frac", "expo - 133); /* 1.frac"),
+    ("f16_sign_dropped", "return sign ? -mag : mag;", "return mag;"),
+    ("merge_not_rescaled", "double c = pl[p] * exp(pm[p] - big);", "double c = pl[p];"),
+    ("q_index_transposed", "const uint16_t *qrow = q + ((int64_t)s * num_heads + h) * head_dim;",
+     "const uint16_t *qrow = q + ((int64_t)h * num_seqs + s) * head_dim;"),
+    ("write_offset_shift", "int offset = (int)(slot % block_size);",
+     "int offset = (int)((slot + 1) % block_size);"),
+]
+# the consistent V-layout mutant also moves the write to token-major order
+EXTRA = {
+    "v_both_token_major": ("v_cache[vbase * block_size + offset] = src_v[d];",
+                           "v_cache[((block * num_kv_heads + j) * (int64_t)block_size + offset)"
+                           " * head_dim + d] = src_v[d];"),
+}
+
+
+def _build_variant(tmp, name, old, new):
+    src = open(oracle.SRC).read()
+    if old is not None:
+        assert old in src, name
+        src = src.replace(old, new, 1)
+        if name in EXTRA:
+            o2, n2 = EXTRA[name]
+            assert o2 in src
+            src = src.replace(o2, n2, 1)
+    c = os.path.join(tmp, f"{name}.c")
+    open(c, "w").write(src)
+    return oracle.build(c, os.path.join(tmp, f"lib{name}.so"))
+
+
+def _run_pins(lib):
+    env = dict(os.environ, PAGED_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", PINS, "-x", "-q", "-p",
+                        "no:cacheprovider"], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=600)
+    return r.returncode, r.stdout[-2000:]
+
+
+def test_pins_catch_every_mutant(tmp_path):
+    tmp = str(tmp_path)
+    jobs = [("control", None, None)] + MUTANTS
+    libs = {name: _build_variant(tmp, name, old, new) for name, old, new in jobs}
+    with cf.ThreadPoolExecutor(max_workers=4) as ex:
+        results = dict(zip(libs, ex.map(_run_pins, libs.values())))
+    rc, out = results.pop("control")
+    assert rc == 0, out
+    survivors = [n for n, (rc, _) in results.items() if rc == 0]
+    assert not survivors, f"mutants not caught by the pins: {survivors}"
