@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Paged decode benchmark on one MI355X: KV append + paged decode attention.
+
+One step = one pass of the whole hot path over the workload's batch:
+``paged_kv_write`` of one new token per sequence, then the two launches of
+``paged_attention_decode`` (partition pass, log-sum-exp merge).  Inputs are
+seeded synthetic data resident in HBM before timing starts.  The K/V pool is
+replicated into several copies that the steps rotate through, so a step never
+finds its blocks in L2 / the 256 MB Infinity Cache from the step before.
+
+Prints one JSON line (stdout).  Headline: KV bytes read per second over the
+whole step (2 * Hkv * D * 2 bytes per context token), with the partition
+pass's own rate against HBM peak in "roofline", and the fp64 CPU oracle timed
+on a bounded sample of the same workload in "cpu_baseline".
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "paged decode KV-read HBM GB/s (% of peak) + seq-tokens/s, Llama-3-8B shape"
+HBM_PEAK_GBS = 8000.0
+WORKLOADS = ("llama8b", "long", "prefix", "short_bs8", "short_bs16", "short_bs32", "tiny")
+
+
+def make_workload(name):
+    from pagedattention_kv_cache_paged_amd import workloads as W
+    if name.startswith("short_bs"):
+        return W.short(int(name[len("short_bs"):]))
+    return W.NAMED[name]()
+
+
+def cpu_baseline(w, seconds: float):
+    """The fp64 oracle (single thread) on the first n sequences, all heads;
+    n grows until about `seconds` of work.  Rate in KV GB/s of the same
+    accounting as the GPU figure."""
+    import oracle
+    kc, vc = w.nan_caches()
+    for which in ("hist", "new"):
+        k, v, s = w.write_batch(which)
+        oracle.kv_write(k, v, s, kc, vc, w.block_size)
+    done_tokens, t_total, n = 0, 0.0, 0
+    while n < w.num_seqs and t_total < seconds:
+        rows = np.array([(n, h) for h in range(w.num_heads)], dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.decode_rows(rows, w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                           w.block_size, w.dtype)
+        t_total += time.perf_counter() - t0
+        done_tokens += int(w.context_lens[n])
+        n += 1
+    gbs = done_tokens * w.bytes_per_token / t_total / 1e9
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {w.num_seqs} sequences, all {w.num_heads} query heads "
+                      f"({done_tokens} context tokens), fp64 C oracle, single thread, "
+                      f"{t_total:.1f} s",
+            "seq_tokens_per_s": round(done_tokens / t_total, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b", choices=WORKLOADS)
+    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
+    ap.add_argument("--copies", type=int, default=0, help="pool copies rotated (0 = enough for >1 GB)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU path only: this build has no multi-GPU "
+              "code (the decode shards by sequence or KV head with no exchange); run with "
+              "--gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from pagedattention_kv_cache_paged_amd import binding as B
+    from pagedattention_kv_cache_paged_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = B.load()
+    w = make_workload(args.workload)
+    tdt = {W.F16: torch.float16, W.BF16: torch.bfloat16}[w.dtype]
+
+    def dev_bits(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(tdt)
+
+    ks, vs = w.cache_shapes()
+    pool_bytes = 2 * int(np.prod(ks)) * 2
+    copies = args.copies or max(4, math.ceil(1.1e9 / pool_bytes))
+    nan_i16 = int(np.array([W.NAN_BITS[w.dtype]], np.uint16).view(np.int16)[0])
+    hk, hv, hs = w.write_batch("hist")
+    nk, nv, ns = w.write_batch("new")
+    hk, hv, hs = dev_bits(hk), dev_bits(hv), torch.from_numpy(hs).to(dev)
+    nk, nv, ns = dev_bits(nk), dev_bits(nv), torch.from_numpy(ns).to(dev)
+    caches = []
+    for _ in range(copies):
+        kc = torch.full(ks, nan_i16, dtype=torch.int16, device=dev).view(tdt)
+        vc = torch.full(vs, nan_i16, dtype=torch.int16, device=dev).view(tdt)
+        if hs.numel():
+            B.paged_kv_write(hk, hv, hs, kc, vc)
+        caches.append((kc, vc))
+    del hk, hv, hs
+    q = dev_bits(w.q)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    cl = torch.from_numpy(w.context_lens).to(dev)
+    pt = args.partition or B.default_partition(w.max_blocks_per_seq, w.block_size)
+    ws_need = B.workspace_bytes(w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq,
+                                w.block_size, pt)
+    ws = torch.empty(max(ws_need, 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    # Pre-marshalled C calls: the host stays well ahead of the GPU.
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    dtc = {W.F16: 0, W.BF16: 1}[w.dtype]
+    T = w.num_seqs
+
+    def write(i):
+        kc, vc = caches[i % copies]
+        rc = lib.paged_kv_write(nk.data_ptr(), nv.data_ptr(), ns.data_ptr(), kc.data_ptr(),
+                                vc.data_ptr(), T, w.num_kv_heads, w.head_dim, w.block_size,
+                                w.num_blocks, dtc, sp)
+        assert rc == 0, rc
+
+    def decode(i, stages):
+        kc, vc = caches[i % copies]
+        rc = lib.paged_attention_decode_stages(
+            out.data_ptr(), q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bt.data_ptr(),
+            cl.data_ptr(), w.scale, w.block_size, w.num_kv_heads, w.num_seqs, w.num_heads,
+            w.head_dim, w.max_blocks_per_seq, w.num_blocks, dtc, pt, ws.data_ptr(),
+            ws.numel(), stages, sp)
+        assert rc == 0, rc
+
+    two_pass = ws_need > 0
+    for i in range(args.warmup):
+        write(i)
+        decode(i, 1)
+        decode(i, 2)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        e = ev[i]
+        e[0].record(stream)
+        write(i)
+        e[1].record(stream)
+        decode(i, 1)
+        e[2].record(stream)
+        decode(i, 2)
+        e[3].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(stop) / K
+    t_write = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e3   # us
+    t_part = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    t_merge = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e3 if two_pass else 0.0
+    p_part = np.percentile([e[1].elapsed_time(e[2]) * 1e3 for e in ev], [10, 50, 90])
+
+    kv_bytes = w.logical_tokens * w.bytes_per_token
+    unique_bytes = w.unique_tokens * w.bytes_per_token
+    gbs = kv_bytes / (ms_step * 1e-3) / 1e9
+    achieved = kv_bytes / (t_part * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {W.F16: "f16", W.BF16: "bf16"}[w.dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: batch {w.num_seqs}, {w.num_heads} q / {w.num_kv_heads} kv "
+                        f"heads, head_dim {w.head_dim}, block {w.block_size}, "
+                        f"{w.logical_tokens} context tokens",
+            "batch": w.num_seqs, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": w.dtype,
+            "context_tokens": w.logical_tokens, "partition_tokens": pt,
+            "pool_copies": copies, "pool_mb_per_copy": round(pool_bytes / 2**20, 1),
+        },
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "seq_tokens_per_s": round(w.logical_tokens / (ms_step * 1e-3), 1),
+        "new_tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "kernel_us": {"kv_write": round(t_write, 3), "decode_partition": round(t_part, 3),
+                      "decode_merge": round(t_merge, 3),
+                      "decode_partition_p10_p50_p90": [round(x, 3) for x in p_part]},
+        "host_wall_ms_per_step": round(t_wall * 1e3 / K, 5),
+        "roofline": {
+            "kernel": "decode_partition_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": kv_bytes,
+        },
+    }
+    if unique_bytes != kv_bytes:
+        result["unique_kv_gbs"] = round(unique_bytes / (ms_step * 1e-3) / 1e9, 2)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * paged_attn.h -- C ABI of the MI355X (gfx950) paged decode attention library.
+ *
+ * The problem these calls solve is the paged KV cache of PagedAttention:
+ *
+ *   - "vLLM core architecture overview: PagedAttention, Continuous Batching,
+ *     distributed inference" (5688vip.com), 4.1: the KV cache is cut into
+ *     fixed-size physical blocks (16 tokens by default, 8 or 32 as options);
+ *     a sequence's logically contiguous KV may sit in non-contiguous blocks,
+ *     mapped through a block table; requests may share prefix blocks.
+ *   - "vLLM memory management and continuous batching from the source"
+ *     (developer.cloud.tencent.cn), part 2, 2.1: appending a token writes its
+ *     K/V at its block's address plus the offset inside the block; 2.3:
+ *     attention takes the list of physical block numbers instead of a
+ *     contiguous (batch, seq_len, dim) tensor and gathers K/V through it.
+ *
+ * All buffers are owned by the caller; the library never allocates or frees
+ * memory.  Device pointers are HIP device (or managed) memory of the current
+ * device; `stream` is a hipStream_t passed as void* (NULL = null stream).
+ * Every call validates its arguments on the host before launching anything;
+ * on error nothing is enqueued and no memory is touched.  A return of PA_OK
+ * means the work was enqueued on `stream` (the calls are asynchronous).
+ * The library holds no state and may be called from several threads.
+ *
+ * Element type: q, k, v, both caches and out share one 16-bit type, IEEE
+ * binary16 (PA_F16) or bfloat16 (PA_BF16); arithmetic is fp32.
+ *
+ * Layouts (row-major, contiguous):
+ *   q, out          [num_seqs][num_heads][head_dim]
+ *   k, v (new)      [num_tokens][num_kv_heads][head_dim]
+ *   k_cache         [num_blocks][num_kv_heads][block_size][head_dim]  token-major
+ *   v_cache         [num_blocks][num_kv_heads][head_dim][block_size]  dim-major
+ *   block_tables    int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens    int32 [num_seqs]   (tokens to attend over, the new one included)
+ *   slot_mapping    int64 [num_tokens] slot = block * block_size + offset; < 0 = skip
+ * Query head h reads KV head h / (num_heads / num_kv_heads).
+ *
+ * Supported: head_dim 64 or 128; block_size 8, 16 or 32;
+ * num_heads / num_kv_heads (the GQA group) from 1 to 16.
+ * Alignment: q, k, v and caches 16 bytes, out 8 bytes, workspace 16 bytes.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
+
+enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,      /* a required pointer is NULL */
+  PA_ERR_DTYPE = -2,     /* dtype is not PA_F16 / PA_BF16 */
+  PA_ERR_SHAPE = -3,     /* unsupported or inconsistent size */
+  PA_ERR_WORKSPACE = -4, /* workspace missing or smaller than required */
+  PA_ERR_LAUNCH = -5,    /* the HIP runtime refused a launch */
+  PA_ERR_METADATA = -6,  /* (validator) bad block table, length or slot */
+  PA_ERR_ALIGN = -7      /* a pointer is not aligned as required */
+};
+
+/* Version of this ABI; bumped on any incompatible change. */
+int pa_abi_version(void);
+
+/* Text for a return code (static storage). */
+const char *pa_strerror(int code);
+
+/*
+ * KV append ("...from the source", part 2, 2.1): for every token i with
+ * 0 <= slot_mapping[i] < num_blocks * block_size, copies k[i][j][:] and
+ * v[i][j][:] bit for bit into block slot/block_size, offset
+ * slot%block_size, of KV head j, for every j.  Slots < 0 are padding and
+ * skipped; slots past the pool are skipped too (the kernel never writes
+ * outside the caches).  Slots must be distinct (else which copy lands is
+ * unspecified), and a block shared by several sequences must be copied
+ * before it is written.  k, v are not modified and must not overlap the
+ * caches.  num_tokens == 0 is a no-op.
+ */
+int paged_kv_write(const void *k, const void *v, const int64_t *slot_mapping,
+                   void *k_cache, void *v_cache, int64_t num_tokens,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int64_t num_blocks, int32_t dtype, void *stream);
+
+/*
+ * Partition length used by paged_attention_decode: contexts are split into
+ * partitions of this many tokens, each reduced by one wavefront, and merged
+ * by a log-sum-exp pass when a sequence has more than one.  Depends only on
+ * the table's capacity (max_blocks_per_seq * block_size).
+ */
+int32_t paged_attention_default_partition(int32_t max_blocks_per_seq,
+                                          int32_t block_size);
+
+/*
+ * Bytes of device workspace that paged_attention_decode_ex needs for these
+ * sizes and partition length (0 = the default above).  Zero when every
+ * sequence fits one partition (then workspace may be NULL).
+ * Returns 0 for unsupported sizes as well; the decode call reports those.
+ */
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                       int32_t head_dim, int32_t max_blocks_per_seq,
+                                       int32_t block_size, int32_t partition_tokens);
+
+/*
+ * Decode attention ("...from the source", part 2, 2.3): for each sequence s
+ * and query head h, with L = context_lens[s] and kv head j = h / G,
+ *   out[s][h][:] = sum_t softmax_t(scale * q[s][h] . K_t) * V_t,  t < L,
+ * where token t's K and V live in block block_tables[s][t / block_size] at
+ * offset t % block_size.  L == 0 gives a zero row.  Table entries past
+ * ceil(L / block_size) are never read; neither are unused slots of the last
+ * block.  Writes `out` (same type as q) and the workspace only.
+ * Device-side contract (not checked, results then unspecified, but the
+ * kernels stay inside every buffer): block ids in [0, num_blocks),
+ * 0 <= L <= max_blocks_per_seq * block_size.  paged_validate_metadata
+ * checks these on host copies.
+ * `workspace` must hold paged_attention_workspace_bytes(...) bytes for the
+ * default partition; out must not overlap any input.
+ */
+int paged_attention_decode(void *out, const void *q, const void *k_cache,
+                           const void *v_cache, const int32_t *block_tables,
+                           const int32_t *context_lens, float scale,
+                           int32_t block_size, int32_t num_kv_heads,
+                           int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                           int32_t max_blocks_per_seq, int64_t num_blocks,
+                           int32_t dtype, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * Same as paged_attention_decode with an explicit partition length
+ * (0 = default).  partition_tokens must be a multiple of 16 and of
+ * block_size, and at most 64 * block_size.
+ */
+int paged_attention_decode_ex(void *out, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *block_tables,
+                              const int32_t *context_lens, float scale,
+                              int32_t block_size, int32_t num_kv_heads,
+                              int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                              int32_t max_blocks_per_seq, int64_t num_blocks,
+                              int32_t dtype, int32_t partition_tokens,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * paged_attention_decode_ex split into its two launches, for callers that
+ * schedule or time them separately.  stages: 1 = partition pass only (each
+ * wavefront reduces one partition; single-partition sequences get their
+ * final row in `out`, the others leave partial results in the workspace),
+ * 2 = merge pass only (log-sum-exp combine of the workspace into `out` for
+ * sequences with more than one partition; the partition pass with the same
+ * arguments must have run before it on the same stream), 3 = both, which is
+ * paged_attention_decode_ex.  Other values give PA_ERR_SHAPE.
+ */
+int paged_attention_decode_stages(void *out, const void *q, const void *k_cache,
+                                  const void *v_cache, const int32_t *block_tables,
+                                  const int32_t *context_lens, float scale,
+                                  int32_t block_size, int32_t num_kv_heads,
+                                  int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int64_t num_blocks,
+                                  int32_t dtype, int32_t partition_tokens,
+                                  void *workspace, size_t workspace_bytes, int32_t stages,
+                                  void *stream);
+
+/*
+ * Host-side check of metadata (host pointers): every context length in
+ * [0, max_blocks_per_seq * block_size]; every table entry a sequence reads,
+ * i.e. the first ceil(L / block_size) of its row, in [0, num_blocks); every
+ * non-negative slot below num_blocks * block_size and no slot repeated.
+ * slot_mapping may be NULL (num_tokens ignored).  Returns PA_OK or
+ * PA_ERR_METADATA.  Meant for tests and debugging, not the hot path.
+ */
+int paged_validate_metadata(const int32_t *block_tables, const int32_t *context_lens,
+                            int32_t num_seqs, int32_t max_blocks_per_seq,
+                            int32_t block_size, int64_t num_blocks,
+                            const int64_t *slot_mapping, int64_t num_tokens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,1 +1,17 @@
-"""Paged decode attention and paged KV append for AMD Instinct MI355X (gfx950)."""
+"""Paged decode attention and paged KV append for AMD Instinct MI355X (gfx950).
+
+The compute lives in libpaged_attn.so (C ABI in include/paged_attn.h);
+``binding`` wraps it for torch tensors.  Binding names are imported lazily so
+that the input generator (``workloads``) can be used without torch.
+"""
+_BINDING = ("paged_kv_write", "paged_attention_decode", "default_partition",
+            "workspace_bytes", "validate_metadata", "PagedAttentionError", "load")
+
+__all__ = list(_BINDING)
+
+
+def __getattr__(name):
+    if name in _BINDING:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,208 @@
+"""Thin Python binding of libpaged_attn.so (include/paged_attn.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels.
+PyTorch supplies device memory and the current stream.  torch is imported
+before the library is loaded so that the library binds to the same HIP
+runtime torch uses; the loader checks that only one HIP runtime is mapped.
+There is no CPU fallback: a missing or unloadable library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpaged_attn.so")
+
+PA_F16, PA_BF16 = 0, 1
+PA_OK = 0
+_ERR_SHAPE = {-2, -3, -7}
+
+_DTYPES = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+
+class PagedAttentionError(RuntimeError):
+    """A call into libpaged_attn returned an error code."""
+
+    def __init__(self, fn: str, code: int, text: str):
+        super().__init__(f"{fn}: {text} (code {code})")
+        self.code = code
+
+
+_lib = None
+
+
+def hip_runtimes_mapped():
+    """Paths of every libamdhip64 mapped into this process."""
+    with open("/proc/self/maps") as f:
+        return sorted({line.split()[-1] for line in f if "libamdhip64" in line})
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run "
+                           "`python -m pagedattention_kv_cache_paged_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    runtimes = hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise RuntimeError(f"two HIP runtimes loaded: {runtimes}")
+    p, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                            ctypes.c_float, ctypes.c_size_t)
+    lib.pa_abi_version.restype = ctypes.c_int
+    lib.pa_abi_version.argtypes = []
+    lib.pa_strerror.restype = ctypes.c_char_p
+    lib.pa_strerror.argtypes = [ctypes.c_int]
+    lib.paged_kv_write.restype = ctypes.c_int
+    lib.paged_kv_write.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i64, i32, p]
+    lib.paged_attention_default_partition.restype = i32
+    lib.paged_attention_default_partition.argtypes = [i32, i32]
+    lib.paged_attention_workspace_bytes.restype = sz
+    lib.paged_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    dec = [p, p, p, p, p, p, f32, i32, i32, i32, i32, i32, i32, i64, i32]
+    lib.paged_attention_decode.restype = ctypes.c_int
+    lib.paged_attention_decode.argtypes = dec + [p, sz, p]
+    lib.paged_attention_decode_ex.restype = ctypes.c_int
+    lib.paged_attention_decode_ex.argtypes = dec + [i32, p, sz, p]
+    lib.paged_attention_decode_stages.restype = ctypes.c_int
+    lib.paged_attention_decode_stages.argtypes = dec + [i32, p, sz, i32, p]
+    lib.paged_validate_metadata.restype = ctypes.c_int
+    lib.paged_validate_metadata.argtypes = [p, p, i32, i32, i32, i64, p, i64]
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, code: int):
+    if code != PA_OK:
+        text = load().pa_strerror(code).decode()
+        if code in _ERR_SHAPE:
+            raise ValueError(f"{fn}: {text} (code {code})")
+        raise PagedAttentionError(fn, code, text)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def _dev(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if t.device.type != "cuda" or t.device != dev:
+            raise ValueError("all tensors must be on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return dev
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def default_partition(max_blocks_per_seq: int, block_size: int) -> int:
+    return int(load().paged_attention_default_partition(max_blocks_per_seq, block_size))
+
+
+def workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size,
+                    partition_tokens: int = 0) -> int:
+    return int(load().paged_attention_workspace_bytes(num_seqs, num_heads, head_dim,
+                                                       max_blocks_per_seq, block_size,
+                                                       partition_tokens))
+
+
+_workspaces = {}
+
+
+def workspace(dev, nbytes: int) -> Optional[torch.Tensor]:
+    """A cached uint8 device buffer of at least nbytes (grown on demand)."""
+    if nbytes == 0:
+        return None
+    key = (dev.type, dev.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def paged_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Scatter k, v [T, Hkv, D] into k_cache [N, Hkv, bs, D] and
+    v_cache [N, Hkv, D, bs] at slot_mapping (int64 [T])."""
+    dev = _dev(k, v, slot_mapping, k_cache, v_cache)
+    if k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("k and v must be [num_tokens, num_kv_heads, head_dim]")
+    T, hkv, d = k.shape
+    if k_cache.dim() != 4 or k_cache.shape[1] != hkv or k_cache.shape[3] != d:
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    nb, _, bs, _ = k_cache.shape
+    if tuple(v_cache.shape) != (nb, hkv, d, bs):
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size]")
+    if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (T,):
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    dt = _dtype(k)
+    if v.dtype != k.dtype or k_cache.dtype != k.dtype or v_cache.dtype != k.dtype:
+        raise ValueError("k, v and the caches must share one dtype")
+    rc = load().paged_kv_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                               k_cache.data_ptr(), v_cache.data_ptr(), T, hkv, d, bs, nb,
+                               dt, _stream(dev))
+    _check("paged_kv_write", rc)
+
+
+def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                           v_cache: torch.Tensor, block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, scale: float, block_size: int,
+                           num_kv_heads: int, partition_tokens: int = 0,
+                           stages: int = 3,
+                           workspace_tensor: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[s, h] = softmax(scale * q[s, h] K^T) V over the paged context of
+    sequence s.  q, out [B, Hq, D]; block_tables int32 [B, max_blocks];
+    context_lens int32 [B].  Returns out."""
+    dev = _dev(out, q, k_cache, v_cache, block_tables, context_lens)
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be [num_seqs, num_heads, head_dim]")
+    B, hq, d = q.shape
+    if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (num_kv_heads, block_size, d):
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    nb = k_cache.shape[0]
+    if tuple(v_cache.shape) != (nb, num_kv_heads, d, block_size):
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [num_seqs, max_blocks_per_seq]")
+    if context_lens.dtype != torch.int32 or tuple(context_lens.shape) != (B,):
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    dt = _dtype(q)
+    if out.dtype != q.dtype or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q, out and the caches must share one dtype")
+    mb = block_tables.shape[1]
+    need = workspace_bytes(B, hq, d, mb, block_size, partition_tokens)
+    ws = workspace_tensor if workspace_tensor is not None else workspace(dev, need)
+    ws_ptr = ws.data_ptr() if ws is not None else None
+    ws_len = ws.numel() * ws.element_size() if ws is not None else 0
+    rc = load().paged_attention_decode_stages(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), block_size,
+        num_kv_heads, B, hq, d, mb, nb, dt, partition_tokens, ws_ptr, ws_len, stages,
+        _stream(dev))
+    _check("paged_attention_decode", rc)
+    return out
+
+
+def validate_metadata(block_tables, context_lens, block_size: int, num_blocks: int,
+                      slot_mapping=None) -> int:
+    """Host check of tables, lengths and slots (numpy or CPU tensors);
+    returns the library's code (0 = valid)."""
+    import numpy as np
+    bt = np.ascontiguousarray(np.asarray(block_tables), dtype=np.int32)
+    cl = np.ascontiguousarray(np.asarray(context_lens), dtype=np.int32)
+    sm = None if slot_mapping is None else np.ascontiguousarray(np.asarray(slot_mapping),
+                                                                dtype=np.int64)
+    return int(load().paged_validate_metadata(
+        bt.ctypes.data, cl.ctypes.data, cl.size, bt.shape[1], block_size, num_blocks,
+        None if sm is None else sm.ctypes.data, 0 if sm is None else sm.size))

@@ -1,0 +1,57 @@
+// Internal interface between the C ABI (pa_api.cpp) and the kernel launchers.
+// Arguments have been validated by the caller; launchers only enqueue.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kTile = 16;           // tokens per MFMA tile
+constexpr int kWave = 64;           // gfx950 wavefront
+constexpr int kMaxGroup = 16;       // query heads per KV head served by one wave
+constexpr int kWorkspaceAlign = 256;
+
+struct DecodeArgs {
+  void *out;
+  const void *q;
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  float scale;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t max_blocks_per_seq;
+  int64_t num_blocks;
+  int32_t dtype;
+  int32_t partition_tokens;
+  int32_t max_parts;   // ceil(max_blocks_per_seq * block_size / partition_tokens)
+  float *ws_o;         // [num_seqs][num_heads][max_parts][head_dim] or null
+  float *ws_ml;        // [num_seqs][num_heads][max_parts][2] or null
+  int32_t stages;      // bit 0: partition pass, bit 1: merge pass
+  void *stream;
+};
+
+struct WriteArgs {
+  const void *k;
+  const void *v;
+  const int64_t *slot_mapping;
+  void *k_cache;
+  void *v_cache;
+  int64_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int64_t num_blocks;
+  void *stream;
+};
+
+// Return 0 on success, a nonzero HIP error code otherwise.
+int launch_decode(const DecodeArgs &a);
+int launch_kv_write(const WriteArgs &a);
+
+}  // namespace pa

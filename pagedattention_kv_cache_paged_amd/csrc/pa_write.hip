@@ -1,0 +1,84 @@
+// Paged KV append for gfx950: the write step of "vLLM memory management and
+// continuous batching from the source" (developer.cloud.tencent.cn), part 2,
+// 2.1 -- each new token's K and V go to its block's address plus the offset
+// inside the block.  The slot (block * block_size + offset) is chosen by the
+// caller's block manager; this is a pure bit copy.
+//
+// One workgroup per token.  A K row (head_dim contiguous elements) lands
+// contiguously in the token-major K cache, moved as 16-byte vectors; a V
+// row is spread across the dim-major V cache with a stride of block_size
+// elements, so it is read as 16-byte vectors and stored as 16-bit elements.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int D, int BS>
+__global__ __launch_bounds__(256) void kv_write_kernel(
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int64_t *__restrict__ slot_mapping, uint16_t *__restrict__ k_cache,
+    uint16_t *__restrict__ v_cache, int num_kv_heads, int64_t num_slots) {
+  constexpr int CH = D / 8;  // 16-byte chunks per head row
+  const int64_t tok = blockIdx.x;
+  const int64_t slot = slot_mapping[tok];
+  if (slot < 0 || slot >= num_slots) return;  // padding, or outside the pool
+  const int64_t blk = slot / BS;
+  const int off = (int)(slot % BS);
+  const int nch = num_kv_heads * CH;
+  for (int c = threadIdx.x; c < nch; c += blockDim.x) {
+    const int h = c / CH;
+    const int d0 = (c % CH) * 8;
+    const int64_t src = (tok * num_kv_heads + h) * D + d0;
+    const u32x4 kx = *(const u32x4 *)(k + src);
+    const u32x4 vx = *(const u32x4 *)(v + src);
+    const int64_t bh = blk * num_kv_heads + h;
+    *(u32x4 *)(k_cache + (bh * BS + off) * D + d0) = kx;
+    uint16_t *vd = v_cache + (bh * D + d0) * BS + off;
+    vd[0 * BS] = (uint16_t)(vx.x & 0xffffu);
+    vd[1 * BS] = (uint16_t)(vx.x >> 16);
+    vd[2 * BS] = (uint16_t)(vx.y & 0xffffu);
+    vd[3 * BS] = (uint16_t)(vx.y >> 16);
+    vd[4 * BS] = (uint16_t)(vx.z & 0xffffu);
+    vd[5 * BS] = (uint16_t)(vx.z >> 16);
+    vd[6 * BS] = (uint16_t)(vx.w & 0xffffu);
+    vd[7 * BS] = (uint16_t)(vx.w >> 16);
+  }
+}
+
+template <int D, int BS>
+int launch_typed(const WriteArgs &a) {
+  const int nch = a.num_kv_heads * (D / 8);
+  int threads = (nch + kWave - 1) / kWave * kWave;
+  threads = threads < kWave ? kWave : (threads > 256 ? 256 : threads);
+  kv_write_kernel<D, BS><<<dim3((unsigned)a.num_tokens), threads, 0, (hipStream_t)a.stream>>>(
+      (const uint16_t *)a.k, (const uint16_t *)a.v, a.slot_mapping, (uint16_t *)a.k_cache,
+      (uint16_t *)a.v_cache, a.num_kv_heads, a.num_blocks * BS);
+  return (int)hipGetLastError();
+}
+
+template <int D>
+int launch_bs(const WriteArgs &a) {
+  switch (a.block_size) {
+    case 8: return launch_typed<D, 8>(a);
+    case 16: return launch_typed<D, 16>(a);
+    case 32: return launch_typed<D, 32>(a);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int launch_kv_write(const WriteArgs &a) {
+  switch (a.head_dim) {
+    case 64: return launch_bs<64>(a);
+    case 128: return launch_bs<128>(a);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace pa

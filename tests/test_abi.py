@@ -1,0 +1,170 @@
+"""C-ABI library on the CPU: it loads, exports every function
+include/paged_attn.h declares, and rejects bad arguments on the host
+before anything is launched (no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch  # noqa: F401  (the binding binds to torch's HIP runtime)
+
+from pagedattention_kv_cache_paged_amd import binding as B
+from pagedattention_kv_cache_paged_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+FAKE = 0x100000  # aligned non-null address; never dereferenced in these tests
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    names = declared_functions()
+    assert {"paged_kv_write", "paged_attention_decode", "paged_attention_decode_ex",
+            "paged_attention_decode_stages", "paged_attention_workspace_bytes",
+            "paged_attention_default_partition", "paged_validate_metadata", "pa_strerror",
+            "pa_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.pa_abi_version() == 1
+
+
+def test_single_hip_runtime():
+    B.load()
+    assert len(B.hip_runtimes_mapped()) == 1
+
+
+def test_strerror():
+    lib = B.load()
+    for code in range(-7, 1):
+        assert lib.pa_strerror(code)
+    assert lib.pa_strerror(-99) == b"unknown error"
+
+
+def _decode(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, scale=0.125, bs=16, hkv=8,
+             B=4, hq=32, d=128, mb=128, nb=1000, dtype=1, pt=0, ws=FAKE, wsb=1 << 30,
+             stages=3, stream=None)
+    a.update(kw)
+    return B.load().paged_attention_decode_stages(
+        a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["scale"], a["bs"], a["hkv"],
+        a["B"], a["hq"], a["d"], a["mb"], a["nb"], a["dtype"], a["pt"], a["ws"], a["wsb"],
+        a["stages"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -2),
+    (dict(d=96), -3),
+    (dict(bs=4), -3),
+    (dict(bs=64), -3),
+    (dict(hq=30), -3),               # not a multiple of the KV heads
+    (dict(hq=8 * 32), -3),           # group of 32 > 16
+    (dict(B=-1), -3),
+    (dict(B=70000), -3),
+    (dict(mb=0), -3),
+    (dict(nb=0), -3),
+    (dict(scale=float("nan")), -3),
+    (dict(pt=24), -3),               # not a multiple of 16
+    (dict(pt=40, bs=8), -3),
+    (dict(pt=16 * 64 + 16), -3),     # more blocks than lanes
+    (dict(stages=0), -3),
+    (dict(stages=4), -3),
+    (dict(out=None), -1),
+    (dict(bt=None), -1),
+    (dict(q=FAKE + 8), -7),
+    (dict(out=FAKE + 2), -7),
+    (dict(ws=None), -4),
+    (dict(wsb=1024), -4),
+    (dict(ws=FAKE + 4), -7),
+])
+def test_decode_rejects(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_decode_zero_seqs_is_noop():
+    assert _decode(B=0, out=None, q=None) == 0
+
+
+def _write(**kw):
+    a = dict(k=FAKE, v=FAKE, slots=FAKE, kc=FAKE, vc=FAKE, T=4, hkv=8, d=128, bs=16, nb=100,
+             dtype=0, stream=None)
+    a.update(kw)
+    return B.load().paged_kv_write(a["k"], a["v"], a["slots"], a["kc"], a["vc"], a["T"],
+                                   a["hkv"], a["d"], a["bs"], a["nb"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), -2),
+    (dict(d=80), -3),
+    (dict(bs=12), -3),
+    (dict(T=-1), -3),
+    (dict(T=1 << 31), -3),
+    (dict(hkv=0), -3),
+    (dict(nb=0), -3),
+    (dict(k=None), -1),
+    (dict(vc=None), -1),
+    (dict(v=FAKE + 2), -7),
+    (dict(slots=FAKE + 4), -7),
+])
+def test_write_rejects(kw, code):
+    assert _write(**kw) == code
+
+
+def test_write_zero_tokens_is_noop():
+    assert _write(T=0, k=None) == 0
+
+
+def test_default_partition_and_workspace():
+    assert B.default_partition(7, 16) == 112       # 100-token capacity: one partition
+    assert B.default_partition(64, 8) == 512
+    assert B.default_partition(32, 16) == 512
+    assert B.default_partition(128, 16) == 256
+    assert B.default_partition(2048, 16) == 256
+    assert B.default_partition(16, 32) == 512
+    assert B.workspace_bytes(4, 4, 64, 7, 16) == 0
+    # 64 seqs x 32 heads x 8 partitions x (128 + 2) floats, o-part rounded to 256 B
+    o = 64 * 32 * 8 * 128 * 4
+    assert B.workspace_bytes(64, 32, 128, 128, 16) == o + 64 * 32 * 8 * 2 * 4
+    assert B.workspace_bytes(64, 32, 128, 128, 16, 2048) == 0
+    assert B.workspace_bytes(8, 64, 128, 2048, 16, 512) == 8 * 64 * 64 * 130 * 4
+
+
+def test_validate_metadata():
+    w = W.tiny()
+    k, v, s = w.write_batch("hist")
+    assert B.validate_metadata(w.block_tables, w.context_lens, 16, w.num_blocks, s) == 0
+    bt = w.block_tables.copy()
+    bt[3, 0] = w.num_blocks
+    assert B.validate_metadata(bt, w.context_lens, 16, w.num_blocks) == -6
+    # entries past the used blocks are not checked
+    bt = w.block_tables.copy()
+    bt[0, 5] = -7
+    assert B.validate_metadata(bt, w.context_lens, 16, w.num_blocks) == 0
+    cl = w.context_lens.copy()
+    cl[1] = 7 * 16 + 1
+    assert B.validate_metadata(w.block_tables, cl, 16, w.num_blocks) == -6
+    s2 = s.copy()
+    s2[5] = s2[4]
+    assert B.validate_metadata(w.block_tables, w.context_lens, 16, w.num_blocks, s2) == -6
+    s2 = s.copy()
+    s2[5] = w.num_blocks * 16
+    assert B.validate_metadata(w.block_tables, w.context_lens, 16, w.num_blocks, s2) == -6
+    s2 = s.copy()
+    s2[5] = -1
+    assert B.validate_metadata(w.block_tables, w.context_lens, 16, w.num_blocks, s2) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    q = torch.zeros(2, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        B.paged_attention_decode(q.clone(), q, torch.zeros(4, 2, 16, 64, dtype=torch.float16),
+                                 torch.zeros(4, 2, 64, 16, dtype=torch.float16),
+                                 torch.zeros(2, 1, dtype=torch.int32),
+                                 torch.ones(2, dtype=torch.int32), 0.125, 16, 2)

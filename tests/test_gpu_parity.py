@@ -1,0 +1,317 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+* paged_kv_write: bit-exact over the whole K and V cache buffers (NaN
+  sentinels in every slot not written must survive).
+* paged_attention_decode: |gpu - oracle| <= 2e-3 + 1e-2 * |oracle| element
+  by element (fp16 / bf16 inputs, fp32 accumulation, output rounded to the
+  input type), on the five named workloads (full outputs where the oracle is
+  fast, sampled rows at full size otherwise, in the launch configuration the
+  benchmark uses), on random ragged shapes over every supported head_dim,
+  block size and GQA group, and on the method's invariants.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from pagedattention_kv_cache_paged_amd import binding as B
+from pagedattention_kv_cache_paged_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TD = {W.F16: torch.float16, W.BF16: torch.bfloat16}
+ATOL, RTOL = 2e-3, 1e-2
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def dev_bits(bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(DEV).view(TD[dtype])
+
+
+def host_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f64(bits, dtype):
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dtype == W.F16:
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+class Case:
+    """Device copies of one workload, caches filled through paged_kv_write."""
+
+    def __init__(self, w, with_new=True):
+        self.w = w
+        ks, vs = w.cache_shapes()
+        nan = W.NAN_BITS[w.dtype]
+        as_i16 = np.array([nan], np.uint16).view(np.int16)[0]
+        self.kc = torch.full(ks, int(as_i16), dtype=torch.int16, device=DEV).view(TD[w.dtype])
+        self.vc = torch.full(vs, int(as_i16), dtype=torch.int16, device=DEV).view(TD[w.dtype])
+        self.write("hist")
+        if with_new:
+            self.write("new")
+        self.q = dev_bits(w.q, w.dtype)
+        self.bt = torch.from_numpy(w.block_tables).to(DEV)
+        self.cl = torch.from_numpy(w.context_lens).to(DEV)
+
+    def write(self, which):
+        k, v, s = self.w.write_batch(which)
+        if s.size == 0:
+            return
+        B.paged_kv_write(dev_bits(k, self.w.dtype), dev_bits(v, self.w.dtype),
+                         torch.from_numpy(s).to(DEV), self.kc, self.vc)
+
+    def decode(self, partition_tokens=0, cl=None, bt=None):
+        w = self.w
+        out = torch.empty_like(self.q)
+        B.paged_attention_decode(out, self.q, self.kc, self.vc,
+                                 self.bt if bt is None else bt,
+                                 self.cl if cl is None else cl, w.scale, w.block_size,
+                                 w.num_kv_heads, partition_tokens=partition_tokens)
+        torch.cuda.synchronize()
+        return host_bits(out)
+
+
+def oracle_caches(w, with_new=True):
+    kc, vc = w.nan_caches()
+    for which in (("hist", "new") if with_new else ("hist",)):
+        k, v, s = w.write_batch(which)
+        oracle.kv_write(k, v, s, kc, vc, w.block_size)
+    return kc, vc
+
+
+def check_close(got_bits, ref, dtype, what=""):
+    g = f64(got_bits, dtype)
+    err = np.abs(g - ref)
+    bound = ATOL + RTOL * np.abs(ref)
+    bad = ~(err <= bound)
+    rel = err[np.abs(ref) > 1e-3] / np.abs(ref[np.abs(ref) > 1e-3])
+    say(f"  {what} max_abs={err.max():.3e} max_rel={rel.max() if rel.size else 0:.3e} "
+        f"n={ref.size}")
+    assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, worst " \
+                          f"{err[bad].max():.3e} at {np.argwhere(bad)[:3].tolist()}"
+
+
+# ---- the named workloads --------------------------------------------------------
+
+NAMED = [("tiny", W.tiny), ("short_bs8", lambda: W.short(8)), ("short_bs16", lambda: W.short(16)),
+         ("short_bs32", lambda: W.short(32)), ("llama8b", W.llama8b), ("prefix", W.prefix),
+         ("long", W.long)]
+
+
+@pytest.mark.parametrize("name,make", NAMED, ids=[n for n, _ in NAMED])
+def test_write_bit_exact(name, make):
+    say(f"write {name}")
+    w = make()
+    c = Case(w)
+    torch.cuda.synchronize()
+    kc, vc = oracle_caches(w)
+    assert np.array_equal(host_bits(c.kc), kc)
+    assert np.array_equal(host_bits(c.vc), vc)
+
+
+def _rows_sample(w, n, seed):
+    g = np.random.default_rng(seed)
+    seqs = np.arange(w.num_seqs) if w.num_seqs <= n else np.sort(
+        g.choice(w.num_seqs, n, replace=False))
+    return np.array([(s, int(g.integers(w.num_heads))) for s in seqs], dtype=np.int32)
+
+
+@pytest.mark.parametrize("name,make,full", [
+    ("tiny", W.tiny, True),
+    ("short_bs8", lambda: W.short(8), True),
+    ("short_bs16", lambda: W.short(16), True),
+    ("short_bs32", lambda: W.short(32), True),
+    ("llama8b", W.llama8b, False),
+    ("prefix", W.prefix, False),
+    ("long", W.long, False),
+], ids=["tiny", "short_bs8", "short_bs16", "short_bs32", "llama8b", "prefix", "long"])
+def test_decode_named(name, make, full):
+    w = make()
+    say(f"decode {name} B={w.num_seqs} Hq={w.num_heads} Hkv={w.num_kv_heads} "
+        f"D={w.head_dim} bs={w.block_size} pt={B.default_partition(w.max_blocks_per_seq, w.block_size)}")
+    got = Case(w).decode()
+    kc, vc = oracle_caches(w)
+    assert np.all(np.isfinite(f64(got, w.dtype)))
+    if full:
+        ref = oracle.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                            w.block_size, w.dtype)
+        check_close(got, ref, w.dtype, name)
+    else:
+        rows = _rows_sample(w, 64 if name != "long" else 16, seed=7)
+        ref = oracle.decode_rows(rows, w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                 w.block_size, w.dtype)
+        check_close(got[rows[:, 0], rows[:, 1]], ref, w.dtype, name)
+
+
+# ---- random ragged shapes ------------------------------------------------------------
+
+SHAPES = []
+for i, (G, D, bs, dt) in enumerate([(1, 64, 8, W.F16), (2, 128, 16, W.BF16),
+                                    (4, 64, 32, W.BF16), (8, 128, 8, W.F16),
+                                    (16, 128, 16, W.BF16), (16, 64, 8, W.F16),
+                                    (3, 128, 32, W.F16), (5, 64, 16, W.BF16),
+                                    (8, 128, 32, W.BF16), (1, 128, 16, W.F16)]):
+    SHAPES.append((i, G, D, bs, dt))
+
+
+@pytest.mark.parametrize("i,G,D,bs,dt", SHAPES)
+@pytest.mark.parametrize("pt", [0, 16, 64])
+def test_decode_ragged(i, G, D, bs, dt, pt):
+    if pt and pt % bs:
+        pt = bs * 2
+    g = np.random.default_rng(1000 + i)
+    hkv = int(g.integers(1, 4))
+    lens = np.concatenate([[1, 2, 15, 16, 17, 31, 33], g.integers(1, 700, size=5)])
+    w = W.build(f"rag{i}", lens, num_heads=hkv * G, num_kv_heads=hkv, head_dim=D,
+                block_size=bs, dtype=dt, seed=2000 + i, max_blocks_per_seq=int(math.ceil(700 / bs)) + 2)
+    say(f"ragged {i}: G={G} D={D} bs={bs} {dt} Hkv={hkv} pt={pt}")
+    got = Case(w).decode(partition_tokens=pt)
+    kc, vc = oracle_caches(w)
+    ref = oracle.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, bs, dt)
+    check_close(got, ref, dt, f"ragged{i}")
+
+
+def test_max_partition_and_group():
+    """G = 16 (no padding), a partition of 64 blocks (one per lane) and full
+    block tables."""
+    for bs in (8, 16, 32):
+        w = W.build("max", [64 * bs * 2, 64 * bs * 2 - 5, 1], num_heads=32, num_kv_heads=2,
+                    head_dim=128, block_size=bs, dtype=W.BF16, seed=77,
+                    max_blocks_per_seq=128)
+        say(f"max bs={bs}")
+        got = Case(w).decode(partition_tokens=64 * bs)
+        kc, vc = oracle_caches(w)
+        ref = oracle.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, bs, w.dtype)
+        check_close(got, ref, w.dtype, f"max bs{bs}")
+
+
+# ---- invariants -----------------------------------------------------------------------------
+
+def test_partition_size_invariance():
+    w = W.build("part", [5, 300, 1000, 2048], num_heads=32, num_kv_heads=8, head_dim=128,
+                block_size=16, dtype=W.BF16, seed=88, max_blocks_per_seq=128)
+    c = Case(w)
+    kc, vc = oracle_caches(w)
+    ref = oracle.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, 16, w.dtype)
+    for pt in (16, 48, 128, 256, 512, 1024):
+        say(f"partition {pt}")
+        check_close(c.decode(partition_tokens=pt), ref, w.dtype, f"pt{pt}")
+
+
+def test_placement_permutation_bit_identical():
+    lens = [3, 50, 129, 777]
+    outs = []
+    for ps in (None, 5, 6):
+        w = W.build("perm", lens, num_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                    dtype=W.BF16, seed=31, placement_seed=ps)
+        outs.append(Case(w).decode())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_shared_prefix_equals_private_copies():
+    bs, P = 16, 256
+    w = W.build("pre", [P + 5, P + 40, P + 300], num_heads=32, num_kv_heads=8, head_dim=128,
+                block_size=bs, dtype=W.BF16, seed=51, shared_prefix_tokens=P)
+    shared = Case(w).decode()
+    # the same logical tokens, every sequence in private blocks of its own
+    lens = w.context_lens
+    priv = W.build("priv", lens, num_heads=32, num_kv_heads=8, head_dim=128, block_size=bs,
+                   dtype=W.BF16, seed=52)
+    toks = [w.seq_kv(s) for s in range(w.num_seqs)]
+    priv.token_k = np.concatenate([t[0] for t in toks])
+    priv.token_v = np.concatenate([t[1] for t in toks])
+    priv.q = w.q.copy()
+    assert not np.array_equal(priv.block_tables[:, :P // bs], w.block_tables[:, :P // bs])
+    assert np.array_equal(Case(priv).decode(), shared)
+
+
+def test_block_size_invariance():
+    outs = {}
+    for bs in (8, 16, 32):
+        w = W.build("bsz", [1, 7, 8, 9, 100, 511, 512], num_heads=32, num_kv_heads=8,
+                    head_dim=128, block_size=bs, dtype=W.F16, seed=61,
+                    max_blocks_per_seq=512 // bs)
+        outs[bs] = f64(Case(w).decode(), W.F16)
+    kc, vc = oracle_caches(w)
+    ref = oracle.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, 32, w.dtype)
+    for bs, o in outs.items():
+        err = np.abs(o - ref)
+        assert np.all(err <= ATOL + RTOL * np.abs(ref)), bs
+
+
+def test_length_one_returns_v_and_zero_length():
+    w = W.tiny()
+    c = Case(w)
+    got = f64(c.decode(), w.dtype)
+    _, V = w.seq_kv(0)
+    for h in range(w.num_heads):
+        assert np.array_equal(got[0, h], f64(V[0, h // w.group], w.dtype))
+    cl = c.cl.clone()
+    cl[2] = 0
+    got0 = f64(c.decode(cl=cl), w.dtype)
+    assert np.all(got0[2] == 0) and np.all(np.isfinite(got0))
+
+
+def test_rescale_on_growing_scores():
+    """Scores that keep growing along the context (by ~20 log2 units per
+    tile) force the running-max rescale in every tile, and a huge common
+    offset must not overflow."""
+    D, L = 128, 600
+    w = W.build("grow", [L, L], num_heads=8, num_kv_heads=1, head_dim=D, block_size=16,
+                dtype=W.BF16, seed=71, scale=1.0)
+    g = np.random.default_rng(5)
+    q = np.zeros((2, 8, D), np.float32)
+    q[:, :, 0] = 1.0
+    q[:, :, 1] = g.standard_normal((2, 8)) * 0.1
+    K = g.standard_normal((w.token_k.shape[0], 1, D)).astype(np.float32) * 0.05
+    pos = np.concatenate([np.arange(L), np.arange(L)]).astype(np.float32)
+    K[:, 0, 0] = pos * 0.9 + 200.0   # logits ramp up to ~740
+    w.q = W.to_bits(q, W.BF16)
+    w.token_k = W.to_bits(K, W.BF16)
+    got = Case(w).decode(partition_tokens=256)
+    kc, vc = oracle_caches(w)
+    ref = oracle.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, 16, w.dtype)
+    check_close(got, ref, w.dtype, "grow")
+
+
+def test_write_skips_padding_and_out_of_range():
+    w = W.tiny()
+    c = Case(w, with_new=False)
+    torch.cuda.synchronize()
+    before_k, before_v = host_bits(c.kc), host_bits(c.vc)
+    k, v, s = w.write_batch("new")
+    s = s.copy()
+    s[0] = -1
+    s[2] = w.num_blocks * w.block_size + 3
+    B.paged_kv_write(dev_bits(k, w.dtype), dev_bits(v, w.dtype), torch.from_numpy(s).to(DEV),
+                     c.kc, c.vc)
+    torch.cuda.synchronize()
+    kc, vc = host_bits(c.kc), host_bits(c.vc)
+    # only tokens 1 and 3 landed
+    exp_k, exp_v = before_k.copy(), before_v.copy()
+    for i in (1, 3):
+        b, o = divmod(int(s[i]), w.block_size)
+        exp_k[b, :, o, :] = k[i]
+        exp_v[b, :, :, o] = v[i]
+    assert np.array_equal(kc, exp_k) and np.array_equal(vc, exp_v)
+
+
+def test_workspace_too_small_raises():
+    w = W.build("ws", [600], num_heads=4, num_kv_heads=1, head_dim=64, block_size=16,
+                dtype=W.F16, seed=3)
+    c = Case(w)
+    out = torch.empty_like(c.q)
+    tiny_ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(B.PagedAttentionError):
+        B.paged_attention_decode(out, c.q, c.kc, c.vc, c.bt, c.cl, w.scale, 16, 1,
+                                 partition_tokens=64, workspace_tensor=tiny_ws)
