@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kWave) void decode_partition_kernel(
     if (part == 0 && head_ok) {
       uint16_t *op = out + ((int64_t)seq * num_heads + head) * D + grp * (D / 4);
 #pragma unroll
-      for (int i = 0; i < D / 4; i += 8) *(u32x4 *)(op + i) = u32x4{0, 0, 0, 0};
+      for (int i = 0; i < D / 4; i += 4) *(u32x2 *)(op + i) = u32x2{0, 0};  // out: 8-byte aligned
     }
     return;
   }
