@@ -3,13 +3,13 @@
 
 One step = one pass of the whole hot path over the workload's batch:
 ``paged_kv_write`` of one new token per sequence, then the two launches of
-``paged_attention_decode`` (partition pass, log-sum-exp merge).  Inputs are
+``paged_attention_decode`` (split pass, log-sum-exp merge).  Inputs are
 seeded synthetic data resident in HBM before timing starts.  The K/V pool is
 replicated into several copies that the steps rotate through, so a step never
 finds its blocks in L2 / the 256 MB Infinity Cache from the step before.
 
 Prints one JSON line (stdout).  Headline: KV bytes read per second over the
-whole step (2 * Hkv * D * 2 bytes per context token), with the partition
+whole step (2 * Hkv * D * 2 bytes per context token), with the split
 pass's own rate against HBM peak in "roofline", and the fp64 CPU oracle timed
 on a bounded sample of the same workload in "cpu_baseline".
 """
@@ -30,10 +30,12 @@ HBM_PEAK_GBS = 8000.0
 WORKLOADS = ("llama8b", "long", "prefix", "short_bs8", "short_bs16", "short_bs32", "tiny")
 
 
-def make_workload(name):
+def make_workload(name, placement="random"):
     from pagedattention_kv_cache_paged_amd import workloads as W
     if name.startswith("short_bs"):
         return W.short(int(name[len("short_bs"):]))
+    if name == "llama8b":
+        return W.llama8b(placement=placement)
     return W.NAMED[name]()
 
 
@@ -71,6 +73,8 @@ def main():
     ap.add_argument("--workload", default="llama8b", choices=WORKLOADS)
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--copies", type=int, default=0, help="pool copies rotated (0 = enough for >1 GB)")
+    ap.add_argument("--placement", default="random", choices=("random", "identity"),
+                    help="physical block placement of the llama8b workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -89,7 +93,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = B.load()
-    w = make_workload(args.workload)
+    w = make_workload(args.workload, args.placement)
     tdt = {W.F16: torch.float16, W.BF16: torch.bfloat16}[w.dtype]
 
     def dev_bits(bits):
@@ -115,9 +119,10 @@ def main():
     out = torch.empty_like(q)
     bt = torch.from_numpy(w.block_tables).to(dev)
     cl = torch.from_numpy(w.context_lens).to(dev)
-    pt = args.partition or B.default_partition(w.max_blocks_per_seq, w.block_size)
-    ws_need = B.workspace_bytes(w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq,
-                                w.block_size, pt)
+    pt = args.partition
+    waves = B.split_waves(w.num_seqs, w.num_kv_heads, w.max_blocks_per_seq, w.block_size, pt)
+    ws_need = B.workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                w.max_blocks_per_seq, w.block_size, pt)
     ws = torch.empty(max(ws_need, 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
@@ -143,7 +148,6 @@ def main():
             ws.numel(), stages, sp)
         assert rc == 0, rc
 
-    two_pass = ws_need > 0
     for i in range(args.warmup):
         write(i)
         decode(i, 1)
@@ -171,7 +175,7 @@ def main():
     ms_step = start.elapsed_time(stop) / K
     t_write = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e3   # us
     t_part = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
-    t_merge = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e3 if two_pass else 0.0
+    t_merge = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
     p_part = np.percentile([e[1].elapsed_time(e[2]) * 1e3 for e in ev], [10, 50, 90])
 
     kv_bytes = w.logical_tokens * w.bytes_per_token
@@ -198,17 +202,19 @@ def main():
             "batch": w.num_seqs, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": w.dtype,
             "context_tokens": w.logical_tokens, "partition_tokens": pt,
+            "waves_per_kv_head": waves,
             "pool_copies": copies, "pool_mb_per_copy": round(pool_bytes / 2**20, 1),
+            "placement": args.placement if args.workload == "llama8b" else "random",
         },
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "seq_tokens_per_s": round(w.logical_tokens / (ms_step * 1e-3), 1),
         "new_tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
-        "kernel_us": {"kv_write": round(t_write, 3), "decode_partition": round(t_part, 3),
+        "kernel_us": {"kv_write": round(t_write, 3), "decode_split": round(t_part, 3),
                       "decode_merge": round(t_merge, 3),
-                      "decode_partition_p10_p50_p90": [round(x, 3) for x in p_part]},
+                      "decode_split_p10_p50_p90": [round(x, 3) for x in p_part]},
         "host_wall_ms_per_step": round(t_wall * 1e3 / K, 5),
         "roofline": {
-            "kernel": "decode_partition_kernel",
+            "kernel": "decode_split_kernel",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

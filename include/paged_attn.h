@@ -85,23 +85,32 @@ int paged_kv_write(const void *k, const void *v, const int64_t *slot_mapping,
                    int64_t num_blocks, int32_t dtype, void *stream);
 
 /*
- * Partition length used by paged_attention_decode: contexts are split into
- * partitions of this many tokens, each reduced by one wavefront, and merged
- * by a log-sum-exp pass when a sequence has more than one.  Depends only on
- * the table's capacity (max_blocks_per_seq * block_size).
+ * How paged_attention_decode splits the work.  For each KV head, the
+ * 16-token tiles of all sequences are laid end to end (sequence s owns tiles
+ * cu[s] .. cu[s+1]-1, cu the prefix sum of ceil(context_lens / 16)) and cut
+ * into W equal contiguous ranges, one wavefront each.  A sequence whose
+ * tiles fall into several ranges is finished by a log-sum-exp merge of the
+ * partial results.  W depends only on the sizes below: at least enough that
+ * no range exceeds 64 tiles when every sequence is full, and by default
+ * about 1024 wavefronts in total (one per SIMD of a 256-CU MI355X); with
+ * partition_tokens = P > 0 (a multiple of 16, at most 1024) instead enough
+ * that a range holds at most about P tokens.  Returns W, or 0 for
+ * unsupported sizes.
  */
-int32_t paged_attention_default_partition(int32_t max_blocks_per_seq,
-                                          int32_t block_size);
+int32_t paged_attention_split_waves(int32_t num_seqs, int32_t num_kv_heads,
+                                    int32_t max_blocks_per_seq, int32_t block_size,
+                                    int32_t partition_tokens);
 
 /*
- * Bytes of device workspace that paged_attention_decode_ex needs for these
- * sizes and partition length (0 = the default above).  Zero when every
- * sequence fits one partition (then workspace may be NULL).
- * Returns 0 for unsupported sizes as well; the decode call reports those.
+ * Bytes of device workspace paged_attention_decode_ex needs for these sizes
+ * and partition_tokens (0 = default): partial results for W + num_seqs slots
+ * per query head plus the tile prefix.  Returns 0 for unsupported sizes
+ * (the decode call reports those).
  */
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
-                                       int32_t head_dim, int32_t max_blocks_per_seq,
-                                       int32_t block_size, int32_t partition_tokens);
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t max_blocks_per_seq, int32_t block_size,
+                                       int32_t partition_tokens);
 
 /*
  * Decode attention ("...from the source", part 2, 2.3): for each sequence s
@@ -114,9 +123,10 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  * Device-side contract (not checked, results then unspecified, but the
  * kernels stay inside every buffer): block ids in [0, num_blocks),
  * 0 <= L <= max_blocks_per_seq * block_size.  paged_validate_metadata
- * checks these on host copies.
- * `workspace` must hold paged_attention_workspace_bytes(...) bytes for the
- * default partition; out must not overlap any input.
+ * checks these on host copies.  num_seqs is at most 8192.
+ * `workspace` (16-byte aligned) must hold paged_attention_workspace_bytes
+ * bytes for the default split; out must not overlap any input.  The call
+ * is two launches on `stream`: the split pass, then the merge pass.
  */
 int paged_attention_decode(void *out, const void *q, const void *k_cache,
                            const void *v_cache, const int32_t *block_tables,
@@ -128,9 +138,9 @@ int paged_attention_decode(void *out, const void *q, const void *k_cache,
                            void *stream);
 
 /*
- * Same as paged_attention_decode with an explicit partition length
- * (0 = default).  partition_tokens must be a multiple of 16 and of
- * block_size, and at most 64 * block_size.
+ * Same as paged_attention_decode with an explicit split (partition_tokens
+ * as in paged_attention_split_waves; 0 = default).  The result does not
+ * depend on the split beyond floating-point rounding.
  */
 int paged_attention_decode_ex(void *out, const void *q, const void *k_cache,
                               const void *v_cache, const int32_t *block_tables,
@@ -143,13 +153,14 @@ int paged_attention_decode_ex(void *out, const void *q, const void *k_cache,
 
 /*
  * paged_attention_decode_ex split into its two launches, for callers that
- * schedule or time them separately.  stages: 1 = partition pass only (each
- * wavefront reduces one partition; single-partition sequences get their
- * final row in `out`, the others leave partial results in the workspace),
- * 2 = merge pass only (log-sum-exp combine of the workspace into `out` for
- * sequences with more than one partition; the partition pass with the same
- * arguments must have run before it on the same stream), 3 = both, which is
- * paged_attention_decode_ex.  Other values give PA_ERR_SHAPE.
+ * schedule or time them separately.  stages: 1 = split pass only (each
+ * wavefront reduces its tile range; sequences held by one wavefront get
+ * their final row in `out`, the others leave partial results and the tile
+ * prefix in the workspace), 2 = merge pass only (log-sum-exp combine of the
+ * workspace into `out` for sequences split across wavefronts; the split
+ * pass with the same arguments must have run before it on the same
+ * stream), 3 = both, which is paged_attention_decode_ex.  Other values give
+ * PA_ERR_SHAPE.
  */
 int paged_attention_decode_stages(void *out, const void *q, const void *k_cache,
                                   const void *v_cache, const int32_t *block_tables,

@@ -60,10 +60,10 @@ def load() -> ctypes.CDLL:
     lib.pa_strerror.argtypes = [ctypes.c_int]
     lib.paged_kv_write.restype = ctypes.c_int
     lib.paged_kv_write.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i64, i32, p]
-    lib.paged_attention_default_partition.restype = i32
-    lib.paged_attention_default_partition.argtypes = [i32, i32]
+    lib.paged_attention_split_waves.restype = i32
+    lib.paged_attention_split_waves.argtypes = [i32, i32, i32, i32, i32]
     lib.paged_attention_workspace_bytes.restype = sz
-    lib.paged_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.paged_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     dec = [p, p, p, p, p, p, f32, i32, i32, i32, i32, i32, i32, i64, i32]
     lib.paged_attention_decode.restype = ctypes.c_int
     lib.paged_attention_decode.argtypes = dec + [p, sz, p]
@@ -105,15 +105,18 @@ def _stream(dev) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
-def default_partition(max_blocks_per_seq: int, block_size: int) -> int:
-    return int(load().paged_attention_default_partition(max_blocks_per_seq, block_size))
+def split_waves(num_seqs: int, num_kv_heads: int, max_blocks_per_seq: int, block_size: int,
+                partition_tokens: int = 0) -> int:
+    """Wavefronts per KV head that the decode splits the tiles over."""
+    return int(load().paged_attention_split_waves(num_seqs, num_kv_heads, max_blocks_per_seq,
+                                                  block_size, partition_tokens))
 
 
-def workspace_bytes(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size,
-                    partition_tokens: int = 0) -> int:
-    return int(load().paged_attention_workspace_bytes(num_seqs, num_heads, head_dim,
-                                                       max_blocks_per_seq, block_size,
-                                                       partition_tokens))
+def workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                    block_size, partition_tokens: int = 0) -> int:
+    return int(load().paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads,
+                                                       head_dim, max_blocks_per_seq,
+                                                       block_size, partition_tokens))
 
 
 _workspaces = {}
@@ -181,7 +184,7 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
     if out.dtype != q.dtype or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise ValueError("q, out and the caches must share one dtype")
     mb = block_tables.shape[1]
-    need = workspace_bytes(B, hq, d, mb, block_size, partition_tokens)
+    need = workspace_bytes(B, hq, num_kv_heads, d, mb, block_size, partition_tokens)
     ws = workspace_tensor if workspace_tensor is not None else workspace(dev, need)
     ws_ptr = ws.data_ptr() if ws is not None else None
     ws_len = ws.numel() * ws.element_size() if ws is not None else 0

@@ -11,35 +11,68 @@
 
 namespace {
 
-constexpr int64_t kMaxGrid = 65535;  // bound kept for grid y / z
+constexpr int64_t kMaxGrid = 65535;  // bound on head counts and tokens per grid axis
 
 bool supported_dim(int32_t d) { return d == 64 || d == 128; }
 bool supported_bs(int32_t b) { return b == 8 || b == 16 || b == 32; }
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-bool valid_partition(int32_t pt, int32_t bs) {
-  return pt >= pa::kTile && pt % pa::kTile == 0 && pt % bs == 0 && pt <= pa::kWave * bs;
+bool valid_partition(int32_t pt) {
+  return pt == 0 || (pt >= pa::kTile && pt % pa::kTile == 0 &&
+                     pt <= pa::kMaxTilesPerWave * pa::kTile);
 }
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-int64_t max_parts_of(int32_t max_blocks, int32_t bs, int32_t pt) {
-  const int64_t cap = (int64_t)max_blocks * bs;
-  return (cap + pt - 1) / pt;
+// Upper bound on the 16-token tiles of one KV head over all sequences.
+int64_t tiles_cap(int64_t seqs, int64_t max_blocks, int64_t bs) {
+  return seqs * ((max_blocks * bs + pa::kTile - 1) / pa::kTile);
 }
 
-// Workspace layout: partial outputs fp32 [B][H][P][D], then (m, l) fp32 [B][H][P][2].
-size_t ws_bytes(int64_t seqs, int64_t heads, int64_t dim, int64_t parts) {
-  if (parts <= 1 || seqs <= 0) return 0;
-  const int64_t o = round_up(seqs * heads * parts * dim * 4, pa::kWorkspaceAlign);
-  return (size_t)(o + seqs * heads * parts * 2 * 4);
+// Wavefronts per KV head.  Enough that no wavefront gets more than
+// kMaxTilesPerWave tiles even when every sequence is full; by default about
+// kTargetWaves in total, otherwise enough that a wavefront holds at most
+// partition_tokens tokens.  Never more than there can be tiles.
+int64_t split_waves(int64_t seqs, int64_t kv_heads, int64_t max_blocks, int64_t bs,
+                    int64_t pt) {
+  const int64_t cap = tiles_cap(seqs, max_blocks, bs);
+  if (cap <= 0) return 1;
+  const int64_t w_min = (cap + pa::kMaxTilesPerWave - 1) / pa::kMaxTilesPerWave;
+  int64_t w = pt ? (cap * pa::kTile + pt - 1) / pt
+                 : (pa::kTargetWaves + kv_heads - 1) / kv_heads;
+  w = w < w_min ? w_min : w;
+  return w < cap ? w : cap;
+}
+
+// Workspace layout: partial outputs fp32 [H][slots][D], then (m, l) fp32
+// [H][slots][2], then the tile prefix int32 [seqs + 1]; slots = waves + seqs.
+struct WsLayout {
+  int64_t o, ml, cu, total;
+};
+WsLayout ws_layout(int64_t seqs, int64_t heads, int64_t dim, int64_t waves) {
+  const int64_t slots = waves + seqs;
+  WsLayout l;
+  l.o = 0;
+  l.ml = round_up(heads * slots * dim * 4, pa::kWorkspaceAlign);
+  l.cu = l.ml + round_up(heads * slots * 2 * 4, pa::kWorkspaceAlign);
+  l.total = l.cu + round_up((seqs + 1) * 4, pa::kWorkspaceAlign);
+  return l;
+}
+
+bool decode_sizes_ok(int32_t num_seqs, int32_t num_kv_heads, int32_t num_heads,
+                     int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size) {
+  return num_seqs >= 0 && num_seqs <= pa::kMaxSeqs && num_kv_heads > 0 &&
+         num_kv_heads <= kMaxGrid && num_heads > 0 && num_heads <= kMaxGrid &&
+         num_heads % num_kv_heads == 0 && num_heads / num_kv_heads <= pa::kMaxGroup &&
+         supported_dim(head_dim) && supported_bs(block_size) && max_blocks_per_seq > 0 &&
+         (int64_t)max_blocks_per_seq * block_size <= INT32_MAX / 2;
 }
 
 }  // namespace
 
 extern "C" {
 
-int pa_abi_version(void) { return 1; }
+int pa_abi_version(void) { return 2; }
 
 const char *pa_strerror(int code) {
   switch (code) {
@@ -55,24 +88,29 @@ const char *pa_strerror(int code) {
   return "unknown error";
 }
 
-int32_t paged_attention_default_partition(int32_t max_blocks_per_seq, int32_t block_size) {
-  if (!supported_bs(block_size) || max_blocks_per_seq <= 0) return 0;
-  const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
-  const int64_t unit = block_size > pa::kTile ? block_size : pa::kTile;
-  if (cap <= 512) return (int32_t)round_up(cap, unit);  // whole context in one partition
-  return 256;
+int32_t paged_attention_split_waves(int32_t num_seqs, int32_t num_kv_heads,
+                                    int32_t max_blocks_per_seq, int32_t block_size,
+                                    int32_t partition_tokens) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+      !supported_bs(block_size) || !valid_partition(partition_tokens))
+    return 0;
+  const int64_t w = split_waves(num_seqs, num_kv_heads, max_blocks_per_seq, block_size,
+                                partition_tokens);
+  return w * num_kv_heads > INT32_MAX ? 0 : (int32_t)w;
 }
 
-size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
                                        int32_t max_blocks_per_seq, int32_t block_size,
                                        int32_t partition_tokens) {
-  if (num_seqs <= 0 || num_heads <= 0 || !supported_dim(head_dim) || !supported_bs(block_size) ||
-      max_blocks_per_seq <= 0)
+  if (num_seqs <= 0 ||
+      !decode_sizes_ok(num_seqs, num_kv_heads, num_heads, head_dim, max_blocks_per_seq,
+                       block_size) ||
+      !valid_partition(partition_tokens))
     return 0;
-  int32_t pt = partition_tokens ? partition_tokens
-                                : paged_attention_default_partition(max_blocks_per_seq, block_size);
-  if (!valid_partition(pt, block_size)) return 0;
-  return ws_bytes(num_seqs, num_heads, head_dim, max_parts_of(max_blocks_per_seq, block_size, pt));
+  const int64_t w = split_waves(num_seqs, num_kv_heads, max_blocks_per_seq, block_size,
+                                partition_tokens);
+  return (size_t)ws_layout(num_seqs, num_heads, head_dim, w).total;
 }
 
 int paged_kv_write(const void *k, const void *v, const int64_t *slot_mapping, void *k_cache,
@@ -103,36 +141,28 @@ int paged_attention_decode_stages(void *out, const void *q, const void *k_cache,
                                   void *stream) {
   if (dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_DTYPE;
   if (stages < 1 || stages > 3) return PA_ERR_SHAPE;
-  if (num_seqs < 0 || num_seqs > kMaxGrid || num_kv_heads <= 0 || num_kv_heads > kMaxGrid ||
-      num_heads <= 0 || num_heads > kMaxGrid || num_heads % num_kv_heads != 0 ||
-      num_heads / num_kv_heads > pa::kMaxGroup || !supported_dim(head_dim) ||
-      !supported_bs(block_size) || max_blocks_per_seq <= 0 ||
-      (int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2 || num_blocks <= 0 ||
-      num_blocks > INT32_MAX || !std::isfinite(scale))
+  if (!decode_sizes_ok(num_seqs, num_kv_heads, num_heads, head_dim, max_blocks_per_seq,
+                       block_size) ||
+      num_blocks <= 0 || num_blocks > INT32_MAX || !std::isfinite(scale) ||
+      !valid_partition(partition_tokens))
     return PA_ERR_SHAPE;
-  const int32_t pt = partition_tokens
-                         ? partition_tokens
-                         : paged_attention_default_partition(max_blocks_per_seq, block_size);
-  if (!valid_partition(pt, block_size)) return PA_ERR_SHAPE;
-  const int64_t parts = max_parts_of(max_blocks_per_seq, block_size, pt);
   if (num_seqs == 0) return PA_OK;
+  const int64_t waves = split_waves(num_seqs, num_kv_heads, max_blocks_per_seq, block_size,
+                                    partition_tokens);
+  if (waves * num_kv_heads > INT32_MAX || waves + num_seqs > INT32_MAX) return PA_ERR_SHAPE;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 8) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PA_ERR_ALIGN;
-  const size_t need = ws_bytes(num_seqs, num_heads, head_dim, parts);
-  float *ws_o = nullptr, *ws_ml = nullptr;
-  if (need) {
-    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
-    ws_o = static_cast<float *>(workspace);
-    ws_ml = reinterpret_cast<float *>(
-        static_cast<char *>(workspace) +
-        round_up((int64_t)num_seqs * num_heads * parts * head_dim * 4, pa::kWorkspaceAlign));
-  }
+  const WsLayout l = ws_layout(num_seqs, num_heads, head_dim, waves);
+  if (!workspace || workspace_bytes < (size_t)l.total) return PA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
+  char *ws = static_cast<char *>(workspace);
   pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                    num_kv_heads, num_seqs, num_heads, head_dim, max_blocks_per_seq, num_blocks,
-                   dtype, pt, (int32_t)parts, ws_o, ws_ml, stages, stream};
+                   dtype, (int32_t)waves, (int32_t)(waves + num_seqs),
+                   reinterpret_cast<float *>(ws + l.o), reinterpret_cast<float *>(ws + l.ml),
+                   reinterpret_cast<int32_t *>(ws + l.cu), stages, stream};
   return pa::launch_decode(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
 }
 

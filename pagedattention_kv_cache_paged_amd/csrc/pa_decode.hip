@@ -1,14 +1,24 @@
-// Paged decode attention for gfx950 (CDNA4): one wavefront per
-// (sequence, KV head, context partition), serving every query head of the
-// KV head's GQA group so each K/V block is read from HBM once.
+// Paged decode attention for gfx950 (CDNA4).
 //
 // Method: "vLLM memory management and continuous batching from the source"
 // (developer.cloud.tencent.cn), part 2, 2.3 -- attention receives block
 // tables instead of a contiguous (batch, seq_len, dim) tensor and gathers
 // K/V through them; 2.1 -- a token lives in block table[t / block_size] at
-// offset t % block_size.  The math is plain softmax(scale * q K^T) V,
-// computed with a running max and sum over 16-token tiles and, for contexts
-// longer than one partition, merged across partitions by log-sum-exp.
+// offset t % block_size.  The math is plain softmax(scale * q K^T) V per
+// query head, computed with a running max and sum over 16-token tiles; a
+// sequence split across several wavefronts is merged by log-sum-exp.
+//
+// Work split ("flat split-K").  For one KV head, the 16-token tiles of all
+// sequences are laid end to end (sequence s owns tiles cu[s] .. cu[s+1]-1)
+// and cut into `waves` equal contiguous ranges, one wavefront each, so every
+// wavefront streams the same number of bytes whatever the length mix.  A
+// range may end inside one sequence and start inside another: the wavefront
+// then produces one partial result (m, l, o) per sequence segment, in slot
+// (wave + sequence) of the workspace, and the merge pass combines the
+// partials of each sequence.  A sequence held entirely by one wavefront is
+// written to `out` directly.  Wavefront (kv head h, range j) is workgroup
+// j * num_kv_heads + h: workgroups go to the eight XCDs round-robin in
+// launch order, so with kv head fastest each XCD streams an equal share.
 //
 // Per 16-token tile, with G <= 16 query heads padded to 16:
 //   S^T[16 tok x 16 head] = K[16 tok x D] * Q^T[D x 16 head]
@@ -26,8 +36,6 @@
 // final sum cross the wave's four 16-lane rows (permlane16/32 swaps).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-
-#include <type_traits>
 
 #include "pa_internal.h"
 
@@ -118,122 +126,195 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-// K and V registers of one 16-token tile.
+
+// Inclusive prefix sum over the wave's 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Wavefront whose range [j*n/w, (j+1)*n/w) holds flat tile tau (0 <= tau < n,
+// 1 <= w <= n, so that no range is empty).
+__device__ __forceinline__ int wave_of(int tau, int n, int w) {
+  return (int)((((int64_t)tau + 1) * w - 1) / n);
+}
+
+// Query, K and V registers of one 16-token tile.
 template <int D>
 struct Frag {
+  u32x4 q[D / 32];
   u32x4 k[D / 32];
   u32x2 v[D / 16];
 };
 
+// Tiles in flight per wave (register ring depth).
+constexpr int kBuf = 2;
+
 template <int DT, int D, int BS>
-__global__ __launch_bounds__(kWave) void decode_partition_kernel(
+__global__ __launch_bounds__(kWave) void decode_split_kernel(
     uint16_t *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml,
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
-    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
-    const int32_t *__restrict__ context_lens, float scale_log2, int num_kv_heads,
-    int num_heads, int group, int max_blocks, int64_t num_blocks, int max_parts,
-    int part_tokens) {
+    int32_t *__restrict__ ws_cu, const uint16_t *__restrict__ q,
+    const uint16_t *__restrict__ k_cache, const uint16_t *__restrict__ v_cache,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
+    float scale_log2, int num_seqs, int num_kv_heads, int num_heads, int group,
+    int max_blocks, int64_t num_blocks, int waves, int slots) {
   using E = Elem<DT>;
   constexpr int KSTEPS = D / 32;  // 16x16x32 MFMAs per QK tile
   constexpr int DTILES = D / 16;  // 16x16x16 MFMAs per PV tile
+  extern __shared__ int lds[];    // cu[num_seqs + 1], then lens[num_seqs]
+  int *cu = lds;
+  int *lens = lds + num_seqs + 1;
 
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int seq = blockIdx.z;
+  const int kvh = blockIdx.x % num_kv_heads;
+  const int j = blockIdx.x / num_kv_heads;
   const int lane = threadIdx.x;
   const int row = lane & 15;  // A-row / B-column / head index inside a tile
   const int grp = lane >> 4;  // quarter of the wave: k-slice and 4-row group
+  const int max_len = max_blocks * BS;
 
-  int len = context_lens[seq];
-  len = len < 0 ? 0 : (len > max_blocks * BS ? max_blocks * BS : len);
-  const int nparts = (len + part_tokens - 1) / part_tokens;
-  const int head = kvh * group + row;
-  const bool head_ok = row < group;
-
-  if (len == 0) {
-    if (part == 0 && head_ok) {
-      uint16_t *op = out + ((int64_t)seq * num_heads + head) * D + grp * (D / 4);
-#pragma unroll
-      for (int i = 0; i < D / 4; i += 4) *(u32x2 *)(op + i) = u32x2{0, 0};  // out: 8-byte aligned
+  // Tile prefix over all sequences (the same in every wavefront).  Range-0
+  // wavefronts also write the zero rows of sequences with nothing to attend.
+  int carry = 0;
+  for (int c = 0; c < num_seqs; c += kWave) {
+    const int s = c + lane;
+    int len = s < num_seqs ? context_lens[s] : 0;
+    len = min(max(len, 0), max_len);
+    const int incl = wave_incl_scan((len + kTile - 1) / kTile) + carry;
+    if (s < num_seqs) {
+      cu[s + 1] = incl;
+      lens[s] = len;
     }
-    return;
+    carry = __shfl(incl, kWave - 1);
+    if (j == 0) {
+      uint64_t zero = __ballot(s < num_seqs && len == 0);
+      while (zero) {
+        const int zs = c + __builtin_ctzll(zero);
+        zero &= zero - 1;
+        uint16_t *op = out + ((int64_t)zs * num_heads + kvh * group) * D;
+        for (int e = lane * 4; e < group * D; e += kWave * 4) *(u32x2 *)(op + e) = u32x2{0, 0};
+      }
+    }
   }
-  if (part >= nparts) return;
+  if (lane == 0) cu[0] = 0;
+  __syncthreads();
+  const int n_tiles = carry;
+  if (kvh == 0 && j == 0)  // for the merge pass
+    for (int s = lane; s <= num_seqs; s += kWave) ws_cu[s] = cu[s];
 
-  const int t_begin = part * part_tokens;
-  const int ntok = min(len - t_begin, part_tokens);
-  const int nblk = (ntok + BS - 1) / BS;
+  // With fewer tiles than wavefronts only the first n_tiles take part, so
+  // that every range is non-empty (the merge pass relies on it).
+  const int wv = min(waves, n_tiles);
+  if (j >= wv) return;
+  const int t0 = (int)((int64_t)j * n_tiles / wv);
+  const int t1 = (int)((int64_t)(j + 1) * n_tiles / wv);
+  const int cnt = t1 - t0;  // 1 .. 64: the host makes waves >= tiles / 64
 
-  // Block numbers of this partition, one per lane (never past the sequence's
-  // last block; ids outside the pool are replaced so no access leaves it).
-  int bid = 0;
-  if (lane < nblk) {
-    const int b = block_tables[(int64_t)seq * max_blocks + t_begin / BS + lane];
-    bid = (b >= 0 && b < num_blocks) ? b : 0;
+  // Lane l describes flat tile t0 + l (lanes past the range repeat the last
+  // one and are never read): its sequence, tile index in that sequence,
+  // valid tokens, block ids, and whether a sequence segment ends there.
+  const int tau = t0 + min(lane, cnt - 1);
+  int lo = 0, hi = num_seqs - 1;  // the largest s with cu[s] <= tau
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= tau) lo = mid;
+    else hi = mid - 1;
   }
-
-  // Query fragment: lane (row, grp) holds q[head row][32*ks + 8*grp .. +8].
-  u32x4 qf[KSTEPS];
-  {
-    const uint16_t *qp = q + ((int64_t)seq * num_heads + head) * D + grp * 8;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      qf[ks] = head_ok ? *(const u32x4 *)(qp + ks * 32) : u32x4{0, 0, 0, 0};
+  const int sq = lo;
+  const int first = cu[sq];
+  const int ntiles_sq = cu[sq + 1] - first;
+  const int it = tau - first;
+  const int nvalid = min(kTile, lens[sq] - it * kTile);  // >= 1
+  const int32_t *tbl = block_tables + (int64_t)sq * max_blocks;
+  int b0, b1 = 0, boff = 0;
+  if constexpr (BS == 8) {  // two blocks per tile
+    b0 = tbl[2 * it];
+    b1 = nvalid > 8 ? tbl[2 * it + 1] : b0;
+  } else if constexpr (BS == 16) {
+    b0 = tbl[it];
+  } else {  // half a block per tile
+    b0 = tbl[it >> 1];
+    boff = (it & 1) * kTile;
   }
+  b0 = (b0 >= 0 && b0 < num_blocks) ? b0 : 0;  // ids outside the pool: stay inside it
+  b1 = (b1 >= 0 && b1 < num_blocks) ? b1 : 0;
+  const int seg_end = (it == ntiles_sq - 1 || tau == t1 - 1) ? 1 : 0;
+  const int whole = (first >= t0 && first + ntiles_sq <= t1) ? 1 : 0;
 
+  // Padded head lanes (row >= group) read a real query row and compute
+  // values that are never stored.
+  const int qh = kvh * group + min(row, group - 1);
   const int64_t blk_stride = (int64_t)num_kv_heads * BS * D;  // elements per block
   const uint16_t *kbase = k_cache + (int64_t)kvh * BS * D;
   const uint16_t *vbase = v_cache + (int64_t)kvh * D * BS;
 
-  // Loads of one tile, straight-line (no branch around them, so the wait for
-  // the current tile does not also wait for the prefetched one).  Token
-  // indices are clamped into the partition; what a clamped lane reads is
-  // masked away in the last tile.
-  auto load = [&](Frag<D> &f, int tile) {
-    const int ktok = min(tile * kTile + row, ntok - 1);
-    const int vtok = min(tile * kTile + grp * 4, (ntok - 1) & ~3);
-    int kb, vb;
-    if constexpr (BS == 8) {  // two blocks per tile
-      kb = __builtin_amdgcn_ds_bpermute((ktok / BS) << 2, bid);
-      vb = __builtin_amdgcn_ds_bpermute((vtok / BS) << 2, bid);
+  // Loads of one tile (idx = position in the range, < cnt), straight-line:
+  // no branch around them, so the wait for one tile never waits for the
+  // prefetched ones.  Token indices are clamped to the tile's valid tokens;
+  // what a clamped lane reads is masked away by step().  K and V are read
+  // once per launch, so they bypass the caches' normal replacement.
+  auto load = [&](Frag<D> &f, int idx) {
+    const int n = __builtin_amdgcn_readlane(nvalid, idx);
+    const int s = __builtin_amdgcn_readlane(sq, idx);
+    const int ka = __builtin_amdgcn_readlane(b0, idx);
+    const int ktok = min(row, n - 1);
+    const int vtok = min(grp * 4, (n - 1) & ~3);
+    int kb, vb, koff, voff;
+    if constexpr (BS == 8) {
+      const int kz = __builtin_amdgcn_readlane(b1, idx);
+      kb = ktok < 8 ? ka : kz;
+      koff = ktok & 7;
+      vb = vtok < 8 ? ka : kz;
+      voff = vtok & 7;
+    } else if constexpr (BS == 16) {
+      kb = vb = ka;
+      koff = ktok;
+      voff = vtok;
     } else {
-      kb = vb = __builtin_amdgcn_readlane(bid, tile * kTile / BS);
+      const int o = __builtin_amdgcn_readlane(boff, idx);
+      kb = vb = ka;
+      koff = o + ktok;
+      voff = o + vtok;
     }
-    const uint16_t *kp = kbase + (int64_t)kb * blk_stride + (ktok % BS) * D + grp * 8;
+    const uint16_t *qp = q + ((int64_t)s * num_heads + qh) * D + grp * 8;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) f.k[ks] = *(const u32x4 *)(kp + ks * 32);
-    const uint16_t *vp = vbase + (int64_t)vb * blk_stride + row * BS + (vtok % BS);
+    for (int ks = 0; ks < KSTEPS; ++ks) f.q[ks] = *(const u32x4 *)(qp + ks * 32);
+    const uint16_t *kp = kbase + (int64_t)kb * blk_stride + koff * D + grp * 8;
 #pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) f.v[dt] = *(const u32x2 *)(vp + dt * 16 * BS);
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      f.k[ks] = __builtin_nontemporal_load((const u32x4 *)(kp + ks * 32));
+    const uint16_t *vp = vbase + (int64_t)vb * blk_stride + row * BS + voff;
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt)
+      f.v[dt] = __builtin_nontemporal_load((const u32x2 *)(vp + dt * 16 * BS));
   };
 
-  // Running max per head in log2 units.  The accumulators are rescaled only
-  // when some head's max has grown by more than 2^kSlack; in between, the
-  // weights exp2(s - m_ref) may exceed one by at most that factor, which
-  // fp32 sums and the 16-bit weights carry without loss of relative
-  // precision.
-  constexpr float kSlack = 8.0f;
+  // Running max per head in log2 units; reset at each sequence segment.
   float m_ref = -INFINITY;
   float l_run = 0.f;  // this lane's share of the running sum
   f32x4 acc[DTILES];
 #pragma unroll
   for (int dt = 0; dt < DTILES; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](Frag<D> &f, int tile, auto last_tag) {
-    constexpr bool kLast = decltype(last_tag)::value;
+  // One tile of scores, softmax update and P.V; at the end of a sequence
+  // segment, the segment's result goes out and the state is reset.  Tokens
+  // at or past the tile's valid count get weight zero and their V entries
+  // are zeroed (unused slots may hold anything, NaN included).
+  auto step = [&](Frag<D> &f, int idx) {
+    const int n = __builtin_amdgcn_readlane(nvalid, idx);
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) sc = E::qk(f.k[ks], qf[ks], sc);
-    const int tb = tile * kTile + grp * 4;  // this lane's first token of the four
+    for (int ks = 0; ks < KSTEPS; ++ks) sc = E::qk(f.k[ks], f.q[ks], sc);
     float s[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s[r] = sc[r] * scale_log2;
-      if constexpr (kLast) s[r] = (tb + r < ntok) ? s[r] : -INFINITY;
-    }
+    for (int r = 0; r < 4; ++r) s[r] = (grp * 4 + r < n) ? sc[r] * scale_log2 : -INFINITY;
     const float mx = rows_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
-    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kSlack) != 0) {
-      const float m_new = fmaxf(m_ref, mx);
+    {  // rescale unconditionally: a branch here costs more than the multiplies
+      const float m_new = fmaxf(m_ref, mx);  // finite: every tile has a valid token
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -255,16 +336,14 @@ __global__ __launch_bounds__(kWave) void decode_partition_kernel(
       // the sum uses the rounded weights the MFMA multiplies with
       l_run += (E::lo(ph.x) + E::hi(ph.x)) + (E::lo(ph.y) + E::hi(ph.y));
     }
-    if constexpr (kLast) {  // ragged tail: zero V of tokens past the end (may hold NaN)
-      const int c = ntok - tb;
-      if (c < 4) {
-        const uint32_t w0 = c >= 2 ? 0xffffffffu : (c == 1 ? 0x0000ffffu : 0u);
-        const uint32_t w1 = c == 3 ? 0x0000ffffu : 0u;
+    {
+      const int c = n - grp * 4;
+      const uint32_t w0 = c >= 2 ? 0xffffffffu : (c == 1 ? 0x0000ffffu : 0u);
+      const uint32_t w1 = c >= 4 ? 0xffffffffu : (c == 3 ? 0x0000ffffu : 0u);
 #pragma unroll
-        for (int dt = 0; dt < DTILES; ++dt) {
-          f.v[dt].x &= w0;
-          f.v[dt].y &= w1;
-        }
+      for (int dt = 0; dt < DTILES; ++dt) {
+        f.v[dt].x &= w0;
+        f.v[dt].y &= w1;
       }
     }
 #pragma unroll
@@ -272,73 +351,86 @@ __global__ __launch_bounds__(kWave) void decode_partition_kernel(
       acc[dt] = E::pv(f.v[dt], ph, acc[dt]);
       if constexpr (E::kSplitP) acc[dt] = E::pv(f.v[dt], pl, acc[dt]);
     }
+    if (__builtin_amdgcn_readlane(seg_end, idx)) {
+      const float l_tot = rows_sum(l_run);
+      const int sqn = __builtin_amdgcn_readlane(sq, idx);
+      if (row < group) {
+        const int head = kvh * group + row;
+        const float inv = 1.0f / l_tot;
+        if (__builtin_amdgcn_readlane(whole, idx)) {
+          // lane (row, grp) holds dims 16*dt + 4*grp + 0..3 of head row
+          uint16_t *op = out + ((int64_t)sqn * num_heads + head) * D + grp * 4;
+#pragma unroll
+          for (int dt = 0; dt < DTILES; ++dt) {
+            u32x2 w;
+            w.x = E::pack(acc[dt][0] * inv, acc[dt][1] * inv);
+            w.y = E::pack(acc[dt][2] * inv, acc[dt][3] * inv);
+            *(u32x2 *)(op + dt * 16) = w;
+          }
+        } else {
+          const int64_t slot = (int64_t)head * slots + j + sqn;
+          float *op = ws_o + slot * D + grp * 4;
+#pragma unroll
+          for (int dt = 0; dt < DTILES; ++dt) *(f32x4 *)(op + dt * 16) = acc[dt] * inv;
+          if (grp == 0) *(f32x2 *)(ws_ml + slot * 2) = f32x2{m_ref, l_tot};
+        }
+      }
+      m_ref = -INFINITY;
+      l_run = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   };
 
-  // Ping-pong over two register sets: the next tile's loads are in flight
-  // while the current one is computed, and no register copy waits on them.
-  const int ntiles = (ntok + kTile - 1) / kTile;
-  Frag<D> fa, fb;
-  load(fa, 0);
-  int tile = 0;
-  for (; tile + 2 < ntiles; tile += 2) {
-    load(fb, tile + 1);
-    step(fa, tile, std::false_type{});
-    load(fa, tile + 2);
-    step(fb, tile + 1, std::false_type{});
-  }
-  if (tile + 1 < ntiles) {
-    load(fb, tile + 1);
-    step(fa, tile, std::false_type{});
-    step(fb, tile + 1, std::true_type{});
-  } else {
-    step(fa, tile, std::true_type{});
-  }
-  const float m_run = m_ref;
-
-  const float l_tot = rows_sum(l_run);
-  if (!head_ok) return;
-  const float inv = 1.0f / l_tot;
-
-  if (nparts == 1) {
-    // lane (row, grp) holds dims 16*dt + 4*grp + 0..3 of head row
-    uint16_t *op = out + ((int64_t)seq * num_heads + head) * D + grp * 4;
+  // Ring of kBuf register sets: while tile t is computed, tiles t+1 ..
+  // t+kBuf-1 are in flight.  The ring is indexed by compile-time constants
+  // (the inner loop is unrolled) so it stays in registers.  Past the last
+  // tile the ring reloads the last tile (cache hits); those steps are
+  // skipped.  sched_barrier keeps the scheduler from sinking a load down to
+  // its use, which would trade the prefetch for fewer registers.
+  Frag<D> f[kBuf];
 #pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) {
-      u32x2 w;
-      w.x = E::pack(acc[dt][0] * inv, acc[dt][1] * inv);
-      w.y = E::pack(acc[dt][2] * inv, acc[dt][3] * inv);
-      *(u32x2 *)(op + dt * 16) = w;
+  for (int b = 0; b < kBuf - 1; ++b) load(f[b], min(b, cnt - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  for (int t = 0; t < cnt; t += kBuf) {
+#pragma unroll
+    for (int b = 0; b < kBuf; ++b) {
+      load(f[(b + kBuf - 1) % kBuf], min(t + b + kBuf - 1, cnt - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + b < cnt) step(f[b], t + b);
+      __builtin_amdgcn_sched_barrier(0);
     }
-  } else {
-    const int64_t slot = ((int64_t)seq * num_heads + head) * max_parts + part;
-    float *op = ws_o + slot * D + grp * 4;
-#pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) *(f32x4 *)(op + dt * 16) = acc[dt] * inv;
-    if (grp == 0) *(f32x2 *)(ws_ml + slot * 2) = f32x2{m_run, l_tot};
   }
 }
 
-// Log-sum-exp merge of the partitions of one (sequence, query head):
+// Log-sum-exp merge of the partial results of one (sequence, query head):
 //   M = max_p m_p,  c_p = l_p * 2^(m_p - M),  out = sum_p c_p o_p / sum_p c_p.
+// The partials of sequence s come from wavefronts wave_of(cu[s]) ..
+// wave_of(cu[s+1] - 1), in consecutive slots starting at that first
+// wavefront + s.
 template <int DT, int D>
 __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     uint16_t *__restrict__ out, const float *__restrict__ ws_o,
-    const float *__restrict__ ws_ml, const int32_t *__restrict__ context_lens,
-    int num_heads, int max_len, int max_parts, int part_tokens) {
+    const float *__restrict__ ws_ml, const int32_t *__restrict__ ws_cu, int num_seqs,
+    int num_heads, int waves, int slots) {
   using E = Elem<DT>;
   constexpr int PER = D / kWave;  // dims per lane
   const int head = blockIdx.x;
   const int seq = blockIdx.y;
   const int lane = threadIdx.x;
-  int len = context_lens[seq];
-  len = len < 0 ? 0 : (len > max_len ? max_len : len);
-  const int nparts = (len + part_tokens - 1) / part_tokens;
-  if (nparts <= 1) return;
+  const int n_tiles = ws_cu[num_seqs];
+  const int c0 = ws_cu[seq], c1 = ws_cu[seq + 1];
+  if (c1 <= c0) return;  // nothing to attend: the split pass wrote zeros
+  const int wv = min(waves, n_tiles);  // as in the split pass: all ranges non-empty
+  const int jf = wave_of(c0, n_tiles, wv);
+  const int jl = wave_of(c1 - 1, n_tiles, wv);
+  if (jf == jl) return;  // one wavefront held the sequence and wrote its row
+  const int np = jl - jf + 1;
 
-  const int64_t base = ((int64_t)seq * num_heads + head) * max_parts;
+  const int64_t base = (int64_t)head * slots + jf + seq;
   const f32x2 *ml = (const f32x2 *)(ws_ml + base * 2);
   float big = -INFINITY;
-  for (int p = lane; p < nparts; p += kWave) big = fmaxf(big, ml[p].x);
+  for (int p = lane; p < np; p += kWave) big = fmaxf(big, ml[p].x);
   big = wave_max(big);
 
   float num[PER];
@@ -347,7 +439,7 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
   float den = 0.f;
   const float *o = ws_o + base * D + lane * PER;
 #pragma unroll 4
-  for (int p = 0; p < nparts; ++p) {
+  for (int p = 0; p < np; ++p) {
     const f32x2 v = ml[p];
     const float c = v.y * __builtin_amdgcn_exp2f(v.x - big);
     den += c;
@@ -370,20 +462,21 @@ int launch_typed(const DecodeArgs &a) {
   const int group = a.num_heads / a.num_kv_heads;
   hipError_t e = hipSuccess;
   if (a.stages & 1) {
-    dim3 grid((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-    decode_partition_kernel<DT, D, BS><<<grid, kWave, 0, st>>>(
-        (uint16_t *)a.out, a.ws_o, a.ws_ml, (const uint16_t *)a.q,
+    dim3 grid((unsigned)a.num_kv_heads * (unsigned)a.waves);
+    const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
+    decode_split_kernel<DT, D, BS><<<grid, kWave, lds, st>>>(
+        (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, (const uint16_t *)a.q,
         (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.block_tables,
-        a.context_lens, scale_log2, a.num_kv_heads, a.num_heads, group,
-        a.max_blocks_per_seq, a.num_blocks, a.max_parts, a.partition_tokens);
+        a.context_lens, scale_log2, a.num_seqs, a.num_kv_heads, a.num_heads, group,
+        a.max_blocks_per_seq, a.num_blocks, a.waves, a.slots);
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
-  if ((a.stages & 2) && a.max_parts > 1) {
+  if (a.stages & 2) {
     dim3 g2((unsigned)a.num_heads, (unsigned)a.num_seqs);
     decode_merge_kernel<DT, D><<<g2, kWave, 0, st>>>(
-        (uint16_t *)a.out, a.ws_o, a.ws_ml, a.context_lens, a.num_heads,
-        a.max_blocks_per_seq * BS, a.max_parts, a.partition_tokens);
+        (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, a.num_seqs, a.num_heads, a.waves,
+        a.slots);
     e = hipGetLastError();
   }
   return (int)e;

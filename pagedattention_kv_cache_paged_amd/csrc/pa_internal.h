@@ -11,6 +11,9 @@ constexpr int kTile = 16;           // tokens per MFMA tile
 constexpr int kWave = 64;           // gfx950 wavefront
 constexpr int kMaxGroup = 16;       // query heads per KV head served by one wave
 constexpr int kWorkspaceAlign = 256;
+constexpr int kMaxTilesPerWave = 64; // one tile per lane of the wave's tile map
+constexpr int kTargetWaves = 1024;   // default split: one wave per SIMD of 256 CUs
+constexpr int kMaxSeqs = 8192;       // tile prefix and lengths live in LDS
 
 struct DecodeArgs {
   void *out;
@@ -28,11 +31,12 @@ struct DecodeArgs {
   int32_t max_blocks_per_seq;
   int64_t num_blocks;
   int32_t dtype;
-  int32_t partition_tokens;
-  int32_t max_parts;   // ceil(max_blocks_per_seq * block_size / partition_tokens)
-  float *ws_o;         // [num_seqs][num_heads][max_parts][head_dim] or null
-  float *ws_ml;        // [num_seqs][num_heads][max_parts][2] or null
-  int32_t stages;      // bit 0: partition pass, bit 1: merge pass
+  int32_t waves;       // wavefronts per KV head (equal shares of the flat tile list)
+  int32_t slots;       // partial-result slots per query head: waves + num_seqs
+  float *ws_o;         // [num_heads][slots][head_dim]
+  float *ws_ml;        // [num_heads][slots][2]  (running max in log2 units, sum)
+  int32_t *ws_cu;      // [num_seqs + 1] tile prefix, written by the split pass
+  int32_t stages;      // bit 0: split pass, bit 1: merge pass
   void *stream;
 };
 

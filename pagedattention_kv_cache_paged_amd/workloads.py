@@ -322,13 +322,15 @@ def tiny(seed: int = 1) -> Workload:
                  block_size=16, dtype=F16, seed=seed, pool=64, max_blocks_per_seq=7)
 
 
-def llama8b(seed: int = 2, block_size: int = 16) -> Workload:
+def llama8b(seed: int = 2, block_size: int = 16, placement: str = "random") -> Workload:
     """Llama-3-8B-shaped single-layer decode: batch 64, 32 query / 8 KV heads,
-    head_dim 128, bf16, block 16, lengths uniform in [128, 2048], pool 1.2x."""
+    head_dim 128, bf16, block 16, lengths uniform in [128, 2048], pool 1.2x.
+    ``placement="identity"`` gives each sequence physically consecutive
+    blocks (a contiguous cache) with the same token data."""
     lengths = rng(seed, _STREAM_LENGTHS).integers(128, 2048, size=64, endpoint=True)
     return build("llama8b", lengths, num_heads=32, num_kv_heads=8, head_dim=128,
                  block_size=block_size, dtype=BF16, seed=seed,
-                 max_blocks_per_seq=2048 // block_size)
+                 max_blocks_per_seq=2048 // block_size, placement=placement)
 
 
 def short(block_size: int = 16, seed: int = 3) -> Workload:

@@ -29,11 +29,11 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"paged_kv_write", "paged_attention_decode", "paged_attention_decode_ex",
             "paged_attention_decode_stages", "paged_attention_workspace_bytes",
-            "paged_attention_default_partition", "paged_validate_metadata", "pa_strerror",
+            "paged_attention_split_waves", "paged_validate_metadata", "pa_strerror",
             "pa_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
 
 
 def test_single_hip_runtime():
@@ -68,12 +68,13 @@ def _decode(**kw):
     (dict(hq=8 * 32), -3),           # group of 32 > 16
     (dict(B=-1), -3),
     (dict(B=70000), -3),
+    (dict(B=8193), -3),              # tile prefix of more sequences than LDS holds
     (dict(mb=0), -3),
     (dict(nb=0), -3),
     (dict(scale=float("nan")), -3),
     (dict(pt=24), -3),               # not a multiple of 16
     (dict(pt=40, bs=8), -3),
-    (dict(pt=16 * 64 + 16), -3),     # more blocks than lanes
+    (dict(pt=16 * 64 + 16), -3),     # more tiles per wave than lanes
     (dict(stages=0), -3),
     (dict(stages=4), -3),
     (dict(out=None), -1),
@@ -121,19 +122,26 @@ def test_write_zero_tokens_is_noop():
     assert _write(T=0, k=None) == 0
 
 
-def test_default_partition_and_workspace():
-    assert B.default_partition(7, 16) == 112       # 100-token capacity: one partition
-    assert B.default_partition(64, 8) == 512
-    assert B.default_partition(32, 16) == 512
-    assert B.default_partition(128, 16) == 256
-    assert B.default_partition(2048, 16) == 256
-    assert B.default_partition(16, 32) == 512
-    assert B.workspace_bytes(4, 4, 64, 7, 16) == 0
-    # 64 seqs x 32 heads x 8 partitions x (128 + 2) floats, o-part rounded to 256 B
-    o = 64 * 32 * 8 * 128 * 4
-    assert B.workspace_bytes(64, 32, 128, 128, 16) == o + 64 * 32 * 8 * 2 * 4
-    assert B.workspace_bytes(64, 32, 128, 128, 16, 2048) == 0
-    assert B.workspace_bytes(8, 64, 128, 2048, 16, 512) == 8 * 64 * 64 * 130 * 4
+def test_split_and_workspace():
+    """Hand-worked split sizes: cap = seqs * ceil(max_blocks * bs / 16) tiles
+    per KV head; waves = max(ceil(1024 / Hkv) or ceil(cap * 16 / pt),
+    ceil(cap / 64)), at most cap."""
+    assert B.split_waves(4, 2, 7, 16) == 28          # cap 28 < 512
+    assert B.split_waves(64, 8, 128, 16) == 128      # cap 8192: 1024 / 8
+    assert B.split_waves(8, 8, 2048, 16) == 256      # cap 16384: 64 tiles per wave
+    assert B.split_waves(256, 8, 64, 8) == 128       # cap 256 * 32
+    assert B.split_waves(64, 8, 128, 16, 256) == 512  # 8192 * 16 / 256
+    assert B.split_waves(64, 8, 128, 16, 1024) == 128
+    assert B.split_waves(3, 1, 64, 32, 16) == 384    # cap 3 * 128, one tile each
+    assert B.split_waves(64, 8, 128, 16, 24) == 0    # not a multiple of 16
+    assert B.split_waves(64, 8, 128, 16, 2048) == 0  # over 64 tiles
+    # llama8b sizes: 128 waves + 64 seqs = 192 slots per query head;
+    # partials 32 x 192 x 128 fp32, (m, l) 32 x 192 x 2 fp32, prefix 65 int32
+    # padded to 512 B
+    assert B.workspace_bytes(64, 32, 8, 128, 128, 16) == (
+        32 * 192 * 128 * 4 + 32 * 192 * 2 * 4 + 512)
+    assert B.workspace_bytes(64, 32, 8, 128, 128, 16, 2048) == 0
+    assert B.workspace_bytes(0, 32, 8, 128, 128, 16) == 0
 
 
 def test_validate_metadata():

@@ -138,7 +138,8 @@ def _rows_sample(w, n, seed):
 def test_decode_named(name, make, full):
     w = make()
     say(f"decode {name} B={w.num_seqs} Hq={w.num_heads} Hkv={w.num_kv_heads} "
-        f"D={w.head_dim} bs={w.block_size} pt={B.default_partition(w.max_blocks_per_seq, w.block_size)}")
+        f"D={w.head_dim} bs={w.block_size} "
+        f"waves={B.split_waves(w.num_seqs, w.num_kv_heads, w.max_blocks_per_seq, w.block_size)}")
     got = Case(w).decode()
     kc, vc = oracle_caches(w)
     assert np.all(np.isfinite(f64(got, w.dtype)))
@@ -167,8 +168,6 @@ for i, (G, D, bs, dt) in enumerate([(1, 64, 8, W.F16), (2, 128, 16, W.BF16),
 @pytest.mark.parametrize("i,G,D,bs,dt", SHAPES)
 @pytest.mark.parametrize("pt", [0, 16, 64])
 def test_decode_ragged(i, G, D, bs, dt, pt):
-    if pt and pt % bs:
-        pt = bs * 2
     g = np.random.default_rng(1000 + i)
     hkv = int(g.integers(1, 4))
     lens = np.concatenate([[1, 2, 15, 16, 17, 31, 33], g.integers(1, 700, size=5)])
@@ -182,14 +181,15 @@ def test_decode_ragged(i, G, D, bs, dt, pt):
 
 
 def test_max_partition_and_group():
-    """G = 16 (no padding), a partition of 64 blocks (one per lane) and full
-    block tables."""
+    """G = 16 (no padding), full block tables, and the widest split: 64
+    tiles per wave (one per lane), both by default (long full sequences) and
+    with partition_tokens = 1024."""
     for bs in (8, 16, 32):
-        w = W.build("max", [64 * bs * 2, 64 * bs * 2 - 5, 1], num_heads=32, num_kv_heads=2,
+        w = W.build("max", [128 * bs, 128 * bs - 5, 1], num_heads=32, num_kv_heads=2,
                     head_dim=128, block_size=bs, dtype=W.BF16, seed=77,
                     max_blocks_per_seq=128)
         say(f"max bs={bs}")
-        got = Case(w).decode(partition_tokens=64 * bs)
+        got = Case(w).decode(partition_tokens=1024)
         kc, vc = oracle_caches(w)
         ref = oracle.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, bs, w.dtype)
         check_close(got, ref, w.dtype, f"max bs{bs}")
@@ -206,6 +206,31 @@ def test_partition_size_invariance():
     for pt in (16, 48, 128, 256, 512, 1024):
         say(f"partition {pt}")
         check_close(c.decode(partition_tokens=pt), ref, w.dtype, f"pt{pt}")
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("pt", [0, 16, 48, 1024])
+def test_split_edges(bs, pt):
+    """Empty sequences first, last and in between, sequences of one token,
+    lengths on tile and block edges, and more waves than tiles (pt = 16), so
+    wave ranges start and end on and off sequence boundaries and some waves
+    are empty."""
+    lens = [0, 1, 0, 16, 17, 0, 300, 31, 32, 33, 0, 5, 64, 0]
+    w = W.build("edges", [max(L, 1) for L in lens], num_heads=8, num_kv_heads=2,
+                head_dim=64, block_size=bs, dtype=W.F16, seed=90 + bs,
+                max_blocks_per_seq=(320 + bs - 1) // bs)
+    c = Case(w)
+    cl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    say(f"edges bs={bs} pt={pt}")
+    got = c.decode(partition_tokens=pt, cl=cl)
+    kc, vc = oracle_caches(w)
+    ref = oracle.decode(w.q, kc, vc, w.block_tables, np.array(lens, np.int32), w.scale, bs,
+                        w.dtype)
+    assert np.all(f64(got, w.dtype)[np.array(lens) == 0] == 0)
+    check_close(got, ref, w.dtype, f"edges bs{bs} pt{pt}")
+    # every sequence empty
+    got0 = f64(c.decode(partition_tokens=pt, cl=torch.zeros_like(cl)), w.dtype)
+    assert np.all(got0 == 0)
 
 
 def test_placement_permutation_bit_identical():
