@@ -144,10 +144,9 @@ __device__ __forceinline__ int wave_of(int tau, int n, int w) {
   return (int)((((int64_t)tau + 1) * w - 1) / n);
 }
 
-// Query, K and V registers of one 16-token tile.
+// K and V registers of one 16-token tile.
 template <int D>
 struct Frag {
-  u32x4 q[D / 32];
   u32x4 k[D / 32];
   u32x2 v[D / 16];
 };
@@ -166,9 +165,12 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   using E = Elem<DT>;
   constexpr int KSTEPS = D / 32;  // 16x16x32 MFMAs per QK tile
   constexpr int DTILES = D / 16;  // 16x16x16 MFMAs per PV tile
-  extern __shared__ int lds[];    // cu[num_seqs + 1], then lens[num_seqs]
+  // LDS: cu[num_seqs + 1], lens[num_seqs], then (16-byte aligned) the
+  // current segment's query fragments, lane-major per k-step.
+  extern __shared__ __align__(16) int lds[];
   int *cu = lds;
   int *lens = lds + num_seqs + 1;
+  u32x4 *q_lds = reinterpret_cast<u32x4 *>(lds + ((2 * num_seqs + 1 + 3) & ~3));
 
   const int kvh = blockIdx.x % num_kv_heads;
   const int j = blockIdx.x / num_kv_heads;
@@ -244,10 +246,33 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   b1 = (b1 >= 0 && b1 < num_blocks) ? b1 : 0;
   const int seg_end = (it == ntiles_sq - 1 || tau == t1 - 1) ? 1 : 0;
   const int whole = (first >= t0 && first + ntiles_sq <= t1) ? 1 : 0;
+  const uint64_t ends = __ballot(seg_end && lane < cnt);  // bit i: a segment ends at tile i
 
-  // Padded head lanes (row >= group) read a real query row and compute
-  // values that are never stored.
+  // Query fragment of the current segment and, one segment ahead, of the
+  // next (lane (row, grp) holds q[head row][32*ks + 8*grp .. +8]).  Padded
+  // head lanes (row >= group) read a real query row and compute values that
+  // are never stored.
   const int qh = kvh * group + min(row, group - 1);
+  auto load_q = [&](u32x4 (&dst)[KSTEPS], int idx) {
+    const int s = __builtin_amdgcn_readlane(sq, idx);
+    const uint16_t *qp = q + ((int64_t)s * num_heads + qh) * D + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) dst[ks] = *(const u32x4 *)(qp + ks * 32);
+  };
+  // first tile of the segment after the one ending at tile `e` (cnt - 1 if none)
+  auto next_first = [&](int e) {
+    return e + 1 < cnt ? e + 1 : cnt - 1;
+  };
+  // The current fragment lives in LDS and is read there each tile; only the
+  // next segment's, prefetched one segment ahead, is held in registers.
+  // (Two register sets swapped at segment ends make the compiler copy a
+  // fresh load, which waits for it and drains the ring.)
+  u32x4 qnext[KSTEPS];
+  load_q(qnext, 0);
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) q_lds[ks * kWave + lane] = qnext[ks];
+  __builtin_amdgcn_sched_barrier(0);
+  load_q(qnext, next_first(__builtin_ctzll(ends)));
   const int64_t blk_stride = (int64_t)num_kv_heads * BS * D;  // elements per block
   const uint16_t *kbase = k_cache + (int64_t)kvh * BS * D;
   const uint16_t *vbase = v_cache + (int64_t)kvh * D * BS;
@@ -259,7 +284,6 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // once per launch, so they bypass the caches' normal replacement.
   auto load = [&](Frag<D> &f, int idx) {
     const int n = __builtin_amdgcn_readlane(nvalid, idx);
-    const int s = __builtin_amdgcn_readlane(sq, idx);
     const int ka = __builtin_amdgcn_readlane(b0, idx);
     const int ktok = min(row, n - 1);
     const int vtok = min(grp * 4, (n - 1) & ~3);
@@ -280,9 +304,6 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
       koff = o + ktok;
       voff = o + vtok;
     }
-    const uint16_t *qp = q + ((int64_t)s * num_heads + qh) * D + grp * 8;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) f.q[ks] = *(const u32x4 *)(qp + ks * 32);
     const uint16_t *kp = kbase + (int64_t)kb * blk_stride + koff * D + grp * 8;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
@@ -306,9 +327,12 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // are zeroed (unused slots may hold anything, NaN included).
   auto step = [&](Frag<D> &f, int idx) {
     const int n = __builtin_amdgcn_readlane(nvalid, idx);
+    u32x4 qf[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = q_lds[ks * kWave + lane];
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) sc = E::qk(f.k[ks], f.q[ks], sc);
+    for (int ks = 0; ks < KSTEPS; ++ks) sc = E::qk(f.k[ks], qf[ks], sc);
     float s[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] = (grp * 4 + r < n) ? sc[r] * scale_log2 : -INFINITY;
@@ -379,6 +403,14 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
       l_run = 0.f;
 #pragma unroll
       for (int dt = 0; dt < DTILES; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // Publish the next segment's query (prefetched a segment ago, so this
+      // does not wait on recent loads), then prefetch the one after it,
+      // which starts after the next segment end following tile idx.
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) q_lds[ks * kWave + lane] = qnext[ks];
+      __builtin_amdgcn_sched_barrier(0);
+      const uint64_t later = idx + 1 < kWave ? ends & (~0ull << (idx + 1)) : 0ull;
+      load_q(qnext, later ? next_first(__builtin_ctzll(later)) : cnt - 1);
     }
   };
 
@@ -463,7 +495,8 @@ int launch_typed(const DecodeArgs &a) {
   hipError_t e = hipSuccess;
   if (a.stages & 1) {
     dim3 grid((unsigned)a.num_kv_heads * (unsigned)a.waves);
-    const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
+    const size_t lds = (size_t)((2 * a.num_seqs + 1 + 3) & ~3) * sizeof(int) +
+                       (size_t)(D / 32) * kWave * 16;
     decode_split_kernel<DT, D, BS><<<grid, kWave, lds, st>>>(
         (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, (const uint16_t *)a.q,
         (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.block_tables,
