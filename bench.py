@@ -28,6 +28,80 @@ import numpy as np
 METRIC = "paged decode KV-read HBM GB/s (% of peak) + seq-tokens/s, Llama-3-8B shape"
 HBM_PEAK_GBS = 8000.0
 WORKLOADS = ("llama8b", "long", "prefix", "short_bs8", "short_bs16", "short_bs32", "tiny")
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(ROOT, "pagedattention_kv_cache_paged_amd", "csrc", "pa_decode.hip")
+SPLIT_KERNEL = "decode_split_kernel"
+COPY_BYTES = 512 << 20   # plain device copy used to calibrate the byte counters
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def counters_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{SPLIT_KERNEL}_{workload}_counters.txt")
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str) -> dict:
+    """Per-launch HBM bytes of the split pass from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for the plain COPY_BYTES device copy of the same run."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        split, copy = [], []
+        for fn in files:
+            for r in csv.DictReader(open(fn)):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"]) * 1024.0
+                if SPLIT_KERNEL in r["Kernel_Name"]:
+                    split.append(v)
+                elif "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= (1 << 16):
+                    copy.append(v)
+        if not split or not copy:
+            raise SystemExit(f"{counter}: found {len(split)} split and {len(copy)} copy dispatches")
+        return float(np.mean(split)), float(np.mean(copy))
+
+    f_split, f_copy = per_dispatch(fetch_dir, "FETCH_SIZE")
+    w_split, w_copy = per_dispatch(write_dir, "WRITE_SIZE")
+    f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    return {
+        "kernel": SPLIT_KERNEL, "workload": workload, "source_sha256": kernel_source_hash(),
+        "fetch_bytes_raw": f_split, "write_bytes_raw": w_split,
+        "copy_bytes": COPY_BYTES, "copy_fetch_raw": f_copy, "copy_write_raw": w_copy,
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        "fetch_bytes": f_split * f_scale, "write_bytes": w_split * w_scale,
+        "traffic_bytes": f_split * f_scale + w_split * w_scale,
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o cnt -- "
+            f"python3 bench.py --workload {workload} --steps 10 --warmup 2 --no-cpu-baseline "
+            f"--copy-calibration",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o cnt -- "
+            f"python3 bench.py --workload {workload} --steps 10 --warmup 2 --no-cpu-baseline "
+            f"--copy-calibration",
+            f"python3 bench.py --summarize-counters {fetch_dir} {write_dir} --workload {workload}",
+        ],
+    }
+
+
+def recorded_traffic(workload: str):
+    """Counter-measured bytes per split launch, if recorded for this workload
+    and for the kernel source as it is now; else None."""
+    try:
+        with open(counters_path(workload)) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes")
 
 
 def make_workload(name, placement="random"):
@@ -77,7 +151,20 @@ def main():
                     help="physical block placement of the llama8b workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (byte-counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the split pass's per-launch HBM bytes from two rocprofv3 "
+                         "--pmc runs to profiles/ and exit (no GPU needed)")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        rec = summarize_counters(*args.summarize_counters, args.workload)
+        os.makedirs(os.path.dirname(counters_path(args.workload)), exist_ok=True)
+        with open(counters_path(args.workload), "w") as f:
+            f.write(json.dumps(rec, indent=1) + "\n")
+        print(json.dumps(rec))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -154,12 +241,35 @@ def main():
         decode(i, 2)
     torch.cuda.synchronize()
 
+    # Timed region: exactly K steps, nothing else on the stream.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
+    for i in range(K):
+        write(i)
+        decode(i, 1)
+        decode(i, 2)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(stop) / K
+
+    # Roofline of the split pass: K back-to-back split launches on the launch
+    # stream, bracketed by two events (average launch duration, no event
+    # overhead between launches).
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for i in range(K):
+        decode(i, 1)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    t_split = s0.elapsed_time(s1) / K * 1e3   # us
+
+    # Per-launch breakdown (informative): the same K steps again with events
+    # between the launches, which adds the events' own overhead.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     for i in range(K):
         e = ev[i]
         e[0].record(stream)
@@ -169,10 +279,14 @@ def main():
         e[2].record(stream)
         decode(i, 2)
         e[3].record(stream)
-    stop.record(stream)
     torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_step = start.elapsed_time(stop) / K
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     t_write = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e3   # us
     t_part = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
     t_merge = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
@@ -181,7 +295,7 @@ def main():
     kv_bytes = w.logical_tokens * w.bytes_per_token
     unique_bytes = w.unique_tokens * w.bytes_per_token
     gbs = kv_bytes / (ms_step * 1e-3) / 1e9
-    achieved = kv_bytes / (t_part * 1e-6) / 1e9
+    achieved = kv_bytes / (t_split * 1e-6) / 1e9
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -209,9 +323,11 @@ def main():
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "seq_tokens_per_s": round(w.logical_tokens / (ms_step * 1e-3), 1),
         "new_tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
-        "kernel_us": {"kv_write": round(t_write, 3), "decode_split": round(t_part, 3),
-                      "decode_merge": round(t_merge, 3),
-                      "decode_split_p10_p50_p90": [round(x, 3) for x in p_part]},
+        "split_us_back_to_back": round(t_split, 3),
+        "kernel_us_event_bracketed": {
+            "kv_write": round(t_write, 3), "decode_split": round(t_part, 3),
+            "decode_merge": round(t_merge, 3),
+            "decode_split_p10_p50_p90": [round(x, 3) for x in p_part]},
         "host_wall_ms_per_step": round(t_wall * 1e3 / K, 5),
         "roofline": {
             "kernel": "decode_split_kernel",
@@ -220,7 +336,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "avg_launch_us": round(t_split, 3),
+            "traffic": recorded_traffic(args.workload),
             "bytes_per_launch": kv_bytes,
         },
     }
