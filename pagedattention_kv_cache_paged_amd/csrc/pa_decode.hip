@@ -120,11 +120,6 @@ __device__ __forceinline__ float rows_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
-}
 
 
 // Inclusive prefix sum over the wave's 64 lanes.
@@ -461,22 +456,26 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
 
   const int64_t base = (int64_t)head * slots + jf + seq;
   const f32x2 *ml = (const f32x2 *)(ws_ml + base * 2);
-  float big = -INFINITY;
-  for (int p = lane; p < np; p += kWave) big = fmaxf(big, ml[p].x);
-  big = wave_max(big);
-
+  // One pass with a running maximum, so each partial's (m, l) and o are
+  // loaded together: c_p = l_p * 2^(m_p - M) rescaled as M grows.
+  float big = -INFINITY, den = 0.f;
   float num[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) num[i] = 0.f;
-  float den = 0.f;
   const float *o = ws_o + base * D + lane * PER;
 #pragma unroll 4
   for (int p = 0; p < np; ++p) {
     const f32x2 v = ml[p];
-    const float c = v.y * __builtin_amdgcn_exp2f(v.x - big);
-    den += c;
+    float op[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) num[i] += c * o[(int64_t)p * D + i];
+    for (int i = 0; i < PER; ++i) op[i] = o[(int64_t)p * D + i];
+    const float m_new = fmaxf(big, v.x);
+    const float a = __builtin_amdgcn_exp2f(big - m_new);  // 0 on the first partial
+    const float c = v.y * __builtin_amdgcn_exp2f(v.x - m_new);
+    den = den * a + c;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) num[i] = num[i] * a + c * op[i];
+    big = m_new;
   }
   const float inv = 1.0f / den;
   uint16_t *op = out + ((int64_t)seq * num_heads + head) * D + lane * PER;

@@ -25,17 +25,26 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
     uint16_t *__restrict__ v_cache, int num_kv_heads, int64_t num_slots) {
   constexpr int CH = D / 8;  // 16-byte chunks per head row
   const int64_t tok = blockIdx.x;
+  const int nch = num_kv_heads * CH;
+  // The first chunk's k/v loads go out together with the slot load (they do
+  // not depend on it), so the launch costs one memory round trip, not two.
+  const int c0 = threadIdx.x;
+  u32x4 kx0 = {0, 0, 0, 0}, vx0 = {0, 0, 0, 0};
+  if (c0 < nch) {
+    const int64_t src = (tok * num_kv_heads + c0 / CH) * D + (c0 % CH) * 8;
+    kx0 = *(const u32x4 *)(k + src);
+    vx0 = *(const u32x4 *)(v + src);
+  }
   const int64_t slot = slot_mapping[tok];
   if (slot < 0 || slot >= num_slots) return;  // padding, or outside the pool
   const int64_t blk = slot / BS;
   const int off = (int)(slot % BS);
-  const int nch = num_kv_heads * CH;
-  for (int c = threadIdx.x; c < nch; c += blockDim.x) {
+  for (int c = c0; c < nch; c += blockDim.x) {
     const int h = c / CH;
     const int d0 = (c % CH) * 8;
     const int64_t src = (tok * num_kv_heads + h) * D + d0;
-    const u32x4 kx = *(const u32x4 *)(k + src);
-    const u32x4 vx = *(const u32x4 *)(v + src);
+    const u32x4 kx = c == c0 ? kx0 : *(const u32x4 *)(k + src);
+    const u32x4 vx = c == c0 ? vx0 : *(const u32x4 *)(v + src);
     const int64_t bh = blk * num_kv_heads + h;
     *(u32x4 *)(k_cache + (bh * BS + off) * D + d0) = kx;
     uint16_t *vd = v_cache + (bh * D + d0) * BS + off;

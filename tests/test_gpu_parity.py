@@ -233,6 +233,41 @@ def test_split_edges(bs, pt):
     assert np.all(got0 == 0)
 
 
+def test_workspace_reuse_across_shapes():
+    """One workspace serves calls of different shapes and splits: repeated
+    calls give bit-identical rows, and a call of another shape on the same
+    (large enough) workspace is still right."""
+    w = W.build("reuse", [3, 300, 1000, 2048, 17], num_heads=32, num_kv_heads=8,
+                head_dim=128, block_size=16, dtype=W.BF16, seed=44, max_blocks_per_seq=128)
+    c = Case(w)
+    need = B.workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                             w.max_blocks_per_seq, w.block_size, 64)
+    ws = torch.full((need + (1 << 20),), 0x7f, dtype=torch.uint8, device=DEV)
+    say("reuse: three calls, one workspace")
+    outs = []
+    for _ in range(3):
+        out = torch.empty_like(c.q)
+        B.paged_attention_decode(out, c.q, c.kc, c.vc, c.bt, c.cl, w.scale, 16, 8,
+                                 partition_tokens=64, workspace_tensor=ws)
+        torch.cuda.synchronize()
+        outs.append(host_bits(out))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    kc, vc = oracle_caches(w)
+    ref = oracle.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, 16, w.dtype)
+    check_close(outs[0], ref, w.dtype, "reuse")
+    w2 = W.build("reuse2", [700, 5], num_heads=16, num_kv_heads=2, head_dim=64,
+                 block_size=8, dtype=W.F16, seed=45, max_blocks_per_seq=100)
+    c2 = Case(w2)
+    out2 = torch.empty_like(c2.q)
+    B.paged_attention_decode(out2, c2.q, c2.kc, c2.vc, c2.bt, c2.cl, w2.scale, 8, 2,
+                             partition_tokens=32, workspace_tensor=ws)
+    torch.cuda.synchronize()
+    kc2, vc2 = oracle_caches(w2)
+    ref2 = oracle.decode(w2.q, kc2, vc2, w2.block_tables, w2.context_lens, w2.scale, 8,
+                         w2.dtype)
+    check_close(host_bits(out2), ref2, w2.dtype, "reuse2")
+
+
 def test_placement_permutation_bit_identical():
     lens = [3, 50, 129, 777]
     outs = []
