@@ -17,6 +17,9 @@ independently in ``oracle.c``):
 * V cache ``uint16 [num_blocks, num_kv_heads, head_dim, block_size]``
 * q ``uint16 [num_seqs, num_heads, head_dim]``; k, v ``uint16 [T, num_kv_heads, head_dim]``
 * ``dtype`` 0 = IEEE binary16, 1 = bfloat16 (raw bit patterns).
+* FP8 caches: uint8 OCP E4M3 codes in the same layouts, standing for
+  code * k_scale (K) or code * v_scale (V); the append quantises
+  float32(x) * float32(1 / scale) to the nearest code, saturating at +-448.
 """
 from __future__ import annotations
 
@@ -85,6 +88,18 @@ def _load():
     lib.oracle_decode_rows.restype = i32
     lib.oracle_decode_row_partitioned.argtypes = [p] + common + [i32, i32, i32]
     lib.oracle_decode_row_partitioned.restype = i32
+    lib.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_f64.restype = dbl
+    lib.oracle_f64_to_e4m3.argtypes = [dbl]
+    lib.oracle_f64_to_e4m3.restype = ctypes.c_uint8
+    f32 = ctypes.c_float
+    lib.oracle_kv_write_fp8.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i64, i32, f32, f32]
+    lib.oracle_kv_write_fp8.restype = i32
+    common8 = [p, p, p, p, p, dbl, i32, i32, i32, i32, i32, i32, i64, i32, dbl, dbl]
+    lib.oracle_decode_fp8.argtypes = [p] + common8
+    lib.oracle_decode_fp8.restype = i32
+    lib.oracle_decode_fp8_rows.argtypes = [p, p, i32] + common8
+    lib.oracle_decode_fp8_rows.restype = i32
     _lib = lib
     return lib
 
@@ -192,3 +207,77 @@ def decode_row_partitioned(s, h, part_tokens, q, k_cache, v_cache, block_tables,
            "oracle_decode_row_partitioned")
     del keep
     return out
+
+
+# ---- FP8 (E4M3) cache ------------------------------------------------------
+
+FP8_NAN = 0x7F
+
+
+def e4m3_to_f64(code: int) -> float:
+    return _load().oracle_e4m3_to_f64(int(code))
+
+
+def f64_to_e4m3(y: float) -> int:
+    return int(_load().oracle_f64_to_e4m3(float(y)))
+
+
+def kv_write_fp8(k, v, slot_mapping, k_cache, v_cache, block_size: int, dtype,
+                 k_scale: float, v_scale: float) -> None:
+    """In-place quantising scatter of 16-bit k/v [T, Hkv, D] into uint8 E4M3
+    caches ([N, Hkv, bs, D] and [N, Hkv, D, bs]) at slot_mapping."""
+    k, v = _u16(k), _u16(v)
+    slot = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    assert k_cache.dtype == np.uint8 and v_cache.dtype == np.uint8
+    T, hkv, d = k.shape
+    nb = k_cache.shape[0]
+    assert k_cache.shape == (nb, hkv, block_size, d)
+    assert v_cache.shape == (nb, hkv, d, block_size)
+    rc = _load().oracle_kv_write_fp8(_ptr(k), _ptr(v), _ptr(slot), _ptr(k_cache),
+                                     _ptr(v_cache), T, hkv, d, block_size, nb,
+                                     dtype_code(dtype), float(k_scale), float(v_scale))
+    _check(rc, "oracle_kv_write_fp8")
+
+
+def _decode_fp8_args(q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                     q_dtype, k_scale, v_scale):
+    q = _u16(q)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    kc = np.ascontiguousarray(k_cache)
+    vc = np.ascontiguousarray(v_cache)
+    assert kc.dtype == np.uint8 and vc.dtype == np.uint8
+    B, hq, d = q.shape
+    nb, hkv = kc.shape[0], kc.shape[1]
+    assert kc.shape == (nb, hkv, block_size, d) and vc.shape == (nb, hkv, d, block_size)
+    keep = (q, bt, cl, kc, vc)
+    args = [_ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(cl), float(scale), block_size, hkv,
+            B, hq, d, bt.shape[1], nb, dtype_code(q_dtype), float(k_scale), float(v_scale)]
+    return keep, args, (B, hq, d)
+
+
+def decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale, block_size, q_dtype,
+               k_scale, v_scale) -> np.ndarray:
+    """Decode attention over E4M3 caches; returns float64 [B, Hq, D]."""
+    keep, args, (B, hq, d) = _decode_fp8_args(q, k_cache, v_cache, block_tables,
+                                              context_lens, scale, block_size, q_dtype,
+                                              k_scale, v_scale)
+    out = np.zeros((B, hq, d), dtype=np.float64)
+    _check(_load().oracle_decode_fp8(_ptr(out), *args), "oracle_decode_fp8")
+    del keep
+    return out
+
+
+def decode_fp8_rows(rows, q, k_cache, v_cache, block_tables, context_lens, scale,
+                    block_size, q_dtype, k_scale, v_scale) -> np.ndarray:
+    """Selected (seq, head) rows of decode_fp8; returns float64 [len(rows), D]."""
+    rows = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
+    keep, args, (_, _, d) = _decode_fp8_args(q, k_cache, v_cache, block_tables, context_lens,
+                                             scale, block_size, q_dtype, k_scale, v_scale)
+    out = np.zeros((rows.shape[0], d), dtype=np.float64)
+    _check(_load().oracle_decode_fp8_rows(_ptr(out), _ptr(rows), rows.shape[0], *args),
+           "oracle_decode_fp8_rows")
+    del keep
+    return out
+

@@ -13,7 +13,8 @@
  *        (developer.cloud.tencent.cn), part 2, 2.1 (BlockTable and
  *        append_token) and 2.3 (attention forward over block tables).
  *   [P4] "vLLM framework analysis: how PagedAttention speeds up LLM
- *        inference 20x" (intelliparadigm.com), 2.3 (shared blocks).
+ *        inference 20x" (intelliparadigm.com), 2.3 (shared blocks), 7
+ *        (mixed precision).
  *
  * The pages never write the attention formula down.  The oracle computes the
  * standard scaled-dot-product softmax attention of one decode query per
@@ -33,7 +34,9 @@
  *   slot     int64 [num_tokens]; slot = physical_block * block_size + offset,
  *            negative = padding, skipped.
  *   Elements are raw IEEE binary16 (dtype 0) or bfloat16 (dtype 1) bit
- *   patterns, decoded here by hand.
+ *   patterns, decoded here by hand; an FP8 cache holds OCP E4M3 codes, one
+ *   byte per element in the same layouts, standing for code * tensor scale
+ *   ([P4] 7: FP8 for attention, FP16 elsewhere).
  *
  * Parity pins: every function below is pinned by tests under tests/ that do
  * not retype its formula (see the test module docstrings).
@@ -45,6 +48,7 @@
 
 #define ORACLE_F16 0
 #define ORACLE_BF16 1
+#define ORACLE_FP8 2 /* cache element type only: E4M3 codes with a tensor scale */
 
 #define ORACLE_OK 0
 #define ORACLE_EARG -1    /* bad sizes or dtype */
@@ -91,6 +95,66 @@ double oracle_bf16_to_f64(uint16_t bits) {
 
 static double decode(uint16_t bits, int dtype) {
   return dtype == ORACLE_BF16 ? oracle_bf16_to_f64(bits) : oracle_f16_to_f64(bits);
+}
+
+/* OCP FP8 E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits (bias 7), 3 fraction
+ * bits, no infinities; S.1111.111 is NaN, the largest finite magnitude is
+ * 1.75 * 2^8 = 448 and subnormals are m * 2^-9.  Exact conversion. */
+double oracle_e4m3_to_f64(uint8_t code) {
+  int sign = code >> 7;
+  int expo = (code >> 3) & 0xf;
+  int frac = code & 7;
+  double mag;
+  if (expo == 0xf && frac == 7) {
+    mag = NAN;
+  } else if (expo == 0) {
+    mag = ldexp((double)frac, -9); /* 0.frac * 2^-6 */
+  } else {
+    mag = ldexp((double)(frac + 8), expo - 10); /* 1.frac * 2^(expo-7) */
+  }
+  return sign ? -mag : mag;
+}
+
+/* The E4M3 code nearest to y, ties to the code with an even fraction (the
+ * representable magnitudes are the integers n * u with u the spacing, and
+ * the fraction's last bit is the parity of n); finite magnitudes beyond 448
+ * saturate to +-448; NaN gives NaN.  All candidates are dyadic rationals, so
+ * the comparisons below are exact in double precision. */
+uint8_t oracle_f64_to_e4m3(double y) {
+  if (isnan(y)) return 0x7f;
+  int sign = signbit(y) ? 1 : 0;
+  double a = fabs(y);
+  if (a >= 448.0) return (uint8_t)((sign << 7) | 0x7e);
+  double u; /* spacing of representable magnitudes at a */
+  if (a < ldexp(1.0, -6)) {
+    u = ldexp(1.0, -9);
+  } else {
+    int e;
+    frexp(a, &e); /* a = f * 2^e, f in [0.5, 1): a in [2^(e-1), 2^e) */
+    u = ldexp(1.0, e - 1 - 3);
+  }
+  double n = floor(a / u); /* a / u is exact: u is a power of two */
+  double below = a - n * u, above = (n + 1) * u - a;
+  if (above < below || (above == below && fmod(n, 2.0) != 0.0)) n += 1.0;
+  double pick = n * u; /* <= 448 because a < 448 */
+  int code;
+  if (pick < ldexp(1.0, -6)) {
+    code = (int)(pick / ldexp(1.0, -9)); /* subnormal (or zero) */
+  } else {
+    int e;
+    double f = frexp(pick, &e); /* pick = f * 2^e */
+    code = ((e - 1 + 7) << 3) | (int)(f * 16.0 - 8.0);
+  }
+  return (uint8_t)((sign << 7) | code);
+}
+
+/* One cache element as a real number: a 16-bit value, or an E4M3 code
+ * times its tensor scale. */
+static double cache_value(const void *cache, int64_t index, int cache_dtype,
+                          double scale) {
+  if (cache_dtype == ORACLE_FP8)
+    return oracle_e4m3_to_f64(((const uint8_t *)cache)[index]) * scale;
+  return decode(((const uint16_t *)cache)[index], cache_dtype) * scale;
 }
 
 /* ---- cache accessors ---------------------------------------------------- */
@@ -171,16 +235,19 @@ int oracle_kv_write(const uint16_t *k, const uint16_t *v,
  *     w[t]   = exp(x[t] - max_t x[t])
  *     out[d] = sum_t w[t] * V[t,d] / sum_t w[t]
  * L == 0 gives an all-zero row.  The normalised weights are checked to sum
- * to one within 1e-12. */
-int oracle_decode_row(double *out_row, const uint16_t *q, const uint16_t *k_cache,
-                      const uint16_t *v_cache, const int32_t *block_tables,
-                      const int32_t *context_lens, double scale, int block_size,
-                      int num_kv_heads, int num_seqs, int num_heads, int head_dim,
-                      int max_blocks_per_seq, int64_t num_blocks, int dtype, int s,
-                      int h) {
+ * to one within 1e-12.  K and V elements are 16-bit values of the q type,
+ * or E4M3 codes times k_scale / v_scale (cache_dtype ORACLE_FP8). */
+static int decode_row_any(double *out_row, const uint16_t *q, const void *k_cache,
+                          const void *v_cache, const int32_t *block_tables,
+                          const int32_t *context_lens, double scale, int block_size,
+                          int num_kv_heads, int num_seqs, int num_heads, int head_dim,
+                          int max_blocks_per_seq, int64_t num_blocks, int q_dtype,
+                          int cache_dtype, double k_scale, double v_scale, int s, int h) {
   if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || s < 0 ||
       s >= num_seqs || h < 0 || h >= num_heads || block_size <= 0 ||
-      head_dim <= 0 || (dtype != ORACLE_F16 && dtype != ORACLE_BF16))
+      head_dim <= 0 || (q_dtype != ORACLE_F16 && q_dtype != ORACLE_BF16) ||
+      (cache_dtype != ORACLE_F16 && cache_dtype != ORACLE_BF16 &&
+       cache_dtype != ORACLE_FP8))
     return ORACLE_EARG;
   int group = num_heads / num_kv_heads;
   int kv_head = h / group;
@@ -200,10 +267,12 @@ int oracle_decode_row(double *out_row, const uint16_t *q, const uint16_t *k_cach
       free(x);
       return ORACLE_EBLOCK;
     }
-    const uint16_t *krow = k_row(k_cache, block, kv_head, (int)(t % block_size),
-                                 num_kv_heads, block_size, head_dim);
+    /* K row of token t: [block][kv_head][offset][:] */
+    int64_t krow = ((block * num_kv_heads + kv_head) * (int64_t)block_size +
+                    (int)(t % block_size)) * head_dim;
     double dot = 0.0;
-    for (int d = 0; d < head_dim; ++d) dot += decode(qrow[d], dtype) * decode(krow[d], dtype);
+    for (int d = 0; d < head_dim; ++d)
+      dot += decode(qrow[d], q_dtype) * cache_value(k_cache, krow + d, cache_dtype, k_scale);
     x[t] = scale * dot;
   }
 
@@ -224,15 +293,28 @@ int oracle_decode_row(double *out_row, const uint16_t *q, const uint16_t *k_cach
   for (int64_t t = 0; t < len; ++t) {
     int64_t block = table[t / block_size];
     int offset = (int)(t % block_size);
-    for (int d = 0; d < head_dim; ++d)
-      out_row[d] += x[t] *
-                    decode(v_elem(v_cache, block, kv_head, offset, d, num_kv_heads,
-                                  block_size, head_dim),
-                           dtype);
+    for (int d = 0; d < head_dim; ++d) {
+      /* V element (token t, dim d): [block][kv_head][d][offset] */
+      int64_t vi = ((block * num_kv_heads + kv_head) * (int64_t)head_dim + d) *
+                       block_size + offset;
+      out_row[d] += x[t] * cache_value(v_cache, vi, cache_dtype, v_scale);
+    }
   }
   for (int d = 0; d < head_dim; ++d) out_row[d] /= z;
   free(x);
   return ORACLE_OK;
+}
+
+/* 16-bit caches: K and V elements are values of the q type (scale 1, exact). */
+int oracle_decode_row(double *out_row, const uint16_t *q, const uint16_t *k_cache,
+                      const uint16_t *v_cache, const int32_t *block_tables,
+                      const int32_t *context_lens, double scale, int block_size,
+                      int num_kv_heads, int num_seqs, int num_heads, int head_dim,
+                      int max_blocks_per_seq, int64_t num_blocks, int dtype, int s,
+                      int h) {
+  return decode_row_any(out_row, q, k_cache, v_cache, block_tables, context_lens, scale,
+                        block_size, num_kv_heads, num_seqs, num_heads, head_dim,
+                        max_blocks_per_seq, num_blocks, dtype, dtype, 1.0, 1.0, s, h);
 }
 
 /* Every (sequence, query head) row; out is [num_seqs][num_heads][head_dim]. */
@@ -363,3 +445,94 @@ int oracle_decode_row_partitioned(double *out_row, const uint16_t *q,
   free(pm); free(pl); free(po); free(x);
   return rc;
 }
+
+/* ---- FP8 (E4M3) KV cache ------------------------------------------------- */
+
+/* "Advanced optimisation directions" of the PagedAttention 20x page,
+ * mixed precision: attention in FP8, the rest in FP16.  Read here as an E4M3
+ * KV cache with one scale per tensor: an element x of the new token's K (or
+ * V) is stored as the code nearest to float32(x) * float32(1 / k_scale),
+ * the product rounded to float32 as written; it stands for code * k_scale.
+ * Same slots, checks and layouts as oracle_kv_write, one byte per element. */
+int oracle_kv_write_fp8(const uint16_t *k, const uint16_t *v,
+                        const int64_t *slot_mapping, uint8_t *k_cache, uint8_t *v_cache,
+                        int64_t num_tokens, int num_kv_heads, int head_dim,
+                        int block_size, int64_t num_blocks, int dtype, float k_scale,
+                        float v_scale) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || (dtype != ORACLE_F16 && dtype != ORACLE_BF16) ||
+      !(k_scale > 0.0f) || !(v_scale > 0.0f) || isinf(k_scale) || isinf(v_scale))
+    return ORACLE_EARG;
+  int64_t num_slots = num_blocks * block_size;
+  unsigned char *seen = calloc((size_t)num_slots, 1);
+  if (!seen) return ORACLE_ENOMEM;
+  for (int64_t i = 0; i < num_tokens; ++i) {
+    int64_t slot = slot_mapping[i];
+    if (slot < 0) continue;
+    if (slot >= num_slots || seen[slot]) {
+      free(seen);
+      return ORACLE_ESLOT;
+    }
+    seen[slot] = 1;
+  }
+  free(seen);
+
+  const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;
+  for (int64_t i = 0; i < num_tokens; ++i) {
+    int64_t slot = slot_mapping[i];
+    if (slot < 0) continue;
+    int64_t block = slot / block_size;
+    int offset = (int)(slot % block_size);
+    for (int j = 0; j < num_kv_heads; ++j) {
+      for (int d = 0; d < head_dim; ++d) {
+        int64_t src = (i * num_kv_heads + j) * (int64_t)head_dim + d;
+        float kx = (float)decode(k[src], dtype) * k_inv;
+        float vx = (float)decode(v[src], dtype) * v_inv;
+        k_cache[((block * num_kv_heads + j) * (int64_t)block_size + offset) * head_dim + d] =
+            oracle_f64_to_e4m3((double)kx);
+        v_cache[((block * num_kv_heads + j) * (int64_t)head_dim + d) * block_size + offset] =
+            oracle_f64_to_e4m3((double)vx);
+      }
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Decode attention over an E4M3 cache: K = code * k_scale, V = code *
+ * v_scale (exact in double), q and the result as for the 16-bit caches. */
+int oracle_decode_fp8(double *out, const uint16_t *q, const uint8_t *k_cache,
+                      const uint8_t *v_cache, const int32_t *block_tables,
+                      const int32_t *context_lens, double scale, int block_size,
+                      int num_kv_heads, int num_seqs, int num_heads, int head_dim,
+                      int max_blocks_per_seq, int64_t num_blocks, int q_dtype,
+                      double k_scale, double v_scale) {
+  for (int s = 0; s < num_seqs; ++s)
+    for (int h = 0; h < num_heads; ++h) {
+      int rc = decode_row_any(out + ((int64_t)s * num_heads + h) * head_dim, q, k_cache,
+                              v_cache, block_tables, context_lens, scale, block_size,
+                              num_kv_heads, num_seqs, num_heads, head_dim,
+                              max_blocks_per_seq, num_blocks, q_dtype, ORACLE_FP8,
+                              k_scale, v_scale, s, h);
+      if (rc != ORACLE_OK) return rc;
+    }
+  return ORACLE_OK;
+}
+
+/* Selected rows of oracle_decode_fp8 (rows as in oracle_decode_rows). */
+int oracle_decode_fp8_rows(double *out, const int32_t *rows, int num_rows,
+                           const uint16_t *q, const uint8_t *k_cache,
+                           const uint8_t *v_cache, const int32_t *block_tables,
+                           const int32_t *context_lens, double scale, int block_size,
+                           int num_kv_heads, int num_seqs, int num_heads, int head_dim,
+                           int max_blocks_per_seq, int64_t num_blocks, int q_dtype,
+                           double k_scale, double v_scale) {
+  for (int i = 0; i < num_rows; ++i) {
+    int rc = decode_row_any(out + (int64_t)i * head_dim, q, k_cache, v_cache, block_tables,
+                            context_lens, scale, block_size, num_kv_heads, num_seqs,
+                            num_heads, head_dim, max_blocks_per_seq, num_blocks, q_dtype,
+                            ORACLE_FP8, k_scale, v_scale, rows[2 * i], rows[2 * i + 1]);
+    if (rc != ORACLE_OK) return rc;
+  }
+  return ORACLE_OK;
+}
+

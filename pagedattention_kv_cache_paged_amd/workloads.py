@@ -37,6 +37,7 @@ import numpy as np
 F16 = "f16"
 BF16 = "bf16"
 NAN_BITS = {F16: 0x7E00, BF16: 0x7FC0}
+FP8_NAN = 0x7F  # E4M3 (e4m3fn) NaN code
 ELEM_BYTES = 2
 
 _STREAM_LENGTHS, _STREAM_PLACEMENT, _STREAM_DATA = 0, 1, 2
@@ -215,6 +216,11 @@ class Workload:
         ks, vs = self.cache_shapes()
         nan = np.uint16(NAN_BITS[self.dtype])
         return np.full(ks, nan, dtype=np.uint16), np.full(vs, nan, dtype=np.uint16)
+
+    def nan_caches_fp8(self):
+        """Host E4M3 K and V caches (one byte per element) filled with NaN."""
+        ks, vs = self.cache_shapes()
+        return (np.full(ks, FP8_NAN, dtype=np.uint8), np.full(vs, FP8_NAN, dtype=np.uint8))
 
 
 def build(name: str, lengths: Sequence[int], *, num_heads: int, num_kv_heads: int,

@@ -1,0 +1,195 @@
+"""Pins of the oracle's FP8 cache functions against things other than
+itself (no GPU).
+
+"vLLM framework analysis: how PagedAttention speeds up LLM inference 20x"
+(intelliparadigm.com), 7, suggests FP8 for the attention computation and
+FP16 for the rest.  The oracle reads that as an OCP E4M3 ("e4m3fn") KV cache
+with one scale per tensor: the append stores the code nearest to
+float32(x) * float32(1 / scale), saturating at +-448, and the decode reads
+code * scale.  Pinned here:
+
+* decoder: all 256 codes against torch's float8_e4m3fn -> float32;
+* encoder: brute force over all finite codes (nearest, ties to the code with
+  an even fraction) at every midpoint and next to it, at random values, in
+  the saturation range and for NaN; and against torch's own rounding where
+  torch does not turn overflow into NaN (|y| < 464);
+* append: every stored code equals torch's rounding of the float32 product,
+  at the documented (block, head, offset, dim) place; padding is skipped;
+* decode: equals numpy brute force over the dequantised logical K and V; and
+  with E4M3-exact data and scale 1 it equals the 16-bit oracle bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from pagedattention_kv_cache_paged_amd import workloads as W
+
+F8 = torch.float8_e4m3fn
+
+
+def torch_values(codes):
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(F8).to(torch.float64).numpy()
+
+
+def test_decoder_all_codes():
+    ref = torch_values(np.arange(256))
+    got = np.array([oracle.e4m3_to_f64(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def _finite_positive():
+    codes = np.array([c for c in range(0x7F)])          # 0x00 .. 0x7E
+    return codes, torch_values(codes)
+
+
+def brute_force(y):
+    """Nearest finite code by exhaustive search; ties to the even code."""
+    if math.isnan(y):
+        return 0x7F
+    sign = 0x80 if math.copysign(1.0, y) < 0 else 0
+    a = abs(y)
+    codes, vals = _finite_positive()
+    if a >= 448.0:
+        return sign | 0x7E
+    d = np.abs(vals - a)
+    best = np.flatnonzero(d == d.min())
+    if best.size > 1:
+        best = best[(codes[best] & 1) == 0]
+    return sign | int(codes[best[0]])
+
+
+def test_encoder_brute_force():
+    _, vals = _finite_positive()
+    mids = (vals[:-1] + vals[1:]) / 2
+    eps = np.concatenate([mids * (1 + 2.0 ** -20), mids * (1 - 2.0 ** -20)])
+    g = np.random.default_rng(3)
+    rnd = np.concatenate([g.uniform(0, 2.0 ** -6, 300), 2.0 ** g.uniform(-12, 9, 700)])
+    ys = np.concatenate([vals, mids, eps, rnd, [447.9, 448.0, 455.99, 464.0, 1e6, np.inf]])
+    ys = np.concatenate([ys, -ys, [np.nan, -0.0, 0.0]])
+    for y in ys:
+        assert oracle.f64_to_e4m3(float(y)) == brute_force(float(y)), y
+
+
+def test_encoder_matches_torch_below_overflow():
+    g = np.random.default_rng(4)
+    y = (g.standard_normal(20000) * 60).astype(np.float32)
+    y = y[np.abs(y) < 464]
+    ref = torch.from_numpy(y).to(F8).view(torch.uint8).numpy()
+    got = np.array([oracle.f64_to_e4m3(float(v)) for v in y], np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def _torch_quantise(bits, dtype, scale):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    t = t.view(torch.float16 if dtype == W.F16 else torch.bfloat16).to(torch.float32)
+    inv = torch.tensor(1.0, dtype=torch.float32) / torch.tensor(scale, dtype=torch.float32)
+    y = t * inv
+    assert float(y.abs().max()) < 464
+    return y.to(F8).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("bs,dtype,ks,vs", [(16, W.BF16, 0.0371, 0.0123),
+                                            (8, W.F16, 0.5, 0.25), (32, W.BF16, 1.0, 2.0)])
+def test_append_codes_and_places(bs, dtype, ks, vs):
+    w = W.build("f8w", [5, 37, 64], num_heads=8, num_kv_heads=2, head_dim=64, block_size=bs,
+                dtype=dtype, seed=8, pool=40)
+    kc, vc = w.nan_caches_fp8()
+    oracle.kv_write_fp8(w.token_k, w.token_v, w.token_slot, kc, vc, bs, dtype, ks, vs)
+    kq = _torch_quantise(w.token_k, dtype, ks)
+    vq = _torch_quantise(w.token_v, dtype, vs)
+    written = np.zeros(kc.shape[0] * bs, bool)
+    for i, slot in enumerate(w.token_slot):
+        b, o = divmod(int(slot), bs)
+        written[slot] = True
+        assert np.array_equal(kc[b, :, o, :], kq[i])
+        assert np.array_equal(vc[b, :, :, o], vq[i])
+    # every other slot is untouched
+    k_slots = kc.transpose(0, 2, 1, 3).reshape(-1, kc.shape[1] * kc.shape[3])
+    assert np.all(k_slots[~written] == W.FP8_NAN)
+
+
+def test_append_skips_padding_and_refuses_bad_slots():
+    w = W.tiny()
+    kc, vc = w.nan_caches_fp8()
+    k, v, s = w.write_batch("new")
+    s = s.copy()
+    s[1] = -1
+    oracle.kv_write_fp8(k, v, s, kc, vc, 16, w.dtype, 0.25, 0.25)
+    b, o = divmod(int(w.write_batch("new")[2][1]), 16)
+    assert np.all(kc[b, :, o, :] == W.FP8_NAN)
+    s[2] = s[0]
+    with pytest.raises(oracle.OracleError):
+        oracle.kv_write_fp8(k, v, s, kc, vc, 16, w.dtype, 0.25, 0.25)
+
+
+def dense_fp8(w, kc, vc, ks, vs):
+    """Brute force from the dequantised cache read through the tables."""
+    G, bs = w.group, w.block_size
+    out = np.zeros((w.num_seqs, w.num_heads, w.head_dim))
+    qf = (w.q.astype(np.uint32) << 16).view(np.float32).astype(np.float64) if w.dtype == W.BF16 \
+        else w.q.view(np.float16).astype(np.float64)
+    kval = torch_values(kc.reshape(-1)).reshape(kc.shape) * ks
+    vval = torch_values(vc.reshape(-1)).reshape(vc.shape) * vs
+    for s in range(w.num_seqs):
+        L = int(w.context_lens[s])
+        blocks = [w.block_tables[s][t // bs] for t in range(L)]
+        for h in range(w.num_heads):
+            j = h // G
+            K = np.stack([kval[blocks[t], j, t % bs, :] for t in range(L)])
+            V = np.stack([vval[blocks[t], j, :, t % bs] for t in range(L)])
+            x = K @ qf[s, h] * w.scale
+            p = np.exp(x - x.max())
+            out[s, h] = p @ V / p.sum()
+    return out
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_decode_brute_force(bs):
+    w = W.build("f8d", [1, 9, 40, 77], num_heads=8, num_kv_heads=2, head_dim=64,
+                block_size=bs, dtype=W.BF16, seed=20 + bs)
+    kc, vc = w.nan_caches_fp8()
+    oracle.kv_write_fp8(w.token_k, w.token_v, w.token_slot, kc, vc, bs, w.dtype, 0.03, 0.05)
+    got = oracle.decode_fp8(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, bs,
+                            w.dtype, 0.03, 0.05)
+    ref = dense_fp8(w, kc, vc, 0.03, 0.05)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_decode_equals_16bit_oracle_on_e4m3_exact_data():
+    """Token values that are E4M3 values (exact in bfloat16) with scale 1:
+    the FP8 cache then stands for the same numbers as the 16-bit cache."""
+    w = W.build("f8x", [3, 30, 100], num_heads=4, num_kv_heads=2, head_dim=64,
+                block_size=16, dtype=W.BF16, seed=33)
+    _, vals = _finite_positive()
+    g = np.random.default_rng(5)
+    pick = lambda shape: (vals[g.integers(0, 0x60, size=shape)] *
+                          g.choice([-1.0, 1.0], size=shape)).astype(np.float32)
+    w.token_k = W.to_bits(pick(w.token_k.shape), W.BF16)
+    w.token_v = W.to_bits(pick(w.token_v.shape), W.BF16)
+    k16, v16 = w.nan_caches()
+    oracle.kv_write(w.token_k, w.token_v, w.token_slot, k16, v16, 16)
+    k8, v8 = w.nan_caches_fp8()
+    oracle.kv_write_fp8(w.token_k, w.token_v, w.token_slot, k8, v8, 16, w.dtype, 1.0, 1.0)
+    a = oracle.decode(w.q, k16, v16, w.block_tables, w.context_lens, w.scale, 16, w.dtype)
+    b = oracle.decode_fp8(w.q, k8, v8, w.block_tables, w.context_lens, w.scale, 16, w.dtype,
+                          1.0, 1.0)
+    assert np.array_equal(a, b)
+
+
+def test_rows_equal_full_fp8():
+    w = W.build("f8r", [20, 70], num_heads=8, num_kv_heads=4, head_dim=64, block_size=16,
+                dtype=W.F16, seed=41)
+    kc, vc = w.nan_caches_fp8()
+    oracle.kv_write_fp8(w.token_k, w.token_v, w.token_slot, kc, vc, 16, w.dtype, 0.1, 0.1)
+    full = oracle.decode_fp8(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, 16,
+                             w.dtype, 0.1, 0.1)
+    rows = np.array([(0, 3), (1, 7), (1, 0)], np.int32)
+    part = oracle.decode_fp8_rows(rows, w.q, kc, vc, w.block_tables, w.context_lens,
+                                  w.scale, 16, w.dtype, 0.1, 0.1)
+    assert np.array_equal(part, full[rows[:, 0], rows[:, 1]])

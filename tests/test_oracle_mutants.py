@@ -2,8 +2,8 @@
 
 Each case plants one mistake in a copy of oracle/oracle.c (a dropped term, a
 wrong sign, index or layout, a transposed operand), builds it on the CPU into
-a temporary library and runs tests/test_oracle_pins.py against that library
-in a subprocess.  The pin suite must fail for every mutant and pass for the
+a temporary library and runs tests/test_oracle_pins.py and
+tests/test_oracle_fp8.py against that library in a subprocess.  The pin suite must fail for every mutant and pass for the
 unmodified copy.
 """
 import concurrent.futures as cf
@@ -16,7 +16,8 @@ import pytest
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+PINS = [os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+        os.path.join(ROOT, "tests", "test_oracle_fp8.py")]
 
 # (name, original text, planted text) -- the first occurrence is replaced
 MUTANTS = [
@@ -30,13 +31,29 @@ MUTANTS = [
     ("first_token_dropped",
      "for (int64_t t = 0; t < len; ++t) {\n    int64_t block = table[t / block_size];\n    int offset",
      "for (int64_t t = 1; t < len; ++t) {\n    int64_t block = table[t / block_size];\n    int offset"),
-    ("v_read_token_major", "return v_cache[base * block_size + offset];",
-     "return v_cache[((block * num_kv_heads + kv_head) * (int64_t)block_size + offset)"
-     " * head_dim + dim];"),
+    ("v_read_token_major",
+     "int64_t vi = ((block * num_kv_heads + kv_head) * (int64_t)head_dim + d) *\n"
+     "                       block_size + offset;",
+     "int64_t vi = ((block * num_kv_heads + kv_head) * (int64_t)block_size + offset) *\n"
+     "                       head_dim + d;"),
     ("v_both_token_major",
-     "return v_cache[base * block_size + offset];",
-     "return v_cache[((block * num_kv_heads + kv_head) * (int64_t)block_size + offset)"
-     " * head_dim + dim];"),
+     "int64_t vi = ((block * num_kv_heads + kv_head) * (int64_t)head_dim + d) *\n"
+     "                       block_size + offset;",
+     "int64_t vi = ((block * num_kv_heads + kv_head) * (int64_t)block_size + offset) *\n"
+     "                       head_dim + d;"),
+    ("k_offset_shift", "(int)(t % block_size)) * head_dim;",
+     "(int)((t + 1) % block_size)) * head_dim;"),
+    # E4M3 coding and the FP8 append
+    ("e4m3_bias", "expo - 10); /* 1.frac", "expo - 9); /* 1.frac"),
+    ("e4m3_ties_up", "(above == below && fmod(n, 2.0) != 0.0)", "(above == below)"),
+    ("e4m3_no_saturation", "if (a >= 448.0) return (uint8_t)((sign << 7) | 0x7e);",
+     "if (a >= 448.0) return (uint8_t)((sign << 7) | 0x7f);"),
+    ("e4m3_subnormal_step", "u = ldexp(1.0, -9);\n", "u = ldexp(1.0, -8);\n"),
+    ("fp8_scale_multiplied", "float kx = (float)decode(k[src], dtype) * k_inv;",
+     "float kx = (float)decode(k[src], dtype) * k_scale;"),
+    ("fp8_v_scale_for_k",
+     "return oracle_e4m3_to_f64(((const uint8_t *)cache)[index]) * scale;",
+     "return oracle_e4m3_to_f64(((const uint8_t *)cache)[index]);"),
     ("f16_bias", "expo - 25); /* 1.frac", "expo - 24); /* 1.frac"),
     ("bf16_bias", "expo - 134); /* 1.frac", "expo - 133); /* 1.frac"),
     ("f16_sign_dropped", "return sign ? -mag : mag;", "return mag;"),
@@ -70,7 +87,7 @@ def _build_variant(tmp, name, old, new):
 
 def _run_pins(lib):
     env = dict(os.environ, PAGED_ORACLE_LIB=lib)
-    r = subprocess.run([sys.executable, "-m", "pytest", PINS, "-x", "-q", "-p",
+    r = subprocess.run([sys.executable, "-m", "pytest", *PINS, "-x", "-q", "-p",
                         "no:cacheprovider"], cwd=ROOT, env=env, capture_output=True,
                        text=True, timeout=600)
     return r.returncode, r.stdout[-2000:]
