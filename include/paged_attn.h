@@ -173,6 +173,40 @@ int paged_attention_decode_stages(void *out, const void *q, const void *k_cache,
                                   void *stream);
 
 /*
+ * FP8 KV cache ("vLLM framework analysis: how PagedAttention speeds up LLM
+ * inference 20x" (intelliparadigm.com), 7: FP8 for the attention
+ * computation, FP16 for the rest).  The caches hold OCP E4M3 ("e4m3fn")
+ * codes, one byte per element, in the layouts above; a K code c stands for
+ * c * k_scale and a V code for c * v_scale (one scale per tensor, finite and
+ * positive).  q, out, k and v stay 16-bit (dtype).
+ *
+ * paged_kv_write_fp8: the append of paged_kv_write, quantising: element x
+ * of k goes in as the E4M3 code nearest to float32(x) * float32(1/k_scale)
+ * (ties to the even code; finite magnitudes from 448 up saturate to +-448;
+ * NaN stays NaN), v likewise with v_scale.  Caches 16-byte aligned.
+ */
+int paged_kv_write_fp8(const void *k, const void *v, const int64_t *slot_mapping,
+                       void *k_cache, void *v_cache, int64_t num_tokens,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int64_t num_blocks, int32_t dtype, float k_scale, float v_scale,
+                       void *stream);
+
+/*
+ * paged_attention_decode_stages over E4M3 caches: the same attention with
+ * K_t = code * k_scale and V_t = code * v_scale.  The codes are converted to
+ * the q type exactly in registers; k_scale joins the score scale and v_scale
+ * the output.  Workspace as for the 16-bit caches.
+ */
+int paged_attention_decode_fp8(void *out, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *block_tables,
+                               const int32_t *context_lens, float scale, float k_scale,
+                               float v_scale, int32_t block_size, int32_t num_kv_heads,
+                               int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                               int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                               int32_t partition_tokens, void *workspace,
+                               size_t workspace_bytes, int32_t stages, void *stream);
+
+/*
  * Host-side check of metadata (host pointers): every context length in
  * [0, max_blocks_per_seq * block_size]; every table entry a sequence reads,
  * i.e. the first ceil(L / block_size) of its row, in [0, num_blocks); every

@@ -4,7 +4,8 @@ The compute lives in libpaged_attn.so (C ABI in include/paged_attn.h);
 ``binding`` wraps it for torch tensors.  Binding names are imported lazily so
 that the input generator (``workloads``) can be used without torch.
 """
-_BINDING = ("paged_kv_write", "paged_attention_decode", "split_waves",
+_BINDING = ("paged_kv_write", "paged_attention_decode", "paged_kv_write_fp8",
+            "paged_attention_decode_fp8", "split_waves",
             "workspace_bytes", "validate_metadata", "PagedAttentionError", "load")
 
 __all__ = list(_BINDING)

@@ -71,6 +71,11 @@ def load() -> ctypes.CDLL:
     lib.paged_attention_decode_ex.argtypes = dec + [i32, p, sz, p]
     lib.paged_attention_decode_stages.restype = ctypes.c_int
     lib.paged_attention_decode_stages.argtypes = dec + [i32, p, sz, i32, p]
+    lib.paged_kv_write_fp8.restype = ctypes.c_int
+    lib.paged_kv_write_fp8.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i64, i32, f32, f32, p]
+    lib.paged_attention_decode_fp8.restype = ctypes.c_int
+    lib.paged_attention_decode_fp8.argtypes = [p, p, p, p, p, p, f32, f32, f32, i32, i32, i32,
+                                               i32, i32, i32, i64, i32, i32, p, sz, i32, p]
     lib.paged_validate_metadata.restype = ctypes.c_int
     lib.paged_validate_metadata.argtypes = [p, p, i32, i32, i32, i64, p, i64]
     _lib = lib
@@ -209,3 +214,73 @@ def validate_metadata(block_tables, context_lens, block_size: int, num_blocks: i
     return int(load().paged_validate_metadata(
         bt.ctypes.data, cl.ctypes.data, cl.size, bt.shape[1], block_size, num_blocks,
         None if sm is None else sm.ctypes.data, 0 if sm is None else sm.size))
+
+
+# ---- FP8 (E4M3) caches -----------------------------------------------------
+
+def paged_kv_write_fp8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                       k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float,
+                       v_scale: float) -> None:
+    """Quantise k, v [T, Hkv, D] (fp16 / bf16) into E4M3 caches: uint8
+    k_cache [N, Hkv, bs, D] and v_cache [N, Hkv, D, bs], at slot_mapping."""
+    dev = _dev(k, v, slot_mapping, k_cache, v_cache)
+    if k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("k and v must be [num_tokens, num_kv_heads, head_dim]")
+    T, hkv, d = k.shape
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("FP8 caches are uint8 tensors of E4M3 codes")
+    if k_cache.dim() != 4 or k_cache.shape[1] != hkv or k_cache.shape[3] != d:
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    nb, _, bs, _ = k_cache.shape
+    if tuple(v_cache.shape) != (nb, hkv, d, bs):
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size]")
+    if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (T,):
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    dt = _dtype(k)
+    if v.dtype != k.dtype:
+        raise ValueError("k and v must share one dtype")
+    rc = load().paged_kv_write_fp8(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                                   k_cache.data_ptr(), v_cache.data_ptr(), T, hkv, d, bs, nb,
+                                   dt, float(k_scale), float(v_scale), _stream(dev))
+    _check("paged_kv_write_fp8", rc)
+
+
+def paged_attention_decode_fp8(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                               v_cache: torch.Tensor, block_tables: torch.Tensor,
+                               context_lens: torch.Tensor, scale: float, k_scale: float,
+                               v_scale: float, block_size: int, num_kv_heads: int,
+                               partition_tokens: int = 0, stages: int = 3,
+                               workspace_tensor: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """paged_attention_decode over E4M3 caches (uint8 tensors, layouts as
+    for the 16-bit caches) with K = code * k_scale, V = code * v_scale."""
+    dev = _dev(out, q, k_cache, v_cache, block_tables, context_lens)
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be [num_seqs, num_heads, head_dim]")
+    B, hq, d = q.shape
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("FP8 caches are uint8 tensors of E4M3 codes")
+    if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (num_kv_heads, block_size, d):
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    nb = k_cache.shape[0]
+    if tuple(v_cache.shape) != (nb, num_kv_heads, d, block_size):
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [num_seqs, max_blocks_per_seq]")
+    if context_lens.dtype != torch.int32 or tuple(context_lens.shape) != (B,):
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    dt = _dtype(q)
+    if out.dtype != q.dtype:
+        raise ValueError("q and out must share one dtype")
+    mb = block_tables.shape[1]
+    need = workspace_bytes(B, hq, num_kv_heads, d, mb, block_size, partition_tokens)
+    ws = workspace_tensor if workspace_tensor is not None else workspace(dev, need)
+    ws_ptr = ws.data_ptr() if ws is not None else None
+    ws_len = ws.numel() * ws.element_size() if ws is not None else 0
+    rc = load().paged_attention_decode_fp8(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), float(k_scale),
+        float(v_scale), block_size, num_kv_heads, B, hq, d, mb, nb, dt, partition_tokens,
+        ws_ptr, ws_len, stages, _stream(dev))
+    _check("paged_attention_decode_fp8", rc)
+    return out
+

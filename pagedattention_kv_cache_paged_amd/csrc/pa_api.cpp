@@ -16,6 +16,8 @@ constexpr int64_t kMaxGrid = 65535;  // bound on head counts and tokens per grid
 bool supported_dim(int32_t d) { return d == 64 || d == 128; }
 bool supported_bs(int32_t b) { return b == 8 || b == 16 || b == 32; }
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+// A tensor scale of an E4M3 cache: finite, positive, with a finite reciprocal.
+bool valid_scale(float s) { return std::isfinite(s) && s > 0.0f && std::isfinite(1.0f / s); }
 
 bool valid_partition(int32_t pt) {
   return pt == 0 || (pt >= pa::kTile && pt % pa::kTile == 0 &&
@@ -72,7 +74,7 @@ bool decode_sizes_ok(int32_t num_seqs, int32_t num_kv_heads, int32_t num_heads,
 
 extern "C" {
 
-int pa_abi_version(void) { return 2; }
+int pa_abi_version(void) { return 3; }
 
 const char *pa_strerror(int code) {
   switch (code) {
@@ -113,34 +115,52 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
   return (size_t)ws_layout(num_seqs, num_heads, head_dim, w).total;
 }
 
-int paged_kv_write(const void *k, const void *v, const int64_t *slot_mapping, void *k_cache,
-                   void *v_cache, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
-                   int32_t block_size, int64_t num_blocks, int32_t dtype, void *stream) {
+static int kv_write_common(const void *k, const void *v, const int64_t *slot_mapping,
+                           void *k_cache, void *v_cache, int64_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int64_t num_blocks, int32_t dtype, int fp8, float k_scale,
+                           float v_scale, void *stream) {
   if (dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_DTYPE;
   if (num_tokens < 0 || num_tokens > INT32_MAX || num_kv_heads <= 0 || num_kv_heads > kMaxGrid ||
       !supported_dim(head_dim) || !supported_bs(block_size) || num_blocks <= 0 ||
       num_blocks > INT64_MAX / ((int64_t)block_size * num_kv_heads * head_dim))
     return PA_ERR_SHAPE;
+  if (fp8 && !(valid_scale(k_scale) && valid_scale(v_scale))) return PA_ERR_SHAPE;
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(slot_mapping, 8))
     return PA_ERR_ALIGN;
   pa::WriteArgs a{k, v, slot_mapping, k_cache, v_cache, num_tokens, num_kv_heads, head_dim,
-                  block_size, num_blocks, stream};
+                  block_size, num_blocks, dtype, fp8, 1.0f / k_scale, 1.0f / v_scale, stream};
   return pa::launch_kv_write(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
 }
 
-int paged_attention_decode_stages(void *out, const void *q, const void *k_cache,
-                                  const void *v_cache, const int32_t *block_tables,
-                                  const int32_t *context_lens, float scale, int32_t block_size,
-                                  int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
-                                  int32_t head_dim, int32_t max_blocks_per_seq,
-                                  int64_t num_blocks, int32_t dtype, int32_t partition_tokens,
-                                  void *workspace, size_t workspace_bytes, int32_t stages,
-                                  void *stream) {
+int paged_kv_write(const void *k, const void *v, const int64_t *slot_mapping, void *k_cache,
+                   void *v_cache, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int64_t num_blocks, int32_t dtype, void *stream) {
+  return kv_write_common(k, v, slot_mapping, k_cache, v_cache, num_tokens, num_kv_heads,
+                         head_dim, block_size, num_blocks, dtype, 0, 1.0f, 1.0f, stream);
+}
+
+int paged_kv_write_fp8(const void *k, const void *v, const int64_t *slot_mapping,
+                       void *k_cache, void *v_cache, int64_t num_tokens, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
+                       float k_scale, float v_scale, void *stream) {
+  return kv_write_common(k, v, slot_mapping, k_cache, v_cache, num_tokens, num_kv_heads,
+                         head_dim, block_size, num_blocks, dtype, 1, k_scale, v_scale, stream);
+}
+
+static int decode_common(void *out, const void *q, const void *k_cache, const void *v_cache,
+                         const int32_t *block_tables, const int32_t *context_lens, float scale,
+                         int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                         int32_t num_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                         int64_t num_blocks, int32_t dtype, int32_t partition_tokens,
+                         void *workspace, size_t workspace_bytes, int32_t stages, int fp8,
+                         float k_scale, float v_scale, void *stream) {
   if (dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_DTYPE;
   if (stages < 1 || stages > 3) return PA_ERR_SHAPE;
+  if (fp8 && !(valid_scale(k_scale) && valid_scale(v_scale))) return PA_ERR_SHAPE;
   if (!decode_sizes_ok(num_seqs, num_kv_heads, num_heads, head_dim, max_blocks_per_seq,
                        block_size) ||
       num_blocks <= 0 || num_blocks > INT32_MAX || !std::isfinite(scale) ||
@@ -160,10 +180,39 @@ int paged_attention_decode_stages(void *out, const void *q, const void *k_cache,
   char *ws = static_cast<char *>(workspace);
   pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                    num_kv_heads, num_seqs, num_heads, head_dim, max_blocks_per_seq, num_blocks,
-                   dtype, (int32_t)waves, (int32_t)(waves + num_seqs),
+                   dtype, fp8, fp8 ? k_scale : 1.0f, fp8 ? v_scale : 1.0f,
+                   (int32_t)waves, (int32_t)(waves + num_seqs),
                    reinterpret_cast<float *>(ws + l.o), reinterpret_cast<float *>(ws + l.ml),
                    reinterpret_cast<int32_t *>(ws + l.cu), stages, stream};
   return pa::launch_decode(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int paged_attention_decode_stages(void *out, const void *q, const void *k_cache,
+                                  const void *v_cache, const int32_t *block_tables,
+                                  const int32_t *context_lens, float scale, int32_t block_size,
+                                  int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                                  int32_t head_dim, int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, int32_t dtype, int32_t partition_tokens,
+                                  void *workspace, size_t workspace_bytes, int32_t stages,
+                                  void *stream) {
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                       num_kv_heads, num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                       num_blocks, dtype, partition_tokens, workspace, workspace_bytes, stages,
+                       0, 1.0f, 1.0f, stream);
+}
+
+int paged_attention_decode_fp8(void *out, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *block_tables,
+                               const int32_t *context_lens, float scale, float k_scale,
+                               float v_scale, int32_t block_size, int32_t num_kv_heads,
+                               int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                               int32_t max_blocks_per_seq, int64_t num_blocks, int32_t dtype,
+                               int32_t partition_tokens, void *workspace,
+                               size_t workspace_bytes, int32_t stages, void *stream) {
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                       num_kv_heads, num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                       num_blocks, dtype, partition_tokens, workspace, workspace_bytes, stages,
+                       1, k_scale, v_scale, stream);
 }
 
 int paged_attention_decode_ex(void *out, const void *q, const void *k_cache, const void *v_cache,

@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -77,6 +79,12 @@ struct Elem<kBF16> {
     f32x2 f = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
   }
+  // four E4M3 codes (bytes 0..3) -> four bfloat16 values, exact
+  static __device__ __forceinline__ u32x2 from_e4m3(uint32_t c) {
+    return u32x2{
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, true))};
+  }
   static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
   static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 };
@@ -95,6 +103,12 @@ struct Elem<kF16> {
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
     f32x2 f = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+  }
+  // four E4M3 codes (bytes 0..3) -> four binary16 values, exact
+  static __device__ __forceinline__ u32x2 from_e4m3(uint32_t c) {
+    return u32x2{
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c, 1.0f, true))};
   }
   static __device__ __forceinline__ float lo(uint32_t w) {
     return (float)__builtin_bit_cast(f16x2, w)[0];
@@ -139,25 +153,36 @@ __device__ __forceinline__ int wave_of(int tau, int n, int w) {
   return (int)((((int64_t)tau + 1) * w - 1) / n);
 }
 
-// K and V registers of one 16-token tile.
+// K and V registers of one 16-token tile as loaded: 16-bit values, or E4M3
+// codes (KV8) that step() converts to the q type before the MFMAs.
+template <int D, bool KV8>
+struct Frag;
 template <int D>
-struct Frag {
-  u32x4 k[D / 32];
-  u32x2 v[D / 16];
+struct Frag<D, false> {
+  u32x4 k[D / 32];  // one 16x16x32 A fragment per k-step
+  u32x2 v[D / 16];  // 4 tokens of one dimension per 16-dim tile
+};
+template <int D>
+struct Frag<D, true> {
+  u32x4 k[D / 64];     // 16 codes = two k-steps
+  uint32_t v[D / 16];  // 4 token codes of one dimension per 16-dim tile
 };
 
 // Tiles in flight per wave (register ring depth).
 constexpr int kBuf = 2;
 
-template <int DT, int D, int BS>
+// KV8: the caches hold E4M3 codes; scale_log2 then carries k_scale and
+// out_scale is v_scale (1 for 16-bit caches).
+template <int DT, int D, int BS, bool KV8>
 __global__ __launch_bounds__(kWave) void decode_split_kernel(
     uint16_t *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml,
     int32_t *__restrict__ ws_cu, const uint16_t *__restrict__ q,
-    const uint16_t *__restrict__ k_cache, const uint16_t *__restrict__ v_cache,
+    const void *__restrict__ k_cache, const void *__restrict__ v_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    float scale_log2, int num_seqs, int num_kv_heads, int num_heads, int group,
-    int max_blocks, int64_t num_blocks, int waves, int slots) {
+    float scale_log2, float out_scale, int num_seqs, int num_kv_heads, int num_heads,
+    int group, int max_blocks, int64_t num_blocks, int waves, int slots) {
   using E = Elem<DT>;
+  using CT = std::conditional_t<KV8, uint8_t, uint16_t>;  // cache element
   constexpr int KSTEPS = D / 32;  // 16x16x32 MFMAs per QK tile
   constexpr int DTILES = D / 16;  // 16x16x16 MFMAs per PV tile
   // LDS: cu[num_seqs + 1], lens[num_seqs], then (16-byte aligned) the
@@ -244,15 +269,21 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   const uint64_t ends = __ballot(seg_end && lane < cnt);  // bit i: a segment ends at tile i
 
   // Query fragment of the current segment and, one segment ahead, of the
-  // next (lane (row, grp) holds q[head row][32*ks + 8*grp .. +8]).  Padded
-  // head lanes (row >= group) read a real query row and compute values that
-  // are never stored.
+  // next.  Lane (row, grp) holds 8 dims of head row per k-step: dims
+  // 32*ks + 8*grp .. +8 for 16-bit caches; for E4M3 caches, whose lanes
+  // load 16 codes at once, dims 64*(ks/2) + 16*grp + 8*(ks%2) .. +8 (the
+  // same permutation of the dimensions on both operands of the dot product).
+  // Padded head lanes (row >= group) read a real query row and compute
+  // values that are never stored.
   const int qh = kvh * group + min(row, group - 1);
   auto load_q = [&](u32x4 (&dst)[KSTEPS], int idx) {
     const int s = __builtin_amdgcn_readlane(sq, idx);
-    const uint16_t *qp = q + ((int64_t)s * num_heads + qh) * D + grp * 8;
+    const uint16_t *qp = q + ((int64_t)s * num_heads + qh) * D;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) dst[ks] = *(const u32x4 *)(qp + ks * 32);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int d0 = KV8 ? 64 * (ks / 2) + 16 * grp + 8 * (ks % 2) : 32 * ks + 8 * grp;
+      dst[ks] = *(const u32x4 *)(qp + d0);
+    }
   };
   // first tile of the segment after the one ending at tile `e` (cnt - 1 if none)
   auto next_first = [&](int e) {
@@ -269,15 +300,15 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   __builtin_amdgcn_sched_barrier(0);
   load_q(qnext, next_first(__builtin_ctzll(ends)));
   const int64_t blk_stride = (int64_t)num_kv_heads * BS * D;  // elements per block
-  const uint16_t *kbase = k_cache + (int64_t)kvh * BS * D;
-  const uint16_t *vbase = v_cache + (int64_t)kvh * D * BS;
+  const CT *kbase = static_cast<const CT *>(k_cache) + (int64_t)kvh * BS * D;
+  const CT *vbase = static_cast<const CT *>(v_cache) + (int64_t)kvh * D * BS;
 
   // Loads of one tile (idx = position in the range, < cnt), straight-line:
   // no branch around them, so the wait for one tile never waits for the
   // prefetched ones.  Token indices are clamped to the tile's valid tokens;
   // what a clamped lane reads is masked away by step().  K and V are read
   // once per launch, so they bypass the caches' normal replacement.
-  auto load = [&](Frag<D> &f, int idx) {
+  auto load = [&](Frag<D, KV8> &f, int idx) {
     const int n = __builtin_amdgcn_readlane(nvalid, idx);
     const int ka = __builtin_amdgcn_readlane(b0, idx);
     const int ktok = min(row, n - 1);
@@ -299,14 +330,24 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
       koff = o + ktok;
       voff = o + vtok;
     }
-    const uint16_t *kp = kbase + (int64_t)kb * blk_stride + koff * D + grp * 8;
+    const CT *vp = vbase + (int64_t)vb * blk_stride + row * BS + voff;
+    if constexpr (KV8) {
+      const CT *kp = kbase + (int64_t)kb * blk_stride + koff * D + grp * 16;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      f.k[ks] = __builtin_nontemporal_load((const u32x4 *)(kp + ks * 32));
-    const uint16_t *vp = vbase + (int64_t)vb * blk_stride + row * BS + voff;
+      for (int h = 0; h < D / 64; ++h)
+        f.k[h] = __builtin_nontemporal_load((const u32x4 *)(kp + h * 64));
 #pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt)
-      f.v[dt] = __builtin_nontemporal_load((const u32x2 *)(vp + dt * 16 * BS));
+      for (int dt = 0; dt < DTILES; ++dt)
+        f.v[dt] = __builtin_nontemporal_load((const uint32_t *)(vp + dt * 16 * BS));
+    } else {
+      const CT *kp = kbase + (int64_t)kb * blk_stride + koff * D + grp * 8;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        f.k[ks] = __builtin_nontemporal_load((const u32x4 *)(kp + ks * 32));
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt)
+        f.v[dt] = __builtin_nontemporal_load((const u32x2 *)(vp + dt * 16 * BS));
+    }
   };
 
   // Running max per head in log2 units; reset at each sequence segment.
@@ -320,14 +361,25 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // segment, the segment's result goes out and the state is reset.  Tokens
   // at or past the tile's valid count get weight zero and their V entries
   // are zeroed (unused slots may hold anything, NaN included).
-  auto step = [&](Frag<D> &f, int idx) {
+  auto step = [&](Frag<D, KV8> &f, int idx) {
     const int n = __builtin_amdgcn_readlane(nvalid, idx);
     u32x4 qf[KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = q_lds[ks * kWave + lane];
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) sc = E::qk(f.k[ks], qf[ks], sc);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4 kf;
+      if constexpr (KV8) {  // codes 8*(ks%2) .. +8 of the 16 loaded for ks/2
+        const u32x4 c = f.k[ks / 2];
+        const u32x2 a = E::from_e4m3(ks % 2 ? c.z : c.x);
+        const u32x2 b = E::from_e4m3(ks % 2 ? c.w : c.y);
+        kf = u32x4{a.x, a.y, b.x, b.y};
+      } else {
+        kf = f.k[ks];
+      }
+      sc = E::qk(kf, qf[ks], sc);
+    }
     float s[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] = (grp * 4 + r < n) ? sc[r] * scale_log2 : -INFINITY;
@@ -361,21 +413,21 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
       const uint32_t w1 = c >= 4 ? 0xffffffffu : (c == 3 ? 0x0000ffffu : 0u);
 #pragma unroll
       for (int dt = 0; dt < DTILES; ++dt) {
-        f.v[dt].x &= w0;
-        f.v[dt].y &= w1;
+        u32x2 vv;
+        if constexpr (KV8) vv = E::from_e4m3(f.v[dt]);
+        else vv = f.v[dt];
+        vv.x &= w0;
+        vv.y &= w1;
+        acc[dt] = E::pv(vv, ph, acc[dt]);
+        if constexpr (E::kSplitP) acc[dt] = E::pv(vv, pl, acc[dt]);
       }
-    }
-#pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) {
-      acc[dt] = E::pv(f.v[dt], ph, acc[dt]);
-      if constexpr (E::kSplitP) acc[dt] = E::pv(f.v[dt], pl, acc[dt]);
     }
     if (__builtin_amdgcn_readlane(seg_end, idx)) {
       const float l_tot = rows_sum(l_run);
       const int sqn = __builtin_amdgcn_readlane(sq, idx);
       if (row < group) {
         const int head = kvh * group + row;
-        const float inv = 1.0f / l_tot;
+        const float inv = out_scale / l_tot;
         if (__builtin_amdgcn_readlane(whole, idx)) {
           // lane (row, grp) holds dims 16*dt + 4*grp + 0..3 of head row
           uint16_t *op = out + ((int64_t)sqn * num_heads + head) * D + grp * 4;
@@ -415,7 +467,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // tile the ring reloads the last tile (cache hits); those steps are
   // skipped.  sched_barrier keeps the scheduler from sinking a load down to
   // its use, which would trade the prefetch for fewer registers.
-  Frag<D> f[kBuf];
+  Frag<D, KV8> f[kBuf];
 #pragma unroll
   for (int b = 0; b < kBuf - 1; ++b) load(f[b], min(b, cnt - 1));
   __builtin_amdgcn_sched_barrier(0);
@@ -488,7 +540,9 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
 
 template <int DT, int D, int BS>
 int launch_typed(const DecodeArgs &a) {
-  const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+  // log2(e) folds the exponential's base into the score scale; an E4M3
+  // cache's k_scale multiplies every score and its v_scale every output.
+  const float scale_log2 = (float)((double)a.scale * (double)a.k_scale * 1.4426950408889634);
   hipStream_t st = (hipStream_t)a.stream;
   const int group = a.num_heads / a.num_kv_heads;
   hipError_t e = hipSuccess;
@@ -496,11 +550,18 @@ int launch_typed(const DecodeArgs &a) {
     dim3 grid((unsigned)a.num_kv_heads * (unsigned)a.waves);
     const size_t lds = (size_t)((2 * a.num_seqs + 1 + 3) & ~3) * sizeof(int) +
                        (size_t)(D / 32) * kWave * 16;
-    decode_split_kernel<DT, D, BS><<<grid, kWave, lds, st>>>(
-        (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, (const uint16_t *)a.q,
-        (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.block_tables,
-        a.context_lens, scale_log2, a.num_seqs, a.num_kv_heads, a.num_heads, group,
-        a.max_blocks_per_seq, a.num_blocks, a.waves, a.slots);
+    if (a.kv_fp8)
+      decode_split_kernel<DT, D, BS, true><<<grid, kWave, lds, st>>>(
+          (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, (const uint16_t *)a.q, a.k_cache,
+          a.v_cache, a.block_tables, a.context_lens, scale_log2, a.v_scale, a.num_seqs,
+          a.num_kv_heads, a.num_heads, group, a.max_blocks_per_seq, a.num_blocks, a.waves,
+          a.slots);
+    else
+      decode_split_kernel<DT, D, BS, false><<<grid, kWave, lds, st>>>(
+          (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, (const uint16_t *)a.q, a.k_cache,
+          a.v_cache, a.block_tables, a.context_lens, scale_log2, 1.0f, a.num_seqs,
+          a.num_kv_heads, a.num_heads, group, a.max_blocks_per_seq, a.num_blocks, a.waves,
+          a.slots);
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }

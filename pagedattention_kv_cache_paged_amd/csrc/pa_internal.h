@@ -31,6 +31,9 @@ struct DecodeArgs {
   int32_t max_blocks_per_seq;
   int64_t num_blocks;
   int32_t dtype;
+  int32_t kv_fp8;      // 1: caches hold E4M3 codes (k_scale, v_scale apply)
+  float k_scale;       // K element = code * k_scale (1 for 16-bit caches)
+  float v_scale;       // V element = code * v_scale (1 for 16-bit caches)
   int32_t waves;       // wavefronts per KV head (equal shares of the flat tile list)
   int32_t slots;       // partial-result slots per query head: waves + num_seqs
   float *ws_o;         // [num_heads][slots][head_dim]
@@ -51,6 +54,10 @@ struct WriteArgs {
   int32_t head_dim;
   int32_t block_size;
   int64_t num_blocks;
+  int32_t dtype;       // k, v element type (PA_F16 / PA_BF16)
+  int32_t fp8;         // 1: quantise into E4M3 caches with k_inv / v_inv
+  float k_inv;         // float32(1 / k_scale)
+  float v_inv;         // float32(1 / v_scale)
   void *stream;
 };
 

@@ -4,6 +4,8 @@
 // inside the block.  The slot (block * block_size + offset) is chosen by the
 // caller's block manager; this is a pure bit copy.
 //
+// The FP8 variant quantises while it scatters (see kv_write_fp8_kernel).
+//
 // One workgroup per token.  A K row (head_dim contiguous elements) lands
 // contiguously in the token-major K cache, moved as 16-byte vectors; a V
 // row is spread across the dim-major V cache with a stride of block_size
@@ -17,6 +19,7 @@ namespace pa {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 template <int D, int BS>
 __global__ __launch_bounds__(256) void kv_write_kernel(
@@ -59,14 +62,99 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
   }
 }
 
+// E4M3 (OCP e4m3fn) code of y: nearest representable value, ties to the
+// even code, finite magnitudes from 448 up saturate to +-448, NaN -> 0x7f.
+// Below 2^-6 the grid is m * 2^-9 (rint of y * 512, exact scaling); above,
+// the fp32 fraction is cut to 3 bits with round-to-nearest-even, a carry
+// moving into the exponent as it should.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (!(a == a)) return 0x7fu;
+  if (a >= 448.0f) return sign | 0x7eu;
+  if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  const uint32_t ua = __float_as_uint(a);
+  uint32_t code = ((((ua >> 23) & 0xffu) - 127u + 7u) << 3) | ((ua >> 20) & 7u);
+  const uint32_t rest = ua & 0xfffffu;  // the 20 fraction bits dropped
+  if (rest > 0x80000u || (rest == 0x80000u && (code & 1u))) code += 1u;
+  return sign | code;
+}
+
+template <int DT>
+__device__ __forceinline__ float elem_to_float(uint32_t bits16) {
+  if constexpr (DT == 1) return __uint_as_float(bits16 << 16);  // bfloat16
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);  // binary16
+}
+
+// Quantising append into E4M3 caches: element x goes in as the code of
+// float32(x) * inv (inv = float32(1 / scale) from the host).  Layouts as for
+// the 16-bit caches, one byte per element.
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(256) void kv_write_fp8_kernel(
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int64_t *__restrict__ slot_mapping, uint8_t *__restrict__ k_cache,
+    uint8_t *__restrict__ v_cache, int num_kv_heads, int64_t num_slots, float k_inv,
+    float v_inv) {
+  constexpr int CH = D / 8;  // 8-element chunks per head row
+  const int64_t tok = blockIdx.x;
+  const int nch = num_kv_heads * CH;
+  const int c0 = threadIdx.x;
+  u32x4 kx0 = {0, 0, 0, 0}, vx0 = {0, 0, 0, 0};
+  if (c0 < nch) {
+    const int64_t src = (tok * num_kv_heads + c0 / CH) * D + (c0 % CH) * 8;
+    kx0 = *(const u32x4 *)(k + src);
+    vx0 = *(const u32x4 *)(v + src);
+  }
+  const int64_t slot = slot_mapping[tok];
+  if (slot < 0 || slot >= num_slots) return;  // padding, or outside the pool
+  const int64_t blk = slot / BS;
+  const int off = (int)(slot % BS);
+  for (int c = c0; c < nch; c += blockDim.x) {
+    const int h = c / CH;
+    const int d0 = (c % CH) * 8;
+    const int64_t src = (tok * num_kv_heads + h) * D + d0;
+    const u32x4 kx = c == c0 ? kx0 : *(const u32x4 *)(k + src);
+    const u32x4 vx = c == c0 ? vx0 : *(const u32x4 *)(v + src);
+    uint32_t kc[8], vc[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kc[2 * i] = e4m3_code(elem_to_float<DT>(kx[i] & 0xffffu) * k_inv);
+      kc[2 * i + 1] = e4m3_code(elem_to_float<DT>(kx[i] >> 16) * k_inv);
+      vc[2 * i] = e4m3_code(elem_to_float<DT>(vx[i] & 0xffffu) * v_inv);
+      vc[2 * i + 1] = e4m3_code(elem_to_float<DT>(vx[i] >> 16) * v_inv);
+    }
+    const int64_t bh = blk * num_kv_heads + h;
+    u32x2 kw;
+    kw.x = kc[0] | (kc[1] << 8) | (kc[2] << 16) | (kc[3] << 24);
+    kw.y = kc[4] | (kc[5] << 8) | (kc[6] << 16) | (kc[7] << 24);
+    *(u32x2 *)(k_cache + (bh * BS + off) * D + d0) = kw;  // 8-byte aligned: d0 % 8 == 0
+    uint8_t *vd = v_cache + (bh * D + d0) * BS + off;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vd[i * BS] = (uint8_t)vc[i];
+  }
+}
+
 template <int D, int BS>
 int launch_typed(const WriteArgs &a) {
   const int nch = a.num_kv_heads * (D / 8);
   int threads = (nch + kWave - 1) / kWave * kWave;
   threads = threads < kWave ? kWave : (threads > 256 ? 256 : threads);
-  kv_write_kernel<D, BS><<<dim3((unsigned)a.num_tokens), threads, 0, (hipStream_t)a.stream>>>(
-      (const uint16_t *)a.k, (const uint16_t *)a.v, a.slot_mapping, (uint16_t *)a.k_cache,
-      (uint16_t *)a.v_cache, a.num_kv_heads, a.num_blocks * BS);
+  const dim3 grid((unsigned)a.num_tokens);
+  hipStream_t st = (hipStream_t)a.stream;
+  if (!a.fp8) {
+    kv_write_kernel<D, BS><<<grid, threads, 0, st>>>(
+        (const uint16_t *)a.k, (const uint16_t *)a.v, a.slot_mapping, (uint16_t *)a.k_cache,
+        (uint16_t *)a.v_cache, a.num_kv_heads, a.num_blocks * BS);
+  } else if (a.dtype == 1) {
+    kv_write_fp8_kernel<1, D, BS><<<grid, threads, 0, st>>>(
+        (const uint16_t *)a.k, (const uint16_t *)a.v, a.slot_mapping, (uint8_t *)a.k_cache,
+        (uint8_t *)a.v_cache, a.num_kv_heads, a.num_blocks * BS, a.k_inv, a.v_inv);
+  } else {
+    kv_write_fp8_kernel<0, D, BS><<<grid, threads, 0, st>>>(
+        (const uint16_t *)a.k, (const uint16_t *)a.v, a.slot_mapping, (uint8_t *)a.k_cache,
+        (uint8_t *)a.v_cache, a.num_kv_heads, a.num_blocks * BS, a.k_inv, a.v_inv);
+  }
   return (int)hipGetLastError();
 }
 

@@ -30,10 +30,10 @@ def test_library_exports_every_declared_symbol():
     assert {"paged_kv_write", "paged_attention_decode", "paged_attention_decode_ex",
             "paged_attention_decode_stages", "paged_attention_workspace_bytes",
             "paged_attention_split_waves", "paged_validate_metadata", "pa_strerror",
-            "pa_abi_version"} <= set(names)
+            "pa_abi_version", "paged_kv_write_fp8", "paged_attention_decode_fp8"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 2
+    assert lib.pa_abi_version() == 3
 
 
 def test_single_hip_runtime():
@@ -120,6 +120,20 @@ def test_write_rejects(kw, code):
 
 def test_write_zero_tokens_is_noop():
     assert _write(T=0, k=None) == 0
+
+
+@pytest.mark.parametrize("ks,vs,code", [(0.0, 1.0, -3), (1.0, -2.0, -3), (float("inf"), 1.0, -3),
+                                       (1.0, float("nan"), -3), (1e-39, 1.0, -3),
+                                       (0.5, 0.25, 0)])
+def test_fp8_scales_checked(ks, vs, code):
+    lib = B.load()
+    rc = lib.paged_kv_write_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 0 if code == 0 else 4, 8, 128, 16,
+                                100, 1, ks, vs, None)
+    assert rc == code
+    rc = lib.paged_attention_decode_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, ks, vs, 16, 8,
+                                        0 if code == 0 else 4, 32, 128, 128, 1000, 1, 0, FAKE,
+                                        1 << 30, 3, None)
+    assert rc == code
 
 
 def test_split_and_workspace():
