@@ -40,11 +40,20 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
+# Tensor scales of the E4M3 cache for N(0, 1) data: codes stay inside +-448.
+FP8_K_SCALE, FP8_V_SCALE = 0.02, 0.02
+
+
+def kv_bytes_per_token(w, fp8: bool) -> int:
+    """K plus V bytes of one context token over all KV heads."""
+    return 2 * w.num_kv_heads * w.head_dim * (1 if fp8 else 2)
+
+
 def counters_path(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"{SPLIT_KERNEL}_{workload}_counters.txt")
 
 
-def summarize_counters(fetch_dir: str, write_dir: str, workload: str) -> dict:
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, fp8: bool) -> dict:
     """Per-launch HBM bytes of the split pass from two rocprofv3 --pmc runs
     (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
     counter reads for the plain COPY_BYTES device copy of the same run."""
@@ -72,8 +81,10 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str) -> dict:
     f_split, f_copy = per_dispatch(fetch_dir, "FETCH_SIZE")
     w_split, w_copy = per_dispatch(write_dir, "WRITE_SIZE")
     f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    opts = f"--workload {workload}" + (" --kv-dtype fp8" if fp8 else "")
     return {
-        "kernel": SPLIT_KERNEL, "workload": workload, "source_sha256": kernel_source_hash(),
+        "kernel": SPLIT_KERNEL, "workload": workload + ("_fp8" if fp8 else ""),
+        "source_sha256": kernel_source_hash(),
         "fetch_bytes_raw": f_split, "write_bytes_raw": w_split,
         "copy_bytes": COPY_BYTES, "copy_fetch_raw": f_copy, "copy_write_raw": w_copy,
         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
@@ -81,12 +92,12 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str) -> dict:
         "traffic_bytes": f_split * f_scale + w_split * w_scale,
         "commands": [
             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o cnt -- "
-            f"python3 bench.py --workload {workload} --steps 10 --warmup 2 --no-cpu-baseline "
+            f"python3 bench.py {opts} --steps 10 --warmup 2 --no-cpu-baseline "
             f"--copy-calibration",
             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o cnt -- "
-            f"python3 bench.py --workload {workload} --steps 10 --warmup 2 --no-cpu-baseline "
+            f"python3 bench.py {opts} --steps 10 --warmup 2 --no-cpu-baseline "
             f"--copy-calibration",
-            f"python3 bench.py --summarize-counters {fetch_dir} {write_dir} --workload {workload}",
+            f"python3 bench.py --summarize-counters {fetch_dir} {write_dir} {opts}",
         ],
     }
 
@@ -113,25 +124,33 @@ def make_workload(name, placement="random"):
     return W.NAMED[name]()
 
 
-def cpu_baseline(w, seconds: float):
+def cpu_baseline(w, seconds: float, fp8: bool = False):
     """The fp64 oracle (single thread) on the first n sequences, all heads;
     n grows until about `seconds` of work.  Rate in KV GB/s of the same
     accounting as the GPU figure."""
     import oracle
-    kc, vc = w.nan_caches()
+    kc, vc = w.nan_caches_fp8() if fp8 else w.nan_caches()
     for which in ("hist", "new"):
         k, v, s = w.write_batch(which)
-        oracle.kv_write(k, v, s, kc, vc, w.block_size)
+        if fp8:
+            oracle.kv_write_fp8(k, v, s, kc, vc, w.block_size, w.dtype, FP8_K_SCALE,
+                                FP8_V_SCALE)
+        else:
+            oracle.kv_write(k, v, s, kc, vc, w.block_size)
     done_tokens, t_total, n = 0, 0.0, 0
     while n < w.num_seqs and t_total < seconds:
         rows = np.array([(n, h) for h in range(w.num_heads)], dtype=np.int32)
         t0 = time.perf_counter()
-        oracle.decode_rows(rows, w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
-                           w.block_size, w.dtype)
+        if fp8:
+            oracle.decode_fp8_rows(rows, w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                   w.block_size, w.dtype, FP8_K_SCALE, FP8_V_SCALE)
+        else:
+            oracle.decode_rows(rows, w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                               w.block_size, w.dtype)
         t_total += time.perf_counter() - t0
         done_tokens += int(w.context_lens[n])
         n += 1
-    gbs = done_tokens * w.bytes_per_token / t_total / 1e9
+    gbs = done_tokens * kv_bytes_per_token(w, fp8) / t_total / 1e9
     return {"value": round(gbs, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} of {w.num_seqs} sequences, all {w.num_heads} query heads "
                       f"({done_tokens} context tokens), fp64 C oracle, single thread, "
@@ -151,6 +170,8 @@ def main():
                     help="physical block placement of the llama8b workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-dtype", default="native", choices=("native", "fp8"),
+                    help="KV cache element type: the workload's 16-bit type, or E4M3 codes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (byte-counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -158,10 +179,12 @@ def main():
                          "--pmc runs to profiles/ and exit (no GPU needed)")
     args = ap.parse_args()
 
+    fp8 = args.kv_dtype == "fp8"
+    tag = args.workload + ("_fp8" if fp8 else "")
     if args.summarize_counters:
-        rec = summarize_counters(*args.summarize_counters, args.workload)
-        os.makedirs(os.path.dirname(counters_path(args.workload)), exist_ok=True)
-        with open(counters_path(args.workload), "w") as f:
+        rec = summarize_counters(*args.summarize_counters, args.workload, fp8)
+        os.makedirs(os.path.dirname(counters_path(tag)), exist_ok=True)
+        with open(counters_path(tag), "w") as f:
             f.write(json.dumps(rec, indent=1) + "\n")
         print(json.dumps(rec))
         return
@@ -187,7 +210,7 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(tdt)
 
     ks, vs = w.cache_shapes()
-    pool_bytes = 2 * int(np.prod(ks)) * 2
+    pool_bytes = 2 * int(np.prod(ks)) * (1 if fp8 else 2)
     copies = args.copies or max(4, math.ceil(1.1e9 / pool_bytes))
     nan_i16 = int(np.array([W.NAN_BITS[w.dtype]], np.uint16).view(np.int16)[0])
     hk, hv, hs = w.write_batch("hist")
@@ -196,10 +219,16 @@ def main():
     nk, nv, ns = dev_bits(nk), dev_bits(nv), torch.from_numpy(ns).to(dev)
     caches = []
     for _ in range(copies):
-        kc = torch.full(ks, nan_i16, dtype=torch.int16, device=dev).view(tdt)
-        vc = torch.full(vs, nan_i16, dtype=torch.int16, device=dev).view(tdt)
-        if hs.numel():
-            B.paged_kv_write(hk, hv, hs, kc, vc)
+        if fp8:
+            kc = torch.full(ks, W.FP8_NAN, dtype=torch.uint8, device=dev)
+            vc = torch.full(vs, W.FP8_NAN, dtype=torch.uint8, device=dev)
+            if hs.numel():
+                B.paged_kv_write_fp8(hk, hv, hs, kc, vc, FP8_K_SCALE, FP8_V_SCALE)
+        else:
+            kc = torch.full(ks, nan_i16, dtype=torch.int16, device=dev).view(tdt)
+            vc = torch.full(vs, nan_i16, dtype=torch.int16, device=dev).view(tdt)
+            if hs.numel():
+                B.paged_kv_write(hk, hv, hs, kc, vc)
         caches.append((kc, vc))
     del hk, hv, hs
     q = dev_bits(w.q)
@@ -221,18 +250,31 @@ def main():
 
     def write(i):
         kc, vc = caches[i % copies]
-        rc = lib.paged_kv_write(nk.data_ptr(), nv.data_ptr(), ns.data_ptr(), kc.data_ptr(),
-                                vc.data_ptr(), T, w.num_kv_heads, w.head_dim, w.block_size,
-                                w.num_blocks, dtc, sp)
+        if fp8:
+            rc = lib.paged_kv_write_fp8(nk.data_ptr(), nv.data_ptr(), ns.data_ptr(),
+                                        kc.data_ptr(), vc.data_ptr(), T, w.num_kv_heads,
+                                        w.head_dim, w.block_size, w.num_blocks, dtc,
+                                        FP8_K_SCALE, FP8_V_SCALE, sp)
+        else:
+            rc = lib.paged_kv_write(nk.data_ptr(), nv.data_ptr(), ns.data_ptr(), kc.data_ptr(),
+                                    vc.data_ptr(), T, w.num_kv_heads, w.head_dim,
+                                    w.block_size, w.num_blocks, dtc, sp)
         assert rc == 0, rc
 
     def decode(i, stages):
         kc, vc = caches[i % copies]
-        rc = lib.paged_attention_decode_stages(
-            out.data_ptr(), q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bt.data_ptr(),
-            cl.data_ptr(), w.scale, w.block_size, w.num_kv_heads, w.num_seqs, w.num_heads,
-            w.head_dim, w.max_blocks_per_seq, w.num_blocks, dtc, pt, ws.data_ptr(),
-            ws.numel(), stages, sp)
+        if fp8:
+            rc = lib.paged_attention_decode_fp8(
+                out.data_ptr(), q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bt.data_ptr(),
+                cl.data_ptr(), w.scale, FP8_K_SCALE, FP8_V_SCALE, w.block_size,
+                w.num_kv_heads, w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq,
+                w.num_blocks, dtc, pt, ws.data_ptr(), ws.numel(), stages, sp)
+        else:
+            rc = lib.paged_attention_decode_stages(
+                out.data_ptr(), q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bt.data_ptr(),
+                cl.data_ptr(), w.scale, w.block_size, w.num_kv_heads, w.num_seqs,
+                w.num_heads, w.head_dim, w.max_blocks_per_seq, w.num_blocks, dtc, pt,
+                ws.data_ptr(), ws.numel(), stages, sp)
         assert rc == 0, rc
 
     for i in range(args.warmup):
@@ -292,8 +334,8 @@ def main():
     t_merge = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
     p_part = np.percentile([e[1].elapsed_time(e[2]) * 1e3 for e in ev], [10, 50, 90])
 
-    kv_bytes = w.logical_tokens * w.bytes_per_token
-    unique_bytes = w.unique_tokens * w.bytes_per_token
+    kv_bytes = w.logical_tokens * kv_bytes_per_token(w, fp8)
+    unique_bytes = w.unique_tokens * kv_bytes_per_token(w, fp8)
     gbs = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (t_split * 1e-6) / 1e9
     result = {
@@ -312,9 +354,11 @@ def main():
         "config": {
             "workload": f"{w.name}: batch {w.num_seqs}, {w.num_heads} q / {w.num_kv_heads} kv "
                         f"heads, head_dim {w.head_dim}, block {w.block_size}, "
-                        f"{w.logical_tokens} context tokens",
+                        f"{w.logical_tokens} context tokens"
+                        + (", E4M3 KV cache" if fp8 else ""),
             "batch": w.num_seqs, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
-            "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": w.dtype,
+            "head_dim": w.head_dim, "block_size": w.block_size,
+            "kv_dtype": "e4m3" if fp8 else w.dtype,
             "context_tokens": w.logical_tokens, "partition_tokens": pt,
             "waves_per_kv_head": waves,
             "pool_copies": copies, "pool_mb_per_copy": round(pool_bytes / 2**20, 1),
@@ -337,14 +381,14 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "avg_launch_us": round(t_split, 3),
-            "traffic": recorded_traffic(args.workload),
+            "traffic": recorded_traffic(tag),
             "bytes_per_launch": kv_bytes,
         },
     }
     if unique_bytes != kv_bytes:
         result["unique_kv_gbs"] = round(unique_bytes / (ms_step * 1e-3) / 1e9, 2)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, fp8)
     print(json.dumps(result), flush=True)
 
 
