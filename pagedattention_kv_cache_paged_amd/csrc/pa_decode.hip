@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   }
   if (lane == 0) cu[0] = 0;
   __syncthreads();
-  const int n_tiles = carry;
+  const int n_tiles = __builtin_amdgcn_readfirstlane(carry);  // uniform: scalar loop control
   if (kvh == 0 && j == 0)  // for the merge pass
     for (int s = lane; s <= num_seqs; s += kWave) ws_cu[s] = cu[s];
 
@@ -267,6 +267,10 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   const int seg_end = (it == ntiles_sq - 1 || tau == t1 - 1) ? 1 : 0;
   const int whole = (first >= t0 && first + ntiles_sq <= t1) ? 1 : 0;
   const uint64_t ends = __ballot(seg_end && lane < cnt);  // bit i: a segment ends at tile i
+  // The flags of tile t0 + lane in one word, so that one readlane per tile
+  // fetches them: bits 0-4 valid tokens, 5 segment end, 6 whole sequence.
+  constexpr int kEnd = 1 << 5, kWhole = 1 << 6;
+  const int meta = nvalid | (seg_end ? kEnd : 0) | (whole ? kWhole : 0);
 
   // Query fragment of the current segment and, one segment ahead, of the
   // next.  Lane (row, grp) holds 8 dims of head row per k-step: dims
@@ -309,30 +313,24 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // what a clamped lane reads is masked away by step().  K and V are read
   // once per launch, so they bypass the caches' normal replacement.
   auto load = [&](Frag<D, KV8> &f, int idx) {
-    const int n = __builtin_amdgcn_readlane(nvalid, idx);
+    const int n = __builtin_amdgcn_readlane(meta, idx) & 31;
     const int ka = __builtin_amdgcn_readlane(b0, idx);
     const int ktok = min(row, n - 1);
     const int vtok = min(grp * 4, (n - 1) & ~3);
-    int kb, vb, koff, voff;
-    if constexpr (BS == 8) {
+    const CT *kp, *vp;
+    if constexpr (BS == 8) {  // the tile's two blocks: per-lane choice
       const int kz = __builtin_amdgcn_readlane(b1, idx);
-      kb = ktok < 8 ? ka : kz;
-      koff = ktok & 7;
-      vb = vtok < 8 ? ka : kz;
-      voff = vtok & 7;
-    } else if constexpr (BS == 16) {
-      kb = vb = ka;
-      koff = ktok;
-      voff = vtok;
+      kp = kbase + (int64_t)(ktok < 8 ? ka : kz) * blk_stride + (ktok & 7) * D + grp * (KV8 ? 16 : 8);
+      vp = vbase + (int64_t)(vtok < 8 ? ka : kz) * blk_stride + row * BS + (vtok & 7);
     } else {
-      const int o = __builtin_amdgcn_readlane(boff, idx);
-      kb = vb = ka;
-      koff = o + ktok;
-      voff = o + vtok;
+      // block base in scalar registers, 32-bit lane offsets
+      const int o = BS == 16 ? 0 : __builtin_amdgcn_readlane(boff, idx);
+      const CT *kblk = kbase + (int64_t)ka * blk_stride + o * D;
+      const CT *vblk = vbase + (int64_t)ka * blk_stride + o;
+      kp = kblk + (uint32_t)(ktok * D + grp * (KV8 ? 16 : 8));
+      vp = vblk + (uint32_t)(row * BS + vtok);
     }
-    const CT *vp = vbase + (int64_t)vb * blk_stride + row * BS + voff;
     if constexpr (KV8) {
-      const CT *kp = kbase + (int64_t)kb * blk_stride + koff * D + grp * 16;
 #pragma unroll
       for (int h = 0; h < D / 64; ++h)
         f.k[h] = __builtin_nontemporal_load((const u32x4 *)(kp + h * 64));
@@ -340,7 +338,6 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
       for (int dt = 0; dt < DTILES; ++dt)
         f.v[dt] = __builtin_nontemporal_load((const uint32_t *)(vp + dt * 16 * BS));
     } else {
-      const CT *kp = kbase + (int64_t)kb * blk_stride + koff * D + grp * 8;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks)
         f.k[ks] = __builtin_nontemporal_load((const u32x4 *)(kp + ks * 32));
@@ -350,7 +347,12 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
     }
   };
 
-  // Running max per head in log2 units; reset at each sequence segment.
+  // Reference max per head in log2 units, reset at each sequence segment.
+  // It is raised only when a tile's max exceeds it by more than kSlack, so
+  // most tiles skip the rescale of the accumulators; the weights
+  // 2^(s - m_ref) then stay below 2^kSlack, far inside fp32 and bfloat16
+  // range.  The softmax is the same for any reference.
+  constexpr float kSlack = 8.f;
   float m_ref = -INFINITY;
   float l_run = 0.f;  // this lane's share of the running sum
   f32x4 acc[DTILES];
@@ -358,11 +360,13 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   for (int dt = 0; dt < DTILES; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // One tile of scores, softmax update and P.V; at the end of a sequence
-  // segment, the segment's result goes out and the state is reset.  Tokens
-  // at or past the tile's valid count get weight zero and their V entries
-  // are zeroed (unused slots may hold anything, NaN included).
+  // segment, the segment's result goes out and the state is reset.  In the
+  // last tile of a sequence, tokens at or past its valid count get weight
+  // zero and their V entries are zeroed (unused slots may hold anything,
+  // NaN included).  Both branches here are wave-uniform and hold no loads.
   auto step = [&](Frag<D, KV8> &f, int idx) {
-    const int n = __builtin_amdgcn_readlane(nvalid, idx);
+    const int mt = __builtin_amdgcn_readlane(meta, idx);
+    const int n = mt & 31;
     u32x4 qf[KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = q_lds[ks * kWave + lane];
@@ -382,9 +386,27 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
     }
     float s[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = (grp * 4 + r < n) ? sc[r] * scale_log2 : -INFINITY;
+    for (int r = 0; r < 4; ++r) s[r] = sc[r] * scale_log2;
+    if (n < kTile) {
+      const int c = n - grp * 4;  // valid tokens among this lane's four
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] = r < c ? s[r] : -INFINITY;
+      if constexpr (KV8) {  // one code byte per token
+        const uint32_t w = c >= 4 ? 0xffffffffu : (c <= 0 ? 0u : (1u << (8 * c)) - 1u);
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) f.v[dt] &= w;
+      } else {  // two 16-bit tokens per word
+        const uint32_t w0 = c >= 2 ? 0xffffffffu : (c == 1 ? 0x0000ffffu : 0u);
+        const uint32_t w1 = c >= 4 ? 0xffffffffu : (c == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) {
+          f.v[dt].x &= w0;
+          f.v[dt].y &= w1;
+        }
+      }
+    }
     const float mx = rows_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
-    {  // rescale unconditionally: a branch here costs more than the multiplies
+    if (__ballot(mx > m_ref + kSlack)) {  // always on a segment's first tile
       const float m_new = fmaxf(m_ref, mx);  // finite: every tile has a valid token
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
       l_run *= alpha;
@@ -407,28 +429,21 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
       // the sum uses the rounded weights the MFMA multiplies with
       l_run += (E::lo(ph.x) + E::hi(ph.x)) + (E::lo(ph.y) + E::hi(ph.y));
     }
-    {
-      const int c = n - grp * 4;
-      const uint32_t w0 = c >= 2 ? 0xffffffffu : (c == 1 ? 0x0000ffffu : 0u);
-      const uint32_t w1 = c >= 4 ? 0xffffffffu : (c == 3 ? 0x0000ffffu : 0u);
 #pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt) {
-        u32x2 vv;
-        if constexpr (KV8) vv = E::from_e4m3(f.v[dt]);
-        else vv = f.v[dt];
-        vv.x &= w0;
-        vv.y &= w1;
-        acc[dt] = E::pv(vv, ph, acc[dt]);
-        if constexpr (E::kSplitP) acc[dt] = E::pv(vv, pl, acc[dt]);
-      }
+    for (int dt = 0; dt < DTILES; ++dt) {
+      u32x2 vv;
+      if constexpr (KV8) vv = E::from_e4m3(f.v[dt]);
+      else vv = f.v[dt];
+      acc[dt] = E::pv(vv, ph, acc[dt]);
+      if constexpr (E::kSplitP) acc[dt] = E::pv(vv, pl, acc[dt]);
     }
-    if (__builtin_amdgcn_readlane(seg_end, idx)) {
+    if (mt & kEnd) {
       const float l_tot = rows_sum(l_run);
       const int sqn = __builtin_amdgcn_readlane(sq, idx);
       if (row < group) {
         const int head = kvh * group + row;
         const float inv = out_scale / l_tot;
-        if (__builtin_amdgcn_readlane(whole, idx)) {
+        if (mt & kWhole) {
           // lane (row, grp) holds dims 16*dt + 4*grp + 0..3 of head row
           uint16_t *op = out + ((int64_t)sqn * num_heads + head) * D + grp * 4;
 #pragma unroll
