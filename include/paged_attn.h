@@ -207,6 +207,38 @@ int paged_attention_decode_fp8(void *out, const void *q, const void *k_cache,
                                size_t workspace_bytes, int32_t stages, void *stream);
 
 /*
+ * One decode step with the append fused in ("vLLM memory management and
+ * continuous batching from the source" (developer.cloud.tencent.cn), part 2:
+ * 2.1, the new token's K/V written at its block's address plus offset; 2.3,
+ * attention reading K/V through the block table).  For every sequence s with
+ * L = context_lens[s] >= 1 the new token is context position L-1: its rows
+ * k_new[s], v_new[s] ([num_seqs, num_kv_heads, head_dim], dtype) are stored
+ * at block block_tables[s][(L-1) / block_size], offset (L-1) % block_size,
+ * of both caches, and out[s] is the attention of q[s] over all L tokens, the
+ * new one included.  That is paged_kv_write with slot_mapping[s] = that slot,
+ * followed by paged_attention_decode, in two launches instead of three: the
+ * split pass covers positions 0 .. L-2 and the merge pass adds the new token
+ * as one more log-sum-exp partial and stores it.  L = 0: out[s] = 0 and no
+ * store; a table entry outside [0, num_blocks) for position L-1: no store.
+ *
+ * kv_fp8 = 0: 16-bit caches, k_scale / v_scale ignored.  kv_fp8 = 1: E4M3
+ * caches as for paged_kv_write_fp8 / paged_attention_decode_fp8; the new
+ * token is quantised with the scales and enters the attention as its codes'
+ * values.  k_new, v_new: 4-byte aligned.  The workspace is that of
+ * paged_attention_decode for the same sizes.  The caller owns all buffers;
+ * out, the new token's cache slots and the workspace are written.
+ */
+int paged_attention_decode_append(void *out, const void *q, const void *k_new,
+                                  const void *v_new, void *k_cache, void *v_cache,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  float scale, float k_scale, float v_scale,
+                                  int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                                  int32_t num_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int64_t num_blocks,
+                                  int32_t dtype, int32_t kv_fp8, int32_t partition_tokens,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Host-side check of metadata (host pointers): every context length in
  * [0, max_blocks_per_seq * block_size]; every table entry a sequence reads,
  * i.e. the first ceil(L / block_size) of its row, in [0, num_blocks); every

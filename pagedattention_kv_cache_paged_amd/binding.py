@@ -76,6 +76,10 @@ def load() -> ctypes.CDLL:
     lib.paged_attention_decode_fp8.restype = ctypes.c_int
     lib.paged_attention_decode_fp8.argtypes = [p, p, p, p, p, p, f32, f32, f32, i32, i32, i32,
                                                i32, i32, i32, i64, i32, i32, p, sz, i32, p]
+    lib.paged_attention_decode_append.restype = ctypes.c_int
+    lib.paged_attention_decode_append.argtypes = [p, p, p, p, p, p, p, p, f32, f32, f32, i32,
+                                                  i32, i32, i32, i32, i32, i64, i32, i32, i32,
+                                                  p, sz, p]
     lib.paged_validate_metadata.restype = ctypes.c_int
     lib.paged_validate_metadata.argtypes = [p, p, i32, i32, i32, i64, p, i64]
     _lib = lib
@@ -284,3 +288,55 @@ def paged_attention_decode_fp8(out: torch.Tensor, q: torch.Tensor, k_cache: torc
     _check("paged_attention_decode_fp8", rc)
     return out
 
+
+
+# ---- decode step with the append fused in ---------------------------------
+
+def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                                  v_new: torch.Tensor, k_cache: torch.Tensor,
+                                  v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, scale: float, block_size: int,
+                                  num_kv_heads: int, k_scale: Optional[float] = None,
+                                  v_scale: Optional[float] = None, partition_tokens: int = 0,
+                                  workspace_tensor: Optional[torch.Tensor] = None
+                                  ) -> torch.Tensor:
+    """Store each sequence's new token (k_new, v_new [B, Hkv, D]) at context
+    position L-1 of its block table, then decode over all L tokens.  uint8
+    caches hold E4M3 codes and need k_scale, v_scale; 16-bit caches share
+    q's dtype.  Returns out."""
+    dev = _dev(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens)
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be [num_seqs, num_heads, head_dim]")
+    B, hq, d = q.shape
+    if tuple(k_new.shape) != (B, num_kv_heads, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
+    if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (num_kv_heads, block_size, d):
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    nb = k_cache.shape[0]
+    if tuple(v_cache.shape) != (nb, num_kv_heads, d, block_size):
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [num_seqs, max_blocks_per_seq]")
+    if context_lens.dtype != torch.int32 or tuple(context_lens.shape) != (B,):
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    dt = _dtype(q)
+    if out.dtype != q.dtype or k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise ValueError("q, out, k_new and v_new must share one dtype")
+    fp8 = k_cache.dtype == torch.uint8
+    if fp8:
+        if v_cache.dtype != torch.uint8 or k_scale is None or v_scale is None:
+            raise ValueError("E4M3 caches: both uint8, with k_scale and v_scale")
+    elif k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("16-bit caches must share q's dtype")
+    mb = block_tables.shape[1]
+    need = workspace_bytes(B, hq, num_kv_heads, d, mb, block_size, partition_tokens)
+    ws = workspace_tensor if workspace_tensor is not None else workspace(dev, need)
+    ws_ptr = ws.data_ptr() if ws is not None else None
+    ws_len = ws.numel() * ws.element_size() if ws is not None else 0
+    rc = load().paged_attention_decode_append(
+        out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
+        float(k_scale or 1.0), float(v_scale or 1.0), block_size, num_kv_heads, B, hq, d, mb,
+        nb, dt, 1 if fp8 else 0, partition_tokens, ws_ptr, ws_len, _stream(dev))
+    _check("paged_attention_decode_append", rc)
+    return out

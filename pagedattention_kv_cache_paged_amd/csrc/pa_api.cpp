@@ -74,7 +74,7 @@ bool decode_sizes_ok(int32_t num_seqs, int32_t num_kv_heads, int32_t num_heads,
 
 extern "C" {
 
-int pa_abi_version(void) { return 3; }
+int pa_abi_version(void) { return 4; }
 
 const char *pa_strerror(int code) {
   switch (code) {
@@ -157,7 +157,8 @@ static int decode_common(void *out, const void *q, const void *k_cache, const vo
                          int32_t num_heads, int32_t head_dim, int32_t max_blocks_per_seq,
                          int64_t num_blocks, int32_t dtype, int32_t partition_tokens,
                          void *workspace, size_t workspace_bytes, int32_t stages, int fp8,
-                         float k_scale, float v_scale, void *stream) {
+                         float k_scale, float v_scale, void *stream, int append = 0,
+                         const void *k_new = nullptr, const void *v_new = nullptr) {
   if (dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_DTYPE;
   if (stages < 1 || stages > 3) return PA_ERR_SHAPE;
   if (fp8 && !(valid_scale(k_scale) && valid_scale(v_scale))) return PA_ERR_SHAPE;
@@ -171,8 +172,10 @@ static int decode_common(void *out, const void *q, const void *k_cache, const vo
                                     partition_tokens);
   if (waves * num_kv_heads > INT32_MAX || waves + num_seqs > INT32_MAX) return PA_ERR_SHAPE;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (append && (!k_new || !v_new)) return PA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 8) ||
-      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      (append && (!aligned(k_new, 4) || !aligned(v_new, 4))))
     return PA_ERR_ALIGN;
   const WsLayout l = ws_layout(num_seqs, num_heads, head_dim, waves);
   if (!workspace || workspace_bytes < (size_t)l.total) return PA_ERR_WORKSPACE;
@@ -183,8 +186,25 @@ static int decode_common(void *out, const void *q, const void *k_cache, const vo
                    dtype, fp8, fp8 ? k_scale : 1.0f, fp8 ? v_scale : 1.0f,
                    (int32_t)waves, (int32_t)(waves + num_seqs),
                    reinterpret_cast<float *>(ws + l.o), reinterpret_cast<float *>(ws + l.ml),
-                   reinterpret_cast<int32_t *>(ws + l.cu), stages, stream};
+                   reinterpret_cast<int32_t *>(ws + l.cu), stages, append, k_new, v_new,
+                   fp8 ? 1.0f / k_scale : 1.0f, fp8 ? 1.0f / v_scale : 1.0f, stream};
   return pa::launch_decode(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int paged_attention_decode_append(void *out, const void *q, const void *k_new,
+                                  const void *v_new, void *k_cache, void *v_cache,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  float scale, float k_scale, float v_scale, int32_t block_size,
+                                  int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                                  int32_t head_dim, int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, int32_t dtype, int32_t kv_fp8,
+                                  int32_t partition_tokens, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  if (kv_fp8 != 0 && kv_fp8 != 1) return PA_ERR_DTYPE;
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                       num_kv_heads, num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                       num_blocks, dtype, partition_tokens, workspace, workspace_bytes, 3,
+                       kv_fp8, k_scale, v_scale, stream, 1, k_new, v_new);
 }
 
 int paged_attention_decode_stages(void *out, const void *q, const void *k_cache,

@@ -39,6 +39,7 @@
 
 #include <type_traits>
 
+#include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
     const void *__restrict__ k_cache, const void *__restrict__ v_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     float scale_log2, float out_scale, int num_seqs, int num_kv_heads, int num_heads,
-    int group, int max_blocks, int64_t num_blocks, int waves, int slots) {
+    int group, int max_blocks, int64_t num_blocks, int waves, int slots, int append) {
   using E = Elem<DT>;
   using CT = std::conditional_t<KV8, uint8_t, uint16_t>;  // cache element
   constexpr int KSTEPS = D / 32;  // 16x16x32 MFMAs per QK tile
@@ -201,18 +202,22 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
 
   // Tile prefix over all sequences (the same in every wavefront).  Range-0
   // wavefronts also write the zero rows of sequences with nothing to attend.
+  // With a fused append the last position is the new token, which the
+  // merge pass adds: this pass covers the L - 1 tokens before it and leaves
+  // every output row to the merge pass.
   int carry = 0;
   for (int c = 0; c < num_seqs; c += kWave) {
     const int s = c + lane;
     int len = s < num_seqs ? context_lens[s] : 0;
     len = min(max(len, 0), max_len);
+    if (append) len = max(len - 1, 0);
     const int incl = wave_incl_scan((len + kTile - 1) / kTile) + carry;
     if (s < num_seqs) {
       cu[s + 1] = incl;
       lens[s] = len;
     }
     carry = __shfl(incl, kWave - 1);
-    if (j == 0) {
+    if (j == 0 && !append) {
       uint64_t zero = __ballot(s < num_seqs && len == 0);
       while (zero) {
         const int zs = c + __builtin_ctzll(zero);
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   b0 = (b0 >= 0 && b0 < num_blocks) ? b0 : 0;  // ids outside the pool: stay inside it
   b1 = (b1 >= 0 && b1 < num_blocks) ? b1 : 0;
   const int seg_end = (it == ntiles_sq - 1 || tau == t1 - 1) ? 1 : 0;
-  const int whole = (first >= t0 && first + ntiles_sq <= t1) ? 1 : 0;
+  const int whole = (!append && first >= t0 && first + ntiles_sq <= t1) ? 1 : 0;
   const uint64_t ends = __ballot(seg_end && lane < cnt);  // bit i: a segment ends at tile i
   // The flags of tile t0 + lane in one word, so that one readlane per tile
   // fetches them: bits 0-4 valid tokens, 5 segment end, 6 whole sequence.
@@ -502,50 +507,146 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
 // The partials of sequence s come from wavefronts wave_of(cu[s]) ..
 // wave_of(cu[s+1] - 1), in consecutive slots starting at that first
 // wavefront + s.
-template <int DT, int D>
+//
+// APPEND: the sequence's new token (position L-1, which the split pass left
+// out) joins as one more partial with m = its score, l = 1, o = its V row,
+// and the wave of each group's first query head stores that token's K and V
+// into the caches at position L-1 of the block table, as the append step
+// would (KV8: as E4M3 codes of x * k_inv / v_inv, whose values then enter
+// the attention).  Every output row is written here, zeros for L = 0.
+template <int DT, int D, bool APPEND, bool KV8>
 __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     uint16_t *__restrict__ out, const float *__restrict__ ws_o,
     const float *__restrict__ ws_ml, const int32_t *__restrict__ ws_cu, int num_seqs,
-    int num_heads, int waves, int slots) {
+    int num_heads, int waves, int slots, const uint16_t *__restrict__ q,
+    const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+    void *__restrict__ k_cache, void *__restrict__ v_cache,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
+    float scale_log2, float v_scale, float k_inv, float v_inv, int num_kv_heads, int group,
+    int block_size, int max_blocks, int64_t num_blocks) {
   using E = Elem<DT>;
   constexpr int PER = D / kWave;  // dims per lane
   const int head = blockIdx.x;
   const int seq = blockIdx.y;
   const int lane = threadIdx.x;
+  uint16_t *op = out + ((int64_t)seq * num_heads + head) * D + lane * PER;
   const int n_tiles = ws_cu[num_seqs];
   const int c0 = ws_cu[seq], c1 = ws_cu[seq + 1];
-  if (c1 <= c0) return;  // nothing to attend: the split pass wrote zeros
-  const int wv = min(waves, n_tiles);  // as in the split pass: all ranges non-empty
-  const int jf = wave_of(c0, n_tiles, wv);
-  const int jl = wave_of(c1 - 1, n_tiles, wv);
-  if (jf == jl) return;  // one wavefront held the sequence and wrote its row
-  const int np = jl - jf + 1;
-
-  const int64_t base = (int64_t)head * slots + jf + seq;
-  const f32x2 *ml = (const f32x2 *)(ws_ml + base * 2);
-  // One pass with a running maximum, so each partial's (m, l) and o are
-  // loaded together: c_p = l_p * 2^(m_p - M) rescaled as M grows.
   float big = -INFINITY, den = 0.f;
   float num[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) num[i] = 0.f;
-  const float *o = ws_o + base * D + lane * PER;
+  if constexpr (APPEND) {
+    const int len = min(max(context_lens[seq], 0), max_blocks * block_size);
+    if (len == 0) {  // nothing to attend and nothing to append
+      if constexpr (PER == 2) *(uint32_t *)op = 0u;
+      else op[0] = 0;
+      return;
+    }
+    const int kvh = head / group;
+    const int64_t src = ((int64_t)seq * num_kv_heads + kvh) * D + lane * PER;
+    float qe[PER], ke[PER], ve[PER];
+    uint32_t kc[PER], vc[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      qe[i] = elem_to_float<DT>(q[((int64_t)seq * num_heads + head) * D + lane * PER + i]);
+      kc[i] = k_new[src + i];
+      vc[i] = v_new[src + i];
+      if constexpr (KV8) {
+        kc[i] = e4m3_code(elem_to_float<DT>(kc[i]) * k_inv);
+        vc[i] = e4m3_code(elem_to_float<DT>(vc[i]) * v_inv);
+        ke[i] = e4m3_value(kc[i]);
+        ve[i] = e4m3_value(vc[i]) * v_scale;
+      } else {
+        ke[i] = elem_to_float<DT>(kc[i]);
+        ve[i] = elem_to_float<DT>(vc[i]);
+      }
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) dot = fmaf(qe[i], ke[i], dot);
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+    big = dot * scale_log2;  // the new token: m = its score, l = 1, o = V
+    den = 1.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) num[i] = ve[i];
+    if (head % group == 0) {  // one writer per KV head
+      const int pos = len - 1;
+      const int64_t blk = block_tables[(int64_t)seq * max_blocks + pos / block_size];
+      if (blk >= 0 && blk < num_blocks) {
+        const int64_t bh = blk * num_kv_heads + kvh;
+        const int off = pos % block_size;
+        const int d0 = lane * PER;
+        if constexpr (KV8) {
+          uint8_t *kd = (uint8_t *)k_cache + (bh * block_size + off) * D + d0;
+          uint8_t *vd = (uint8_t *)v_cache + (bh * D + d0) * block_size + off;
+#pragma unroll
+          for (int i = 0; i < PER; ++i) {
+            kd[i] = (uint8_t)kc[i];
+            vd[i * block_size] = (uint8_t)vc[i];
+          }
+        } else {
+          uint16_t *kd = (uint16_t *)k_cache + (bh * block_size + off) * D + d0;
+          uint16_t *vd = (uint16_t *)v_cache + (bh * D + d0) * block_size + off;
+#pragma unroll
+          for (int i = 0; i < PER; ++i) {
+            kd[i] = (uint16_t)kc[i];
+            vd[i * block_size] = (uint16_t)vc[i];
+          }
+        }
+      }
+    }
+    if (c1 > c0) {
+      const int wv = min(waves, n_tiles);
+      const int jf = wave_of(c0, n_tiles, wv);
+      const int jl = wave_of(c1 - 1, n_tiles, wv);
+      // fall through to the partials below
+      const int64_t base = (int64_t)head * slots + jf + seq;
+      const f32x2 *ml = (const f32x2 *)(ws_ml + base * 2);
+      const float *o = ws_o + base * D + lane * PER;
+      for (int p = 0; p <= jl - jf; ++p) {
+        const f32x2 v = ml[p];
+        float opv[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) opv[i] = o[(int64_t)p * D + i];
+        const float m_new = fmaxf(big, v.x);
+        const float a = __builtin_amdgcn_exp2f(big - m_new);
+        const float c = v.y * __builtin_amdgcn_exp2f(v.x - m_new);
+        den = den * a + c;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) num[i] = num[i] * a + c * opv[i];
+        big = m_new;
+      }
+    }
+  } else {
+    if (c1 <= c0) return;  // nothing to attend: the split pass wrote zeros
+    const int wv = min(waves, n_tiles);  // as in the split pass: all ranges non-empty
+    const int jf = wave_of(c0, n_tiles, wv);
+    const int jl = wave_of(c1 - 1, n_tiles, wv);
+    if (jf == jl) return;  // one wavefront held the sequence and wrote its row
+    const int np = jl - jf + 1;
+    const int64_t base = (int64_t)head * slots + jf + seq;
+    const f32x2 *ml = (const f32x2 *)(ws_ml + base * 2);
+    // One pass with a running maximum, so each partial's (m, l) and o are
+    // loaded together: c_p = l_p * 2^(m_p - M) rescaled as M grows.
+    const float *o = ws_o + base * D + lane * PER;
 #pragma unroll 4
-  for (int p = 0; p < np; ++p) {
-    const f32x2 v = ml[p];
-    float op[PER];
+    for (int p = 0; p < np; ++p) {
+      const f32x2 v = ml[p];
+      float opv[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) op[i] = o[(int64_t)p * D + i];
-    const float m_new = fmaxf(big, v.x);
-    const float a = __builtin_amdgcn_exp2f(big - m_new);  // 0 on the first partial
-    const float c = v.y * __builtin_amdgcn_exp2f(v.x - m_new);
-    den = den * a + c;
+      for (int i = 0; i < PER; ++i) opv[i] = o[(int64_t)p * D + i];
+      const float m_new = fmaxf(big, v.x);
+      const float a = __builtin_amdgcn_exp2f(big - m_new);  // 0 on the first partial
+      const float c = v.y * __builtin_amdgcn_exp2f(v.x - m_new);
+      den = den * a + c;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) num[i] = num[i] * a + c * op[i];
-    big = m_new;
+      for (int i = 0; i < PER; ++i) num[i] = num[i] * a + c * opv[i];
+      big = m_new;
+    }
   }
   const float inv = 1.0f / den;
-  uint16_t *op = out + ((int64_t)seq * num_heads + head) * D + lane * PER;
   if constexpr (PER == 2) {
     *(uint32_t *)op = E::pack(num[0] * inv, num[1] * inv);
   } else {
@@ -570,21 +671,29 @@ int launch_typed(const DecodeArgs &a) {
           (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, (const uint16_t *)a.q, a.k_cache,
           a.v_cache, a.block_tables, a.context_lens, scale_log2, a.v_scale, a.num_seqs,
           a.num_kv_heads, a.num_heads, group, a.max_blocks_per_seq, a.num_blocks, a.waves,
-          a.slots);
+          a.slots, a.append);
     else
       decode_split_kernel<DT, D, BS, false><<<grid, kWave, lds, st>>>(
           (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, (const uint16_t *)a.q, a.k_cache,
           a.v_cache, a.block_tables, a.context_lens, scale_log2, 1.0f, a.num_seqs,
           a.num_kv_heads, a.num_heads, group, a.max_blocks_per_seq, a.num_blocks, a.waves,
-          a.slots);
+          a.slots, a.append);
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
   if (a.stages & 2) {
     dim3 g2((unsigned)a.num_heads, (unsigned)a.num_seqs);
-    decode_merge_kernel<DT, D><<<g2, kWave, 0, st>>>(
-        (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, a.num_seqs, a.num_heads, a.waves,
-        a.slots);
+#define PA_MERGE(APPEND, KV8)                                                                 \
+  decode_merge_kernel<DT, D, APPEND, KV8><<<g2, kWave, 0, st>>>(                              \
+      (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, a.num_seqs, a.num_heads, a.waves, a.slots, \
+      (const uint16_t *)a.q, (const uint16_t *)a.k_new, (const uint16_t *)a.v_new,          \
+      (void *)a.k_cache, (void *)a.v_cache, a.block_tables, a.context_lens, scale_log2,       \
+      a.v_scale, a.k_inv, a.v_inv, a.num_kv_heads, group, a.block_size,                       \
+      a.max_blocks_per_seq, a.num_blocks)
+    if (!a.append) PA_MERGE(false, false);
+    else if (a.kv_fp8) PA_MERGE(true, true);
+    else PA_MERGE(true, false);
+#undef PA_MERGE
     e = hipGetLastError();
   }
   return (int)e;

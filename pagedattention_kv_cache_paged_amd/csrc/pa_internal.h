@@ -40,6 +40,15 @@ struct DecodeArgs {
   float *ws_ml;        // [num_heads][slots][2]  (running max in log2 units, sum)
   int32_t *ws_cu;      // [num_seqs + 1] tile prefix, written by the split pass
   int32_t stages;      // bit 0: split pass, bit 1: merge pass
+  // Fused append: the new token of each sequence (k_new, v_new [num_seqs,
+  // num_kv_heads, head_dim], the q dtype) is context position L-1.  The
+  // split pass then attends over positions 0 .. L-2 only, and the merge
+  // pass adds the new token and stores it into its cache slot.
+  int32_t append;
+  const void *k_new;
+  const void *v_new;
+  float k_inv;         // float32(1 / k_scale): E4M3 quantisation of k_new
+  float v_inv;
   void *stream;
 };
 

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -60,31 +61,6 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
     vd[6 * BS] = (uint16_t)(vx.w & 0xffffu);
     vd[7 * BS] = (uint16_t)(vx.w >> 16);
   }
-}
-
-// E4M3 (OCP e4m3fn) code of y: nearest representable value, ties to the
-// even code, finite magnitudes from 448 up saturate to +-448, NaN -> 0x7f.
-// Below 2^-6 the grid is m * 2^-9 (rint of y * 512, exact scaling); above,
-// the fp32 fraction is cut to 3 bits with round-to-nearest-even, a carry
-// moving into the exponent as it should.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = fabsf(y);
-  if (!(a == a)) return 0x7fu;
-  if (a >= 448.0f) return sign | 0x7eu;
-  if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);
-  const uint32_t ua = __float_as_uint(a);
-  uint32_t code = ((((ua >> 23) & 0xffu) - 127u + 7u) << 3) | ((ua >> 20) & 7u);
-  const uint32_t rest = ua & 0xfffffu;  // the 20 fraction bits dropped
-  if (rest > 0x80000u || (rest == 0x80000u && (code & 1u))) code += 1u;
-  return sign | code;
-}
-
-template <int DT>
-__device__ __forceinline__ float elem_to_float(uint32_t bits16) {
-  if constexpr (DT == 1) return __uint_as_float(bits16 << 16);  // bfloat16
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);  // binary16
 }
 
 // Quantising append into E4M3 caches: element x goes in as the code of

@@ -30,10 +30,11 @@ def test_library_exports_every_declared_symbol():
     assert {"paged_kv_write", "paged_attention_decode", "paged_attention_decode_ex",
             "paged_attention_decode_stages", "paged_attention_workspace_bytes",
             "paged_attention_split_waves", "paged_validate_metadata", "pa_strerror",
-            "pa_abi_version", "paged_kv_write_fp8", "paged_attention_decode_fp8"} <= set(names)
+            "pa_abi_version", "paged_kv_write_fp8", "paged_attention_decode_fp8",
+            "paged_attention_decode_append"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 3
+    assert lib.pa_abi_version() == 4
 
 
 def test_single_hip_runtime():
@@ -190,3 +191,38 @@ def test_binding_rejects_cpu_tensors():
                                  torch.zeros(4, 2, 64, 16, dtype=torch.float16),
                                  torch.zeros(2, 1, dtype=torch.int32),
                                  torch.ones(2, dtype=torch.int32), 0.125, 16, 2)
+
+
+def _append(**kw):
+    a = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, scale=0.125,
+             ks=1.0, vs=1.0, bs=16, hkv=8, B=4, hq=32, d=128, mb=128, nb=1000, dtype=1, fp8=0,
+             pt=0, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return B.load().paged_attention_decode_append(
+        a["out"], a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["bt"], a["cl"], a["scale"],
+        a["ks"], a["vs"], a["bs"], a["hkv"], a["B"], a["hq"], a["d"], a["mb"], a["nb"],
+        a["dtype"], a["fp8"], a["pt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), -1), (dict(vn=None), -1), (dict(out=None), -1),
+    (dict(kn=FAKE + 2), -7), (dict(vn=FAKE + 1), -7),
+    (dict(fp8=2), -2), (dict(dtype=3), -2),
+    (dict(fp8=1, ks=0.0), -3), (dict(fp8=1, vs=float("nan")), -3),
+    (dict(d=96), -3), (dict(bs=12), -3), (dict(hq=30), -3),
+    (dict(wsb=16), -4), (dict(ws=None), -4),
+])
+def test_append_rejects_before_launch(kw, code):
+    assert _append(**kw) == code
+
+
+def test_append_zero_sequences_is_noop():
+    assert _append(B=0, out=None, q=None, kn=None, vn=None) == 0
+
+
+def test_append_binding_checks_shapes():
+    """The Python mirror rejects mismatched tensors before calling the
+    library (CPU tensors never reach it: the device check comes first)."""
+    q = torch.zeros(2, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        B.paged_attention_decode_append(q, q, q, q, q, q, q, q, 0.1, 16, 2)
