@@ -1,9 +1,13 @@
 #!/usr/bin/env python3
 """Paged decode benchmark on one MI355X: KV append + paged decode attention.
 
-One step = one pass of the whole hot path over the workload's batch:
-``paged_kv_write`` of one new token per sequence, then the two launches of
-``paged_attention_decode`` (split pass, log-sum-exp merge).  Inputs are
+One step = one pass of the whole hot path over the workload's batch: the
+append of one new token per sequence and decode attention over every
+context.  By default the step is ``paged_attention_decode_append`` (split
+pass, then the log-sum-exp merge that also adds and stores the new token);
+``--step separate`` times ``paged_kv_write`` followed by the two launches of
+``paged_attention_decode`` instead, and each run reports the other form's
+time per step too.  Inputs are
 seeded synthetic data resident in HBM before timing starts.  The K/V pool is
 replicated into several copies that the steps rotate through, so a step never
 finds its blocks in L2 / the 256 MB Infinity Cache from the step before.
@@ -170,6 +174,9 @@ def main():
                     help="physical block placement of the llama8b workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step", default="fused", choices=("fused", "separate"),
+                    help="fused: paged_attention_decode_append (two launches); separate: "
+                         "paged_kv_write + paged_attention_decode (three launches)")
     ap.add_argument("--kv-dtype", default="native", choices=("native", "fp8"),
                     help="KV cache element type: the workload's 16-bit type, or E4M3 codes")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -277,10 +284,26 @@ def main():
                 ws.data_ptr(), ws.numel(), stages, sp)
         assert rc == 0, rc
 
-    for i in range(args.warmup):
+    def fused(i):
+        kc, vc = caches[i % copies]
+        rc = lib.paged_attention_decode_append(
+            out.data_ptr(), q.data_ptr(), nk.data_ptr(), nv.data_ptr(), kc.data_ptr(),
+            vc.data_ptr(), bt.data_ptr(), cl.data_ptr(), w.scale, FP8_K_SCALE, FP8_V_SCALE,
+            w.block_size, w.num_kv_heads, w.num_seqs, w.num_heads, w.head_dim,
+            w.max_blocks_per_seq, w.num_blocks, dtc, 1 if fp8 else 0, pt, ws.data_ptr(),
+            ws.numel(), sp)
+        assert rc == 0, rc
+
+    def separate(i):
         write(i)
         decode(i, 1)
         decode(i, 2)
+
+    steps = {"fused": fused, "separate": separate}
+    step = steps[args.step]
+    for i in range(args.warmup):
+        for f in steps.values():
+            f(i)
     torch.cuda.synchronize()
 
     # Timed region: exactly K steps, nothing else on the stream.
@@ -290,13 +313,21 @@ def main():
     t_wall = time.perf_counter()
     start.record(stream)
     for i in range(K):
-        write(i)
-        decode(i, 1)
-        decode(i, 2)
+        step(i)
     stop.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(stop) / K
+
+    # The other form of the step, timed the same way (informative).
+    other = "separate" if args.step == "fused" else "fused"
+    o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    o0.record(stream)
+    for i in range(K):
+        steps[other](i)
+    o1.record(stream)
+    torch.cuda.synchronize()
+    ms_other = o0.elapsed_time(o1) / K
 
     # Roofline of the split pass: K back-to-back split launches on the launch
     # stream, bracketed by two events (average launch duration, no event
@@ -365,6 +396,8 @@ def main():
             "placement": args.placement if args.workload == "llama8b" else "random",
         },
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "step": args.step,
+        f"ms_per_step_{other}": round(ms_other, 5),
         "seq_tokens_per_s": round(w.logical_tokens / (ms_step * 1e-3), 1),
         "new_tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "split_us_back_to_back": round(t_split, 3),

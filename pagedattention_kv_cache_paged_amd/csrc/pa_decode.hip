@@ -507,15 +507,66 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
 // The partials of sequence s come from wavefronts wave_of(cu[s]) ..
 // wave_of(cu[s+1] - 1), in consecutive slots starting at that first
 // wavefront + s.
-//
-// APPEND: the sequence's new token (position L-1, which the split pass left
-// out) joins as one more partial with m = its score, l = 1, o = its V row,
-// and the wave of each group's first query head stores that token's K and V
-// into the caches at position L-1 of the block table, as the append step
-// would (KV8: as E4M3 codes of x * k_inv / v_inv, whose values then enter
-// the attention).  Every output row is written here, zeros for L = 0.
-template <int DT, int D, bool APPEND, bool KV8>
+template <int DT, int D>
 __global__ __launch_bounds__(kWave) void decode_merge_kernel(
+    uint16_t *__restrict__ out, const float *__restrict__ ws_o,
+    const float *__restrict__ ws_ml, const int32_t *__restrict__ ws_cu, int num_seqs,
+    int num_heads, int waves, int slots) {
+  using E = Elem<DT>;
+  constexpr int PER = D / kWave;  // dims per lane
+  const int head = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int n_tiles = ws_cu[num_seqs];
+  const int c0 = ws_cu[seq], c1 = ws_cu[seq + 1];
+  if (c1 <= c0) return;  // nothing to attend: the split pass wrote zeros
+  const int wv = min(waves, n_tiles);  // as in the split pass: all ranges non-empty
+  const int jf = wave_of(c0, n_tiles, wv);
+  const int jl = wave_of(c1 - 1, n_tiles, wv);
+  if (jf == jl) return;  // one wavefront held the sequence and wrote its row
+  const int np = jl - jf + 1;
+
+  const int64_t base = (int64_t)head * slots + jf + seq;
+  const f32x2 *ml = (const f32x2 *)(ws_ml + base * 2);
+  // One pass with a running maximum, so each partial's (m, l) and o are
+  // loaded together: c_p = l_p * 2^(m_p - M) rescaled as M grows.
+  float big = -INFINITY, den = 0.f;
+  float num[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) num[i] = 0.f;
+  const float *o = ws_o + base * D + lane * PER;
+#pragma unroll 4
+  for (int p = 0; p < np; ++p) {
+    const f32x2 v = ml[p];
+    float op[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) op[i] = o[(int64_t)p * D + i];
+    const float m_new = fmaxf(big, v.x);
+    const float a = __builtin_amdgcn_exp2f(big - m_new);  // 0 on the first partial
+    const float c = v.y * __builtin_amdgcn_exp2f(v.x - m_new);
+    den = den * a + c;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) num[i] = num[i] * a + c * op[i];
+    big = m_new;
+  }
+  const float inv = 1.0f / den;
+  uint16_t *op = out + ((int64_t)seq * num_heads + head) * D + lane * PER;
+  if constexpr (PER == 2) {
+    *(uint32_t *)op = E::pack(num[0] * inv, num[1] * inv);
+  } else {
+    op[0] = (uint16_t)(E::pack(num[0] * inv, 0.f) & 0xffffu);
+  }
+}
+
+// The merge of a decode step with the append fused in: the sequence's new
+// token (position L-1, which the split pass left out) joins as one more
+// partial with m = its score, l = 1, o = its V row, and the wave of each
+// group's first query head stores that token's K and V into the caches at
+// position L-1 of the block table, as the append step would (KV8: as E4M3
+// codes of x * k_inv / v_inv, whose values then enter the attention).
+// Every output row is written here, zeros for L = 0.
+template <int DT, int D, bool KV8>
+__global__ __launch_bounds__(kWave) void decode_merge_append_kernel(
     uint16_t *__restrict__ out, const float *__restrict__ ws_o,
     const float *__restrict__ ws_ml, const int32_t *__restrict__ ws_cu, int num_seqs,
     int num_heads, int waves, int slots, const uint16_t *__restrict__ q,
@@ -532,11 +583,13 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
   uint16_t *op = out + ((int64_t)seq * num_heads + head) * D + lane * PER;
   const int n_tiles = ws_cu[num_seqs];
   const int c0 = ws_cu[seq], c1 = ws_cu[seq + 1];
+  // Running combination: M the max so far (log2 units), den = sum c_p,
+  // num = sum c_p o_p, with c_p = l_p * 2^(m_p - M).
   float big = -INFINITY, den = 0.f;
   float num[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) num[i] = 0.f;
-  if constexpr (APPEND) {
+  {
     const int len = min(max(context_lens[seq], 0), max_blocks * block_size);
     if (len == 0) {  // nothing to attend and nothing to append
       if constexpr (PER == 2) *(uint32_t *)op = 0u;
@@ -597,40 +650,18 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
         }
       }
     }
-    if (c1 > c0) {
-      const int wv = min(waves, n_tiles);
-      const int jf = wave_of(c0, n_tiles, wv);
-      const int jl = wave_of(c1 - 1, n_tiles, wv);
-      // fall through to the partials below
-      const int64_t base = (int64_t)head * slots + jf + seq;
-      const f32x2 *ml = (const f32x2 *)(ws_ml + base * 2);
-      const float *o = ws_o + base * D + lane * PER;
-      for (int p = 0; p <= jl - jf; ++p) {
-        const f32x2 v = ml[p];
-        float opv[PER];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) opv[i] = o[(int64_t)p * D + i];
-        const float m_new = fmaxf(big, v.x);
-        const float a = __builtin_amdgcn_exp2f(big - m_new);
-        const float c = v.y * __builtin_amdgcn_exp2f(v.x - m_new);
-        den = den * a + c;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) num[i] = num[i] * a + c * opv[i];
-        big = m_new;
-      }
-    }
-  } else {
-    if (c1 <= c0) return;  // nothing to attend: the split pass wrote zeros
+    if (c1 <= c0) goto done;  // the new token is the whole context
+  }
+  {
     const int wv = min(waves, n_tiles);  // as in the split pass: all ranges non-empty
     const int jf = wave_of(c0, n_tiles, wv);
     const int jl = wave_of(c1 - 1, n_tiles, wv);
-    if (jf == jl) return;  // one wavefront held the sequence and wrote its row
     const int np = jl - jf + 1;
     const int64_t base = (int64_t)head * slots + jf + seq;
     const f32x2 *ml = (const f32x2 *)(ws_ml + base * 2);
+    const float *o = ws_o + base * D + lane * PER;
     // One pass with a running maximum, so each partial's (m, l) and o are
     // loaded together: c_p = l_p * 2^(m_p - M) rescaled as M grows.
-    const float *o = ws_o + base * D + lane * PER;
 #pragma unroll 4
     for (int p = 0; p < np; ++p) {
       const f32x2 v = ml[p];
@@ -638,7 +669,7 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
 #pragma unroll
       for (int i = 0; i < PER; ++i) opv[i] = o[(int64_t)p * D + i];
       const float m_new = fmaxf(big, v.x);
-      const float a = __builtin_amdgcn_exp2f(big - m_new);  // 0 on the first partial
+      const float a = __builtin_amdgcn_exp2f(big - m_new);  // 0 while nothing is held
       const float c = v.y * __builtin_amdgcn_exp2f(v.x - m_new);
       den = den * a + c;
 #pragma unroll
@@ -646,6 +677,7 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
       big = m_new;
     }
   }
+done:
   const float inv = 1.0f / den;
   if constexpr (PER == 2) {
     *(uint32_t *)op = E::pack(num[0] * inv, num[1] * inv);
@@ -683,16 +715,19 @@ int launch_typed(const DecodeArgs &a) {
   }
   if (a.stages & 2) {
     dim3 g2((unsigned)a.num_heads, (unsigned)a.num_seqs);
-#define PA_MERGE(APPEND, KV8)                                                                 \
-  decode_merge_kernel<DT, D, APPEND, KV8><<<g2, kWave, 0, st>>>(                              \
+#define PA_MERGE(KV8)                                                                         \
+  decode_merge_append_kernel<DT, D, KV8><<<g2, kWave, 0, st>>>(                               \
       (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, a.num_seqs, a.num_heads, a.waves, a.slots, \
       (const uint16_t *)a.q, (const uint16_t *)a.k_new, (const uint16_t *)a.v_new,          \
       (void *)a.k_cache, (void *)a.v_cache, a.block_tables, a.context_lens, scale_log2,       \
       a.v_scale, a.k_inv, a.v_inv, a.num_kv_heads, group, a.block_size,                       \
       a.max_blocks_per_seq, a.num_blocks)
-    if (!a.append) PA_MERGE(false, false);
-    else if (a.kv_fp8) PA_MERGE(true, true);
-    else PA_MERGE(true, false);
+    if (!a.append)
+      decode_merge_kernel<DT, D><<<g2, kWave, 0, st>>>(
+          (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, a.num_seqs, a.num_heads, a.waves,
+          a.slots);
+    else if (a.kv_fp8) PA_MERGE(true);
+    else PA_MERGE(false);
 #undef PA_MERGE
     e = hipGetLastError();
   }
