@@ -100,6 +100,8 @@ def _load():
     lib.oracle_decode_fp8.restype = i32
     lib.oracle_decode_fp8_rows.argtypes = [p, p, i32] + common8
     lib.oracle_decode_fp8_rows.restype = i32
+    lib.oracle_copy_blocks.argtypes = [p, p, p, i64, i32, i32, i32, i64, i32]
+    lib.oracle_copy_blocks.restype = i32
     _lib = lib
     return lib
 
@@ -281,3 +283,17 @@ def decode_fp8_rows(rows, q, k_cache, v_cache, block_tables, context_lens, scale
     del keep
     return out
 
+
+
+def copy_blocks(pairs, k_cache, v_cache, block_size: int) -> None:
+    """In-place copy-on-write block copies: for each (src, dst) row of
+    pairs (int64 [n, 2]; negative ids skipped), block dst of both caches
+    (16-bit bits or uint8 E4M3 codes) becomes block src."""
+    pairs = np.ascontiguousarray(pairs, dtype=np.int64).reshape(-1, 2)
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    assert k_cache.dtype == v_cache.dtype and k_cache.dtype.itemsize in (1, 2)
+    nb, hkv, bs, d = k_cache.shape
+    assert bs == block_size and v_cache.shape == (nb, hkv, d, bs)
+    rc = _load().oracle_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0],
+                                    hkv, d, bs, nb, k_cache.dtype.itemsize)
+    _check(rc, "oracle_copy_blocks")

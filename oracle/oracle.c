@@ -536,3 +536,62 @@ int oracle_decode_fp8_rows(double *out, const int32_t *rows, int num_rows,
   return ORACLE_OK;
 }
 
+
+/* ---- block copy for copy-on-write ------------------------------------------ */
+
+/* [P4] 2.3: a sequence about to write into a block it shares with others
+ * gets a private copy first.  For each pair i in order (src = pairs[2i],
+ * dst = pairs[2i+1]), every element of block dst in both caches becomes the
+ * element of block src at the same (kv head, offset, dim): K[dst][j][o][d] =
+ * K[src][j][o][d] and V[dst][j][d][o] = V[src][j][d][o].  Elements are
+ * elem_bytes wide (2: binary16 / bfloat16 bits, 1: E4M3 codes) and copied
+ * as raw bytes.  A pair with a negative id is skipped.  The pairs must have
+ * distinct destinations, none of them also a source, so that the order of
+ * the copies cannot matter; otherwise, or for an id >= num_blocks, nothing
+ * is copied and ORACLE_EBLOCK is returned. */
+int oracle_copy_blocks(void *k_cache, void *v_cache, const int64_t *pairs, int64_t num_pairs,
+                       int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                       int elem_bytes) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || (elem_bytes != 1 && elem_bytes != 2))
+    return ORACLE_EARG;
+  unsigned char *role = calloc((size_t)num_blocks, 1); /* bit 0: source, bit 1: destination */
+  if (!role) return ORACLE_ENOMEM;
+  for (int64_t i = 0; i < num_pairs; ++i) {
+    int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (src >= num_blocks || dst >= num_blocks) {
+      free(role);
+      return ORACLE_EBLOCK;
+    }
+    if (src < 0 || dst < 0) continue;
+    if (role[dst] & 2) {
+      free(role);
+      return ORACLE_EBLOCK;
+    }
+    role[dst] |= 2;
+    role[src] |= 1;
+  }
+  for (int64_t b = 0; b < num_blocks; ++b)
+    if (role[b] == 3) {
+      free(role);
+      return ORACLE_EBLOCK;
+    }
+  free(role);
+
+  unsigned char *kc = (unsigned char *)k_cache, *vc = (unsigned char *)v_cache;
+  for (int64_t i = 0; i < num_pairs; ++i) {
+    int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (src < 0 || dst < 0) continue;
+    for (int j = 0; j < num_kv_heads; ++j)
+      for (int o = 0; o < block_size; ++o)
+        for (int d = 0; d < head_dim; ++d) {
+          int64_t ks = (((src * num_kv_heads + j) * (int64_t)block_size + o) * head_dim + d);
+          int64_t kd = (((dst * num_kv_heads + j) * (int64_t)block_size + o) * head_dim + d);
+          int64_t vs = (((src * num_kv_heads + j) * (int64_t)head_dim + d) * block_size + o);
+          int64_t vd = (((dst * num_kv_heads + j) * (int64_t)head_dim + d) * block_size + o);
+          memcpy(kc + kd * elem_bytes, kc + ks * elem_bytes, (size_t)elem_bytes);
+          memcpy(vc + vd * elem_bytes, vc + vs * elem_bytes, (size_t)elem_bytes);
+        }
+  }
+  return ORACLE_OK;
+}

@@ -80,6 +80,26 @@ def load() -> ctypes.CDLL:
     lib.paged_attention_decode_append.argtypes = [p, p, p, p, p, p, p, p, f32, f32, f32, i32,
                                                   i32, i32, i32, i32, i32, i64, i32, i32, i32,
                                                   p, sz, p]
+    lib.pa_pool_create.restype = ctypes.c_int
+    lib.pa_pool_create.argtypes = [i64, p, ctypes.POINTER(p)]
+    lib.pa_pool_destroy.restype = None
+    lib.pa_pool_destroy.argtypes = [p]
+    for fn in ("pa_pool_num_blocks", "pa_pool_num_free"):
+        getattr(lib, fn).restype = i64
+        getattr(lib, fn).argtypes = [p]
+    lib.pa_pool_alloc.restype = i64
+    lib.pa_pool_alloc.argtypes = [p]
+    for fn in ("pa_pool_incref", "pa_pool_decref"):
+        getattr(lib, fn).restype = ctypes.c_int
+        getattr(lib, fn).argtypes = [p, i64]
+    lib.pa_pool_refcount.restype = i32
+    lib.pa_pool_refcount.argtypes = [p, i64]
+    lib.pa_pool_cow.restype = ctypes.c_int
+    lib.pa_pool_cow.argtypes = [p, i64, ctypes.POINTER(i64), ctypes.POINTER(i32)]
+    lib.paged_copy_blocks.restype = ctypes.c_int
+    lib.paged_copy_blocks.argtypes = [p, p, p, i64, i32, i32, i32, i64, i32, p]
+    lib.paged_validate_copy_pairs.restype = ctypes.c_int
+    lib.paged_validate_copy_pairs.argtypes = [p, i64, i64]
     lib.paged_validate_metadata.restype = ctypes.c_int
     lib.paged_validate_metadata.argtypes = [p, p, i32, i32, i32, i64, p, i64]
     _lib = lib
@@ -340,3 +360,85 @@ def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: tor
         nb, dt, 1 if fp8 else 0, partition_tokens, ws_ptr, ws_len, _stream(dev))
     _check("paged_attention_decode_append", rc)
     return out
+
+
+# ---- block pool and copy-on-write (include/paged_blocks.h) ------------------
+
+class BlockPool:
+    """Reference-counted pool of physical block ids (host object of the
+    library).  alloc() returns -1 when the pool is exhausted."""
+
+    def __init__(self, num_blocks: int, order=None):
+        import numpy as np
+        lib = load()
+        self._order = None if order is None else np.ascontiguousarray(order, dtype=np.int64)
+        h = ctypes.c_void_p()
+        _check("pa_pool_create", lib.pa_pool_create(
+            num_blocks, None if self._order is None else self._order.ctypes.data,
+            ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if self._h:
+            load().pa_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_blocks(self) -> int:
+        return int(load().pa_pool_num_blocks(self._h))
+
+    @property
+    def num_free(self) -> int:
+        return int(load().pa_pool_num_free(self._h))
+
+    def alloc(self) -> int:
+        return int(load().pa_pool_alloc(self._h))
+
+    def incref(self, block: int) -> None:
+        _check("pa_pool_incref", load().pa_pool_incref(self._h, block))
+
+    def decref(self, block: int) -> None:
+        _check("pa_pool_decref", load().pa_pool_decref(self._h, block))
+
+    def refcount(self, block: int) -> int:
+        return int(load().pa_pool_refcount(self._h, block))
+
+    def cow(self, block: int):
+        """(dst, copy): the block to write into and whether block -> dst
+        must be copied first."""
+        dst, copy = ctypes.c_int64(), ctypes.c_int32()
+        _check("pa_pool_cow", load().pa_pool_cow(self._h, block, ctypes.byref(dst),
+                                                 ctypes.byref(copy)))
+        return int(dst.value), bool(copy.value)
+
+
+def paged_copy_blocks(pairs: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
+                      ) -> None:
+    """Block pairs[i, 1] of both caches becomes a copy of block pairs[i, 0]
+    (int64 [n, 2] on the caches' device; negative ids skipped).  16-bit or
+    uint8 (E4M3) caches in the layouts of paged_kv_write."""
+    dev = _dev(pairs, k_cache, v_cache)
+    if pairs.dtype != torch.int64 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int64 [num_pairs, 2]")
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    nb, hkv, bs, d = k_cache.shape
+    if tuple(v_cache.shape) != (nb, hkv, d, bs) or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size], "
+                         "k_cache's dtype")
+    rc = load().paged_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), pairs.data_ptr(),
+                                  pairs.shape[0], hkv, d, bs, nb, k_cache.element_size(),
+                                  _stream(dev))
+    _check("paged_copy_blocks", rc)
+
+
+def validate_copy_pairs(pairs, num_blocks: int) -> int:
+    import numpy as np
+    pr = np.ascontiguousarray(np.asarray(pairs), dtype=np.int64).reshape(-1, 2)
+    return int(load().paged_validate_copy_pairs(pr.ctypes.data, pr.shape[0], num_blocks))

@@ -70,8 +70,19 @@ struct WriteArgs {
   void *stream;
 };
 
+struct CopyArgs {
+  void *k_cache;
+  void *v_cache;
+  const int64_t *pairs;  // device [num_pairs][2] (src, dst)
+  int64_t num_pairs;
+  int64_t run_bytes;     // bytes of one block of one cache (a multiple of 16)
+  int64_t num_blocks;
+  void *stream;
+};
+
 // Return 0 on success, a nonzero HIP error code otherwise.
 int launch_decode(const DecodeArgs &a);
 int launch_kv_write(const WriteArgs &a);
+int launch_copy_blocks(const CopyArgs &a);
 
 }  // namespace pa

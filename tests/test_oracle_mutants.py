@@ -2,8 +2,9 @@
 
 Each case plants one mistake in a copy of oracle/oracle.c (a dropped term, a
 wrong sign, index or layout, a transposed operand), builds it on the CPU into
-a temporary library and runs tests/test_oracle_pins.py and
-tests/test_oracle_fp8.py against that library in a subprocess.  The pin suite must fail for every mutant and pass for the
+a temporary library and runs tests/test_oracle_pins.py,
+tests/test_oracle_fp8.py and tests/test_oracle_blocks.py against that
+library in a subprocess.  The pin suite must fail for every mutant and pass for the
 unmodified copy.
 """
 import concurrent.futures as cf
@@ -17,7 +18,8 @@ import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = [os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-        os.path.join(ROOT, "tests", "test_oracle_fp8.py")]
+        os.path.join(ROOT, "tests", "test_oracle_fp8.py"),
+        os.path.join(ROOT, "tests", "test_oracle_blocks.py")]
 
 # (name, original text, planted text) -- the first occurrence is replaced
 MUTANTS = [
@@ -62,6 +64,14 @@ MUTANTS = [
      "const uint16_t *qrow = q + ((int64_t)h * num_seqs + s) * head_dim;"),
     ("write_offset_shift", "int offset = (int)(slot % block_size);",
      "int offset = (int)((slot + 1) % block_size);"),
+    ("copy_first_head_only", "for (int j = 0; j < num_kv_heads; ++j)\n      for (int o = 0; o < block_size; ++o)",
+     "for (int j = 0; j < 1; ++j)\n      for (int o = 0; o < block_size; ++o)"),
+    ("copy_v_token_major",
+     "int64_t vd = (((dst * num_kv_heads + j) * (int64_t)head_dim + d) * block_size + o);",
+     "int64_t vd = (((dst * num_kv_heads + j) * (int64_t)block_size + o) * head_dim + d);"),
+    ("copy_reversed", "memcpy(kc + kd * elem_bytes, kc + ks * elem_bytes, (size_t)elem_bytes);",
+     "memcpy(kc + ks * elem_bytes, kc + kd * elem_bytes, (size_t)elem_bytes);"),
+    ("copy_accepts_dst_as_src", "    if (role[b] == 3) {", "    if (role[b] == 7) {"),
 ]
 # the consistent V-layout mutant also moves the write to token-major order
 EXTRA = {
