@@ -162,6 +162,89 @@ def cpu_baseline(w, seconds: float, fp8: bool = False):
             "seq_tokens_per_s": round(done_tokens / t_total, 1)}
 
 
+COPY_KERNEL = "copy_blocks_kernel"
+
+
+def bench_copy_blocks(args, torch, B, W, dev, lib):
+    """Copy-on-write at the prefix-sharing shape: 128 sequences forked from a
+    1000-token prompt (bs 16, so the prompt's last block holds 8 tokens and is
+    shared) each copy that block before their first append: 128 (src, dst)
+    pairs, one source, distinct destinations; 8 KV heads, head_dim 128, bf16.
+    Bytes per pair: K + V runs of H_kv * bs * D * 2 B, read and written.
+    A second figure copies 4096 distinct random pairs (a swap-sized batch)."""
+    hkv, d, bs, nforks = 8, 128, 16, 128
+    run = hkv * bs * d * 2
+    nb = 8192
+    g = np.random.default_rng(31)
+    ids = g.permutation(nb)
+    shared = int(ids[0])
+    cow_pairs = np.stack([np.full(nforks, shared), ids[1:1 + nforks]], axis=1).astype(np.int64)
+    big_pairs = np.stack([ids[:4096], ids[4096:8192]], axis=1).astype(np.int64)
+    kc = torch.randint(-30000, 30000, (nb, hkv, bs, d), dtype=torch.int16, device=dev)
+    vc = torch.randint(-30000, 30000, (nb, hkv, d, bs), dtype=torch.int16, device=dev)
+    sp = torch.cuda.current_stream().cuda_stream
+    stream = torch.cuda.current_stream()
+
+    def timed(pairs_np, K):
+        pairs = torch.from_numpy(pairs_np).to(dev)
+        n = pairs.shape[0]
+
+        def launch():
+            rc = lib.paged_copy_blocks(kc.data_ptr(), vc.data_ptr(), pairs.data_ptr(), n, hkv,
+                                       d, bs, nb, 2, sp)
+            assert rc == 0, rc
+        for _ in range(args.warmup):
+            launch()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(K):
+            launch()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / K * 1e3  # us
+
+    K = args.steps
+    t_cow = timed(cow_pairs, K)
+    t_big = timed(big_pairs, K)
+    cow_bytes = nforks * 2 * run * 2          # K and V runs, read + written
+    big_bytes = big_pairs.shape[0] * 2 * run * 2
+    gbs = cow_bytes / (t_cow * 1e-6) / 1e9
+    big_gbs = big_bytes / (t_big * 1e-6) / 1e9
+    result = {
+        "metric": "copy-on-write block copy GB/s (read + written), prefix-sharing shape",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(t_cow * 1e-3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"prefix CoW: {nforks} forks copy one shared partly-filled "
+                               f"block; {hkv} kv heads, head_dim {d}, block {bs}, bf16",
+                   "pairs": nforks, "bytes_per_pair": 2 * run * 2},
+        "roofline": {"kernel": COPY_KERNEL, "bound": "hbm", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "avg_launch_us": round(t_cow, 3), "traffic": None,
+                     "bytes_per_launch": cow_bytes},
+        "batch_4096_pairs": {"us": round(t_big, 3), "GB/s": round(big_gbs, 2),
+                             "frac": round(big_gbs / HBM_PEAK_GBS, 4),
+                             "bytes_per_launch": big_bytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        hk = kc[:].cpu().numpy().view(np.uint16)
+        hv = vc[:].cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            oracle.copy_blocks(cow_pairs, hk, hv, bs)
+            reps += 1
+        t_cpu = (time.perf_counter() - t0) / reps
+        result["cpu_baseline"] = {"value": round(cow_bytes / t_cpu / 1e9, 6), "unit": "GB/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"the same {nforks} pairs, {reps} repetitions, "
+                                            f"the oracle's byte copy, single thread"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,6 +257,9 @@ def main():
                     help="physical block placement of the llama8b workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", default="decode", choices=("decode", "copy_blocks"),
+                    help="decode: the decode step (default); copy_blocks: the copy-on-write "
+                         "block copy of 128 forks of a shared prompt (prefix-sharing shape)")
     ap.add_argument("--step", default="fused", choices=("fused", "separate"),
                     help="fused: paged_attention_decode_append (two launches); separate: "
                          "paged_kv_write + paged_attention_decode (three launches)")
@@ -210,6 +296,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = B.load()
+    if args.op == "copy_blocks":
+        return bench_copy_blocks(args, torch, B, W, dev, lib)
     w = make_workload(args.workload, args.placement)
     tdt = {W.F16: torch.float16, W.BF16: torch.bfloat16}[w.dtype]
 
