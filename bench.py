@@ -245,6 +245,70 @@ def bench_copy_blocks(args, torch, B, W, dev, lib):
     print(json.dumps(result), flush=True)
 
 
+HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
+
+
+def bench_swap_blocks(args, torch, B, dev, lib):
+    """Preemption-sized swap at the Llama-3-8B head shape (8 KV heads,
+    head_dim 128, block 16, bf16: 32 KiB per block per cache): 1024 random
+    device blocks out to a pinned host pool, then back into other device
+    blocks.  Bytes per block: K + V runs (64 KiB) crossing the host link."""
+    hkv, d, bs, n = 8, 128, 16, 1024
+    run = hkv * bs * d * 2
+    nd = 8192
+    g = np.random.default_rng(41)
+    ids = g.permutation(nd)
+    out_pairs = torch.from_numpy(np.stack([ids[:n], np.arange(n)], 1).astype(np.int64)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([np.arange(n), ids[n:2 * n]], 1).astype(np.int64)).to(dev)
+    kc = torch.randint(-30000, 30000, (nd, hkv, bs, d), dtype=torch.int16, device=dev)
+    vc = torch.randint(-30000, 30000, (nd, hkv, d, bs), dtype=torch.int16, device=dev)
+    hk = torch.empty((n, hkv, bs, d), dtype=torch.int16).pin_memory()
+    hv = torch.empty((n, hkv, d, bs), dtype=torch.int16).pin_memory()
+    sp = torch.cuda.current_stream().cuda_stream
+    stream = torch.cuda.current_stream()
+
+    def swap(pairs, dk, dv, dn, sk, sv, sn):
+        rc = lib.paged_swap_blocks(dk.data_ptr(), dv.data_ptr(), dn, sk.data_ptr(),
+                                   sv.data_ptr(), sn, pairs.data_ptr(), n, hkv, d, bs, 2, sp)
+        assert rc == 0, rc
+
+    def timed(fn, K):
+        for _ in range(min(args.warmup, 3)):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(K):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / K * 1e3
+
+    K = max(1, min(args.steps, 20))
+    t_out = timed(lambda: swap(out_pairs, hk, hv, n, kc, vc, nd), K)
+    t_in = timed(lambda: swap(in_pairs, kc, vc, nd, hk, hv, n), K)
+    nbytes = n * 2 * run
+    gb_out, gb_in = nbytes / (t_out * 1e-6) / 1e9, nbytes / (t_in * 1e-6) / 1e9
+    result = {
+        "metric": "KV block swap GB/s over the host link (out and in), Llama-3-8B head shape",
+        "value": round(nbytes * 2 / ((t_out + t_in) * 1e-6) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": min(args.warmup, 3),
+        "ms_per_step": round((t_out + t_in) * 1e-3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"swap {n} blocks out to pinned host memory and back into "
+                               f"other device blocks; {hkv} kv heads, head_dim {d}, block "
+                               f"{bs}, bf16", "blocks": n, "bytes_per_block": 2 * run},
+        "swap_out": {"us": round(t_out, 2), "GB/s": round(gb_out, 2)},
+        "swap_in": {"us": round(t_in, 2), "GB/s": round(gb_in, 2)},
+        "roofline": {"kernel": COPY_KERNEL, "bound": "host link",
+                     "achieved": round(max(gb_out, gb_in), 2), "peak": HOST_LINK_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(max(gb_out, gb_in) / HOST_LINK_PEAK_GBS, 4),
+                     "avg_launch_us": round(min(t_out, t_in), 3), "traffic": None,
+                     "bytes_per_launch": nbytes},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,9 +321,10 @@ def main():
                     help="physical block placement of the llama8b workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="decode", choices=("decode", "copy_blocks"),
+    ap.add_argument("--op", default="decode", choices=("decode", "copy_blocks", "swap_blocks"),
                     help="decode: the decode step (default); copy_blocks: the copy-on-write "
-                         "block copy of 128 forks of a shared prompt (prefix-sharing shape)")
+                         "block copy of 128 forks of a shared prompt (prefix-sharing shape); "
+                         "swap_blocks: swap 1024 blocks out to pinned host memory and back")
     ap.add_argument("--step", default="fused", choices=("fused", "separate"),
                     help="fused: paged_attention_decode_append (two launches); separate: "
                          "paged_kv_write + paged_attention_decode (three launches)")
@@ -298,6 +363,8 @@ def main():
     lib = B.load()
     if args.op == "copy_blocks":
         return bench_copy_blocks(args, torch, B, W, dev, lib)
+    if args.op == "swap_blocks":
+        return bench_swap_blocks(args, torch, B, dev, lib)
     w = make_workload(args.workload, args.placement)
     tdt = {W.F16: torch.float16, W.BF16: torch.bfloat16}[w.dtype]
 

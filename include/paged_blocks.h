@@ -10,7 +10,8 @@
  * shared block goes to a private copy first (copy-on-write).  "vLLM memory
  * management and continuous batching from the source" (developer.cloud.
  * tencent.cn), part 2, 2.1-2.2: the physical blocks are a fixed pool handed
- * out on demand as sequences grow.
+ * out on demand as sequences grow.  "vLLM core architecture overview"
+ * (5688vip.com), 4.2: preempted requests' KV moves to CPU memory.
  *
  * Return codes are those of paged_attn.h (PA_OK, PA_ERR_*).
  */
@@ -91,6 +92,39 @@ int paged_copy_blocks(void *k_cache, void *v_cache, const int64_t *pairs, int64_
  * (skipped), destinations distinct, no destination also a source.
  * PA_OK or PA_ERR_METADATA. */
 int paged_validate_copy_pairs(const int64_t *pairs, int64_t num_pairs, int64_t num_blocks);
+
+/* ---- block swap between the device pool and a host pool -------------------
+ *
+ * "vLLM core architecture overview: PagedAttention, Continuous Batching,
+ * distributed inference" (5688vip.com), 4.2: when GPU memory runs short, a
+ * low-priority request is preempted and its KV blocks are moved out to CPU
+ * memory (and brought back when it resumes).  The host pool has the layouts
+ * of the device caches (paged_attn.h) with its own block count; allocate it
+ * as pinned memory (hipHostMalloc, or torch's pin_memory=True), which the
+ * kernel reads and writes directly through its device mapping.
+ *
+ * For every pair i < num_pairs with src = pairs[2i] in [0, src_num_blocks)
+ * and dst = pairs[2i+1] in [0, dst_num_blocks), block dst of the destination
+ * pool (both caches) becomes a bit copy of block src of the source pool.
+ * Swap-out: source = device caches, destination = host pool; swap-in: the
+ * other way round.  Pairs with an id outside its pool are skipped.
+ *   pairs: int64 [num_pairs][2], readable by the device (device or pinned
+ *   host memory), 8-byte aligned; caches and pools 16-byte aligned;
+ *   elem_bytes 2 (fp16 / bf16) or 1 (E4M3).
+ * The two pools must not overlap (within one pool use paged_copy_blocks)
+ * and destinations must be distinct (paged_validate_swap_pairs checks a
+ * host copy).  Asynchronous on `stream`: the host pool may be read only
+ * after the stream has been synchronised.  num_pairs = 0 is a no-op.
+ */
+int paged_swap_blocks(void *dst_k_cache, void *dst_v_cache, int64_t dst_num_blocks,
+                      const void *src_k_cache, const void *src_v_cache, int64_t src_num_blocks,
+                      const int64_t *pairs, int64_t num_pairs, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t elem_bytes, void *stream);
+
+/* Host check of swap pairs: ids below their pool's size or negative,
+ * destinations distinct.  PA_OK or PA_ERR_METADATA. */
+int paged_validate_swap_pairs(const int64_t *pairs, int64_t num_pairs, int64_t src_num_blocks,
+                              int64_t dst_num_blocks);
 
 #ifdef __cplusplus
 }

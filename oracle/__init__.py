@@ -102,6 +102,8 @@ def _load():
     lib.oracle_decode_fp8_rows.restype = i32
     lib.oracle_copy_blocks.argtypes = [p, p, p, i64, i32, i32, i32, i64, i32]
     lib.oracle_copy_blocks.restype = i32
+    lib.oracle_swap_blocks.argtypes = [p, p, i64, p, p, i64, p, i64, i32, i32, i32, i32]
+    lib.oracle_swap_blocks.restype = i32
     _lib = lib
     return lib
 
@@ -297,3 +299,20 @@ def copy_blocks(pairs, k_cache, v_cache, block_size: int) -> None:
     rc = _load().oracle_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0],
                                     hkv, d, bs, nb, k_cache.dtype.itemsize)
     _check(rc, "oracle_copy_blocks")
+
+
+def swap_blocks(pairs, dst_k, dst_v, src_k, src_v, block_size: int) -> None:
+    """Block copies between two pools (swap-out / swap-in): for each (src,
+    dst) row of pairs, block dst of (dst_k, dst_v) becomes block src of
+    (src_k, src_v); negative ids are skipped."""
+    pairs = np.ascontiguousarray(pairs, dtype=np.int64).reshape(-1, 2)
+    for a in (dst_k, dst_v, src_k, src_v):
+        assert a.flags.c_contiguous and a.dtype == dst_k.dtype and a.dtype.itemsize in (1, 2)
+    nd, hkv, bs, d = dst_k.shape
+    ns = src_k.shape[0]
+    assert bs == block_size and src_k.shape[1:] == dst_k.shape[1:]
+    assert dst_v.shape == (nd, hkv, d, bs) and src_v.shape == (ns, hkv, d, bs)
+    rc = _load().oracle_swap_blocks(_ptr(dst_k), _ptr(dst_v), nd, _ptr(src_k), _ptr(src_v), ns,
+                                    _ptr(pairs), pairs.shape[0], hkv, d, bs,
+                                    dst_k.dtype.itemsize)
+    _check(rc, "oracle_swap_blocks")

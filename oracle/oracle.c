@@ -595,3 +595,56 @@ int oracle_copy_blocks(void *k_cache, void *v_cache, const int64_t *pairs, int64
   }
   return ORACLE_OK;
 }
+
+/* ---- block swap between two pools ------------------------------------------- */
+
+/* [P1] 4.2: a preempted request's KV blocks move to CPU memory and back.
+ * For each pair i (src = pairs[2i] of the source pool, dst = pairs[2i+1] of
+ * the destination pool; both pools in the cache layouts above, with their
+ * own block counts), every element of destination block dst in both caches
+ * becomes the source element at the same (kv head, offset, dim), copied as
+ * raw bytes of elem_bytes.  A pair with a negative id is skipped.
+ * Destinations must be distinct; otherwise, or for an id past its pool,
+ * nothing is copied and ORACLE_EBLOCK is returned.  The pools are distinct
+ * objects, so no copy can read another's destination. */
+int oracle_swap_blocks(void *dst_k, void *dst_v, int64_t dst_num_blocks, const void *src_k,
+                       const void *src_v, int64_t src_num_blocks, const int64_t *pairs,
+                       int64_t num_pairs, int num_kv_heads, int head_dim, int block_size,
+                       int elem_bytes) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      dst_num_blocks <= 0 || src_num_blocks <= 0 || (elem_bytes != 1 && elem_bytes != 2))
+    return ORACLE_EARG;
+  unsigned char *taken = calloc((size_t)dst_num_blocks, 1);
+  if (!taken) return ORACLE_ENOMEM;
+  for (int64_t i = 0; i < num_pairs; ++i) {
+    int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (src >= src_num_blocks || dst >= dst_num_blocks) {
+      free(taken);
+      return ORACLE_EBLOCK;
+    }
+    if (src < 0 || dst < 0) continue;
+    if (taken[dst]) {
+      free(taken);
+      return ORACLE_EBLOCK;
+    }
+    taken[dst] = 1;
+  }
+  free(taken);
+  unsigned char *dk = (unsigned char *)dst_k, *dv = (unsigned char *)dst_v;
+  const unsigned char *sk = (const unsigned char *)src_k, *sv = (const unsigned char *)src_v;
+  for (int64_t i = 0; i < num_pairs; ++i) {
+    int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (src < 0 || dst < 0) continue;
+    for (int j = 0; j < num_kv_heads; ++j)
+      for (int o = 0; o < block_size; ++o)
+        for (int d = 0; d < head_dim; ++d) {
+          int64_t ks = (((src * num_kv_heads + j) * (int64_t)block_size + o) * head_dim + d);
+          int64_t kd = (((dst * num_kv_heads + j) * (int64_t)block_size + o) * head_dim + d);
+          int64_t vs = (((src * num_kv_heads + j) * (int64_t)head_dim + d) * block_size + o);
+          int64_t vd = (((dst * num_kv_heads + j) * (int64_t)head_dim + d) * block_size + o);
+          memcpy(dk + kd * elem_bytes, sk + ks * elem_bytes, (size_t)elem_bytes);
+          memcpy(dv + vd * elem_bytes, sv + vs * elem_bytes, (size_t)elem_bytes);
+        }
+  }
+  return ORACLE_OK;
+}

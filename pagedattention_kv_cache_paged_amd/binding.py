@@ -98,6 +98,10 @@ def load() -> ctypes.CDLL:
     lib.pa_pool_cow.argtypes = [p, i64, ctypes.POINTER(i64), ctypes.POINTER(i32)]
     lib.paged_copy_blocks.restype = ctypes.c_int
     lib.paged_copy_blocks.argtypes = [p, p, p, i64, i32, i32, i32, i64, i32, p]
+    lib.paged_swap_blocks.restype = ctypes.c_int
+    lib.paged_swap_blocks.argtypes = [p, p, i64, p, p, i64, p, i64, i32, i32, i32, i32, p]
+    lib.paged_validate_swap_pairs.restype = ctypes.c_int
+    lib.paged_validate_swap_pairs.argtypes = [p, i64, i64, i64]
     lib.paged_validate_copy_pairs.restype = ctypes.c_int
     lib.paged_validate_copy_pairs.argtypes = [p, i64, i64]
     lib.paged_validate_metadata.restype = ctypes.c_int
@@ -442,3 +446,41 @@ def validate_copy_pairs(pairs, num_blocks: int) -> int:
     import numpy as np
     pr = np.ascontiguousarray(np.asarray(pairs), dtype=np.int64).reshape(-1, 2)
     return int(load().paged_validate_copy_pairs(pr.ctypes.data, pr.shape[0], num_blocks))
+
+
+def paged_swap_blocks(pairs: torch.Tensor, dst_k: torch.Tensor, dst_v: torch.Tensor,
+                      src_k: torch.Tensor, src_v: torch.Tensor,
+                      stream_device: Optional[torch.device] = None) -> None:
+    """Block pairs[i, 1] of (dst_k, dst_v) becomes block pairs[i, 0] of
+    (src_k, src_v): device caches <-> a pinned host pool of the same layout
+    (swap-out / swap-in).  pairs: int64 [n, 2] on the device or pinned.
+    Runs on the current stream of the GPU involved."""
+    for t in (dst_k, dst_v, src_k, src_v, pairs):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if t.device.type == "cpu" and not t.is_pinned():
+            raise ValueError("host tensors must be pinned (pin_memory=True)")
+    dev = stream_device or next((t.device for t in (dst_k, src_k, pairs)
+                                 if t.device.type == "cuda"), None)
+    if dev is None:
+        raise ValueError("one side of the swap must be a GPU tensor")
+    if pairs.dtype != torch.int64 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int64 [num_pairs, 2]")
+    nd, hkv, bs, d = dst_k.shape
+    ns = src_k.shape[0]
+    if (tuple(src_k.shape[1:]) != (hkv, bs, d) or tuple(dst_v.shape) != (nd, hkv, d, bs) or
+            tuple(src_v.shape) != (ns, hkv, d, bs)):
+        raise ValueError("pools must share the cache layouts and sizes per block")
+    if len({t.dtype for t in (dst_k, dst_v, src_k, src_v)}) != 1:
+        raise ValueError("pools must share one element type")
+    rc = load().paged_swap_blocks(dst_k.data_ptr(), dst_v.data_ptr(), nd, src_k.data_ptr(),
+                                  src_v.data_ptr(), ns, pairs.data_ptr(), pairs.shape[0], hkv,
+                                  d, bs, dst_k.element_size(), _stream(dev))
+    _check("paged_swap_blocks", rc)
+
+
+def validate_swap_pairs(pairs, src_num_blocks: int, dst_num_blocks: int) -> int:
+    import numpy as np
+    pr = np.ascontiguousarray(np.asarray(pairs), dtype=np.int64).reshape(-1, 2)
+    return int(load().paged_validate_swap_pairs(pr.ctypes.data, pr.shape[0], src_num_blocks,
+                                                dst_num_blocks))

@@ -71,12 +71,15 @@ struct WriteArgs {
 };
 
 struct CopyArgs {
-  void *k_cache;
-  void *v_cache;
-  const int64_t *pairs;  // device [num_pairs][2] (src, dst)
+  void *dst_k;
+  void *dst_v;
+  const void *src_k;
+  const void *src_v;
+  const int64_t *pairs;  // device-visible [num_pairs][2] (src, dst)
   int64_t num_pairs;
   int64_t run_bytes;     // bytes of one block of one cache (a multiple of 16)
-  int64_t num_blocks;
+  int64_t src_blocks;
+  int64_t dst_blocks;
   void *stream;
 };
 

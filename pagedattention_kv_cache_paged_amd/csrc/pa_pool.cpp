@@ -124,8 +124,46 @@ int paged_copy_blocks(void *k_cache, void *v_cache, const int64_t *pairs, int64_
   if (!k_cache || !v_cache || !pairs) return PA_ERR_NULL;
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(pairs, 8))
     return PA_ERR_ALIGN;
-  pa::CopyArgs a{k_cache, v_cache, pairs, num_pairs, run, num_blocks, stream};
+  pa::CopyArgs a{k_cache, v_cache, k_cache, v_cache, pairs, num_pairs, run, num_blocks,
+                 num_blocks, stream};
   return pa::launch_copy_blocks(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int paged_swap_blocks(void *dst_k_cache, void *dst_v_cache, int64_t dst_num_blocks,
+                      const void *src_k_cache, const void *src_v_cache, int64_t src_num_blocks,
+                      const int64_t *pairs, int64_t num_pairs, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t elem_bytes, void *stream) {
+  if (elem_bytes != 1 && elem_bytes != 2) return PA_ERR_DTYPE;
+  if (num_pairs < 0 || num_kv_heads <= 0 || num_kv_heads > 65535 ||
+      (head_dim != 64 && head_dim != 128) ||
+      (block_size != 8 && block_size != 16 && block_size != 32) || dst_num_blocks <= 0 ||
+      src_num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  const int64_t run = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes;
+  if (dst_num_blocks > INT64_MAX / run || src_num_blocks > INT64_MAX / run) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!dst_k_cache || !dst_v_cache || !src_k_cache || !src_v_cache || !pairs) return PA_ERR_NULL;
+  if (!aligned(dst_k_cache, 16) || !aligned(dst_v_cache, 16) || !aligned(src_k_cache, 16) ||
+      !aligned(src_v_cache, 16) || !aligned(pairs, 8))
+    return PA_ERR_ALIGN;
+  pa::CopyArgs a{dst_k_cache, dst_v_cache, src_k_cache, src_v_cache, pairs, num_pairs, run,
+                 src_num_blocks, dst_num_blocks, stream};
+  return pa::launch_copy_blocks(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int paged_validate_swap_pairs(const int64_t *pairs, int64_t num_pairs, int64_t src_num_blocks,
+                              int64_t dst_num_blocks) {
+  if (num_pairs < 0 || src_num_blocks <= 0 || dst_num_blocks <= 0) return PA_ERR_SHAPE;
+  if (num_pairs > 0 && !pairs) return PA_ERR_NULL;
+  std::vector<uint8_t> is_dst((size_t)dst_num_blocks, 0);
+  for (int64_t i = 0; i < num_pairs; ++i) {
+    const int64_t s = pairs[2 * i], d = pairs[2 * i + 1];
+    if (s >= src_num_blocks || d >= dst_num_blocks) return PA_ERR_METADATA;
+    if (s < 0 || d < 0) continue;
+    if (is_dst[(size_t)d]) return PA_ERR_METADATA;
+    is_dst[(size_t)d] = 1;
+  }
+  return PA_OK;
 }
 
 int paged_validate_copy_pairs(const int64_t *pairs, int64_t num_pairs, int64_t num_blocks) {

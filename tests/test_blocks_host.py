@@ -167,3 +167,36 @@ def test_copy_zero_pairs_is_noop():
 ])
 def test_validate_copy_pairs(pairs, code):
     assert B.validate_copy_pairs(np.array(pairs, np.int64).reshape(-1, 2), 10) == code
+
+
+def _swap(**kw):
+    a = dict(dk=FAKE, dv=FAKE, dn=100, sk=FAKE, sv=FAKE, sn=50, pairs=FAKE, n=4, hkv=8, d=128,
+             bs=16, eb=2, stream=None)
+    a.update(kw)
+    return B.load().paged_swap_blocks(a["dk"], a["dv"], a["dn"], a["sk"], a["sv"], a["sn"],
+                                      a["pairs"], a["n"], a["hkv"], a["d"], a["bs"], a["eb"],
+                                      a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(eb=3), -2), (dict(d=32), -3), (dict(bs=64), -3), (dict(dn=0), -3), (dict(sn=-5), -3),
+    (dict(n=-2), -3), (dict(sk=None), -1), (dict(dv=None), -1), (dict(pairs=None), -1),
+    (dict(sv=FAKE + 4), -7), (dict(dk=FAKE + 2), -7), (dict(pairs=FAKE + 2), -7),
+])
+def test_swap_rejects_before_launch(kw, code):
+    assert _swap(**kw) == code
+
+
+def test_swap_zero_pairs_is_noop():
+    assert _swap(n=0, dk=None, dv=None, sk=None, sv=None, pairs=None) == 0
+
+
+@pytest.mark.parametrize("pairs,code", [
+    ([(0, 1), (2, 3), (-1, 5), (4, -1)], 0),
+    ([(0, 1), (0, 2)], 0),                 # one device block to two host slots
+    ([(0, 1), (1, 0)], 0),                 # distinct pools: a source may share an id with a dst
+    ([(0, 1), (2, 1)], -6),
+    ([(0, 20)], -6), ([(10, 0)], -6),      # past the destination / source pool
+])
+def test_validate_swap_pairs(pairs, code):
+    assert B.validate_swap_pairs(np.array(pairs, np.int64).reshape(-1, 2), 10, 20) == code

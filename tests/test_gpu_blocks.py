@@ -148,3 +148,84 @@ def test_cow_flow_on_device(bs):
     ref = oracle.decode(q, pkc, pvc, pbt, lens, 0.125, bs, W.BF16)
     got = out.float().cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - ref) <= 2e-3 + 1e-2 * np.abs(ref))
+
+
+# ---- swap between the device caches and a pinned host pool ---------------------
+
+def pinned(a):
+    t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+    return t.pin_memory()
+
+
+@pytest.mark.parametrize("itemsize", [2, 1])
+@pytest.mark.parametrize("hkv,bs,d", [(2, 16, 128), (8, 8, 64), (1, 32, 128)])
+def test_swap_out_and_in_bit_exact(itemsize, hkv, bs, d):
+    g = np.random.default_rng(800 + hkv + bs + d + itemsize)
+    nd, nh = 96, 40
+    dk, dv = rand_caches(g, nd, hkv, bs, d, itemsize)
+    hk, hv = rand_caches(g, nh, hkv, bs, d, itemsize)
+    dkt, dvt = to_dev(dk), to_dev(dv)
+    hkt, hvt = pinned(hk), pinned(hv)
+    ids = g.permutation(nd)
+    out_pairs = np.stack([ids[:30], g.permutation(nh)[:30]], 1)
+    out_pairs = np.concatenate([out_pairs, [[-1, 35], [3, -1], [nd + 1, 36]]])
+    say(f"swap out hkv={hkv} bs={bs} d={d} itemsize={itemsize}")
+    B.paged_swap_blocks(torch.from_numpy(out_pairs).to(DEV), hkt, hvt, dkt, dvt)
+    torch.cuda.synchronize()
+    ek, ev = hk.copy(), hv.copy()
+    ok_pairs = [(s, t) for s, t in out_pairs if 0 <= s < nd and 0 <= t < nh]
+    oracle.swap_blocks(np.array(ok_pairs), ek, ev, dk, dv, bs)
+    assert np.array_equal(to_host(hkt, hk), ek) and np.array_equal(to_host(hvt, hv), ev)
+    in_pairs = np.stack([np.arange(nh), ids[40:40 + nh]], 1)          # pairs in pinned memory
+    say("swap in")
+    B.paged_swap_blocks(torch.from_numpy(in_pairs).pin_memory(), dkt, dvt, hkt, hvt,
+                        stream_device=torch.device(DEV))
+    torch.cuda.synchronize()
+    fk, fv = dk.copy(), dv.copy()
+    oracle.swap_blocks(in_pairs, fk, fv, ek, ev, bs)
+    assert np.array_equal(to_host(dkt, dk), fk) and np.array_equal(to_host(dvt, dv), fv)
+
+
+def test_preempt_and_resume_on_device():
+    """Swap a sequence out to pinned host memory, overwrite its device
+    blocks, swap it back into other blocks and rewrite its table: decode is
+    bit-identical to the decode before preemption."""
+    w = W.build("swapg", [300, 77, 512, 1000], num_heads=16, num_kv_heads=2, head_dim=128,
+                block_size=16, dtype=W.BF16, seed=13, pool=200, max_blocks_per_seq=70)
+    ksh, vsh = w.cache_shapes()
+    kc = torch.zeros(ksh, dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros(vsh, dtype=torch.bfloat16, device=DEV)
+    for which in ("hist", "new"):
+        k, v, s = w.write_batch(which)
+        B.paged_kv_write(torch.from_numpy(k.view(np.int16)).to(DEV).view(torch.bfloat16),
+                         torch.from_numpy(v.view(np.int16)).to(DEV).view(torch.bfloat16),
+                         torch.from_numpy(s).to(DEV), kc, vc)
+    q = torch.from_numpy(w.q.view(np.int16)).to(DEV).view(torch.bfloat16)
+    cl = torch.from_numpy(w.context_lens).to(DEV)
+
+    def decode(bt):
+        out = torch.empty_like(q)
+        B.paged_attention_decode(out, q, kc, vc, torch.from_numpy(bt).to(DEV), cl, w.scale,
+                                 16, 2)
+        torch.cuda.synchronize()
+        return out.view(torch.int16).cpu().numpy()
+
+    before = decode(w.block_tables)
+    seq = 3
+    used = int(np.ceil(w.context_lens[seq] / 16))
+    blocks = w.block_tables[seq, :used].copy()
+    hk = torch.empty((used,) + ksh[1:], dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty((used,) + vsh[1:], dtype=torch.bfloat16).pin_memory()
+    say(f"preempt seq {seq}: {used} blocks out")
+    B.paged_swap_blocks(torch.from_numpy(np.stack([blocks, np.arange(used)], 1)).to(DEV),
+                        hk, hv, kc, vc)
+    kc[torch.from_numpy(blocks).to(DEV)] = float("nan")   # the blocks are reused meanwhile
+    vc[torch.from_numpy(blocks).to(DEV)] = float("nan")
+    in_use = set(w.block_tables.ravel().tolist())
+    fresh = np.array([b for b in range(200) if b not in in_use][:used])
+    B.paged_swap_blocks(torch.from_numpy(np.stack([np.arange(used), fresh], 1)).to(DEV),
+                        kc, vc, hk, hv)
+    bt = w.block_tables.copy()
+    bt[seq, :used] = fresh
+    after = decode(bt)
+    assert np.array_equal(before, after)

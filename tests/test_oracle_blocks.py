@@ -8,6 +8,9 @@ things other than itself (no GPU):
 * skipped pairs (negative ids) and refused pairs (repeated destination, a
   destination that is also a source, an id past the pool) leave the caches
   untouched;
+* swap (block moves between a device pool and a host pool): against numpy
+  slices both ways, refused pairs, and a preempt/resume round trip whose
+  decode is bit-identical to the one before preemption;
 * copy-on-write end to end: sequences forked from a prompt whose last block
   is only partly filled share every prompt block; each fork's first append
   copies the shared partial block (a reference model of the decision in the
@@ -155,3 +158,66 @@ def test_cow_fork_equals_private_copies(bs):
     pk, pv, pbt = private_layout(logical, bs, hkv, d)
     ref = oracle.decode(q, pk, pv, pbt, lens, 0.125, bs, W.BF16)
     assert np.array_equal(got, ref)
+
+
+# ---- swap between two pools ---------------------------------------------------
+
+@pytest.mark.parametrize("itemsize", [2, 1])
+def test_swap_equals_block_slices(itemsize):
+    g = np.random.default_rng(70 + itemsize)
+    dk, dv = rand_caches(g, 50, 2, 16, 64, itemsize)   # device pool
+    hk, hv = rand_caches(g, 20, 2, 16, 64, itemsize)   # host pool
+    hk0, hv0 = hk.copy(), hv.copy()
+    out_pairs = np.array([(5, 0), (17, 3), (49, 19), (-1, 4), (6, -1)])
+    oracle.swap_blocks(out_pairs, hk, hv, dk, dv, 16)          # swap-out: device -> host
+    ek, ev = hk0.copy(), hv0.copy()
+    for s_, d_ in out_pairs:
+        if s_ >= 0 and d_ >= 0:
+            ek[d_], ev[d_] = dk[s_], dv[s_]
+    assert np.array_equal(hk, ek) and np.array_equal(hv, ev)
+    dk0, dv0 = dk.copy(), dv.copy()
+    in_pairs = np.array([(0, 30), (3, 31), (19, 32)])
+    oracle.swap_blocks(in_pairs, dk, dv, hk, hv, 16)           # swap-in: host -> device
+    for (s_, _), (_, d_) in zip(out_pairs[:3], in_pairs):
+        assert np.array_equal(dk[d_], dk0[s_]) and np.array_equal(dv[d_], dv0[s_])
+    untouched = [b for b in range(50) if b not in (30, 31, 32)]
+    assert np.array_equal(dk[untouched], dk0[untouched])
+
+
+@pytest.mark.parametrize("pairs", [[(1, 2), (3, 2)], [(1, 20)], [(50, 1)]])
+def test_swap_refuses_bad_pairs(pairs):
+    g = np.random.default_rng(8)
+    dk, dv = rand_caches(g, 50, 2, 16, 64, 2)
+    hk, hv = rand_caches(g, 20, 2, 16, 64, 2)
+    hk0 = hk.copy()
+    with pytest.raises(oracle.OracleError):
+        oracle.swap_blocks(np.array(pairs), hk, hv, dk, dv, 16)
+    assert np.array_equal(hk, hk0)
+
+
+def test_preempt_and_resume_decodes_the_same():
+    """Swap a sequence's blocks out, reuse its device blocks for other data,
+    swap it back into different blocks and point its table there: the
+    oracle's decode is bit-identical to the one before preemption."""
+    w = W.build("swap", [300, 77, 512], num_heads=8, num_kv_heads=2, head_dim=64,
+                block_size=16, dtype=W.BF16, seed=12, pool=80, max_blocks_per_seq=40)
+    kc, vc = w.nan_caches()
+    for which in ("hist", "new"):
+        k, v, s = w.write_batch(which)
+        oracle.kv_write(k, v, s, kc, vc, 16)
+    before = oracle.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, 16, w.dtype)
+    seq = 0
+    used = int(np.ceil(w.context_lens[seq] / 16))
+    blocks = w.block_tables[seq, :used].copy()
+    hk = np.zeros((used, 2, 16, 64), np.uint16)
+    hv = np.zeros((used, 2, 64, 16), np.uint16)
+    oracle.swap_blocks(np.stack([blocks, np.arange(used)], 1), hk, hv, kc, vc, 16)
+    kc[blocks] = 0x7FC0                      # the freed blocks now hold something else
+    vc[blocks] = 0x7FC0
+    in_use = set(w.block_tables[:, :40].ravel().tolist())
+    fresh = np.array([b for b in range(80) if b not in in_use][:used])
+    oracle.swap_blocks(np.stack([np.arange(used), fresh], 1), kc, vc, hk, hv, 16)
+    bt = w.block_tables.copy()
+    bt[seq, :used] = fresh
+    after = oracle.decode(w.q, kc, vc, bt, w.context_lens, w.scale, 16, w.dtype)
+    assert np.array_equal(before, after)

@@ -72,6 +72,9 @@ MUTANTS = [
     ("copy_reversed", "memcpy(kc + kd * elem_bytes, kc + ks * elem_bytes, (size_t)elem_bytes);",
      "memcpy(kc + ks * elem_bytes, kc + kd * elem_bytes, (size_t)elem_bytes);"),
     ("copy_accepts_dst_as_src", "    if (role[b] == 3) {", "    if (role[b] == 7) {"),
+    ("swap_reads_destination", "memcpy(dk + kd * elem_bytes, sk + ks * elem_bytes, (size_t)elem_bytes);",
+     "memcpy(dk + kd * elem_bytes, sk + kd * elem_bytes, (size_t)elem_bytes);"),
+    ("swap_v_skipped", "memcpy(dv + vd * elem_bytes, sv + vs * elem_bytes, (size_t)elem_bytes);", ""),
 ]
 # the consistent V-layout mutant also moves the write to token-major order
 EXTRA = {
