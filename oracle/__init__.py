@@ -104,6 +104,9 @@ def _load():
     lib.oracle_copy_blocks.restype = i32
     lib.oracle_swap_blocks.argtypes = [p, p, i64, p, p, i64, p, i64, i32, i32, i32, i32]
     lib.oracle_swap_blocks.restype = i32
+    lib.oracle_prefill.argtypes = [p, p, p, p, p, p, p, dbl, i32, i32, i32, i32, i32, i32, i64,
+                                   i32]
+    lib.oracle_prefill.restype = i32
     _lib = lib
     return lib
 
@@ -316,3 +319,24 @@ def swap_blocks(pairs, dst_k, dst_v, src_k, src_v, block_size: int) -> None:
                                     _ptr(pairs), pairs.shape[0], hkv, d, bs,
                                     dst_k.dtype.itemsize)
     _check(rc, "oracle_swap_blocks")
+
+
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+            block_size: int, dtype) -> np.ndarray:
+    """Chunked-prefill attention: q [total_q, Hq, D] bits, rows
+    query_start[s] .. query_start[s+1]-1 are sequence s's last positions
+    L-n .. L-1, each attending causally over positions 0 .. its own.
+    Returns float64 [total_q, Hq, D]."""
+    q = _u16(q)
+    k_cache, v_cache = _u16(k_cache), _u16(v_cache)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    total, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    assert bs == block_size and qs.size == cl.size + 1 and qs[-1] == total
+    out = np.zeros((total, hq, d), dtype=np.float64)
+    _check(_load().oracle_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt),
+                                  _ptr(cl), _ptr(qs), float(scale), bs, hkv, cl.size, hq, d,
+                                  bt.shape[1], nb, dtype_code(dtype)), "oracle_prefill")
+    return out

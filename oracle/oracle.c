@@ -648,3 +648,80 @@ int oracle_swap_blocks(void *dst_k, void *dst_v, int64_t dst_num_blocks, const v
   }
   return ORACLE_OK;
 }
+
+/* ---- paged prefill (chunked prefill) ------------------------------------------ */
+
+/* [P1] 4.3 (a long prompt is split into chunks so that its prefill does not
+ * hold up decoding) and [P4] 4.2 (chunked prefill, a prefill chunk size):
+ * each chunk's tokens attend over the sequence's cached KV and, causally,
+ * over the chunk itself.  Sequence s contributes n_s = query_start[s+1] -
+ * query_start[s] query rows (rows query_start[s] .. query_start[s+1]-1 of q
+ * and out, layout [row][num_heads][head_dim]); they are its context
+ * positions L-n_s .. L-1, where L = context_lens[s] counts the chunk too, so
+ * their K and V are in the caches already (appended before the call).  Row
+ * i of the chunk (position p = L-n_s+i), query head h:
+ *     x[t]   = scale * sum_d q[i,h,d] * K[t,d]        for t = 0 .. p
+ *     out[d] = sum_t exp(x[t] - max x) V[t,d] / sum_t exp(x[t] - max x)
+ * reaching token t through block_tables[s][t / bs] at offset t % bs, with
+ * KV head h / (num_heads / num_kv_heads).  n_s > L is an error
+ * (ORACLE_ELEN); n_s = 0 contributes nothing.  16-bit caches only. */
+int oracle_prefill(double *out, const uint16_t *q, const uint16_t *k_cache,
+                   const uint16_t *v_cache, const int32_t *block_tables,
+                   const int32_t *context_lens, const int32_t *query_start, double scale,
+                   int block_size, int num_kv_heads, int num_seqs, int num_heads, int head_dim,
+                   int max_blocks_per_seq, int64_t num_blocks, int dtype) {
+  if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || num_seqs < 0 ||
+      block_size <= 0 || head_dim <= 0 || (dtype != ORACLE_F16 && dtype != ORACLE_BF16))
+    return ORACLE_EARG;
+  int group = num_heads / num_kv_heads;
+  for (int s = 0; s < num_seqs; ++s) {
+    int64_t row0 = query_start[s], n = (int64_t)query_start[s + 1] - query_start[s];
+    int64_t len = context_lens[s];
+    if (n < 0) return ORACLE_EARG;
+    if (n == 0) continue;
+    if (n > len || len > (int64_t)max_blocks_per_seq * block_size) return ORACLE_ELEN;
+    const int32_t *table = block_tables + (int64_t)s * max_blocks_per_seq;
+    for (int64_t t = 0; t < len; ++t)
+      if (table[t / block_size] < 0 || table[t / block_size] >= num_blocks) return ORACLE_EBLOCK;
+    double *x = malloc((size_t)len * sizeof(double));
+    if (!x) return ORACLE_ENOMEM;
+    for (int64_t i = 0; i < n; ++i) {
+      int64_t p = len - n + i; /* the row's own position: it sees tokens 0 .. p */
+      for (int h = 0; h < num_heads; ++h) {
+        int kv_head = h / group;
+        const uint16_t *qrow = q + ((row0 + i) * num_heads + h) * (int64_t)head_dim;
+        double *orow = out + ((row0 + i) * num_heads + h) * (int64_t)head_dim;
+        for (int64_t t = 0; t <= p; ++t) {
+          int64_t block = table[t / block_size];
+          int64_t krow = ((block * num_kv_heads + kv_head) * (int64_t)block_size +
+                          (int)(t % block_size)) * head_dim;
+          double dot = 0.0;
+          for (int d = 0; d < head_dim; ++d)
+            dot += decode(qrow[d], dtype) * decode(k_cache[krow + d], dtype);
+          x[t] = scale * dot;
+        }
+        double m = x[0];
+        for (int64_t t = 1; t <= p; ++t)
+          if (x[t] > m) m = x[t];
+        double z = 0.0;
+        for (int64_t t = 0; t <= p; ++t) {
+          x[t] = exp(x[t] - m);
+          z += x[t];
+        }
+        for (int d = 0; d < head_dim; ++d) orow[d] = 0.0;
+        for (int64_t t = 0; t <= p; ++t) {
+          int64_t block = table[t / block_size];
+          int offset = (int)(t % block_size);
+          for (int d = 0; d < head_dim; ++d) {
+            int64_t vi = ((block * num_kv_heads + kv_head) * (int64_t)head_dim + d) *
+                             block_size + offset;
+            orow[d] += x[t] * decode(v_cache[vi], dtype);
+          }
+        }
+        for (int d = 0; d < head_dim; ++d) orow[d] /= z;
+      }
+    }
+    free(x);
+  }
+  return ORACLE_OK;
+}

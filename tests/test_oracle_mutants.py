@@ -3,8 +3,8 @@
 Each case plants one mistake in a copy of oracle/oracle.c (a dropped term, a
 wrong sign, index or layout, a transposed operand), builds it on the CPU into
 a temporary library and runs tests/test_oracle_pins.py,
-tests/test_oracle_fp8.py and tests/test_oracle_blocks.py against that
-library in a subprocess.  The pin suite must fail for every mutant and pass for the
+tests/test_oracle_fp8.py, tests/test_oracle_blocks.py and
+tests/test_oracle_prefill.py against that library in a subprocess.  The pin suite must fail for every mutant and pass for the
 unmodified copy.
 """
 import concurrent.futures as cf
@@ -19,7 +19,8 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = [os.path.join(ROOT, "tests", "test_oracle_pins.py"),
         os.path.join(ROOT, "tests", "test_oracle_fp8.py"),
-        os.path.join(ROOT, "tests", "test_oracle_blocks.py")]
+        os.path.join(ROOT, "tests", "test_oracle_blocks.py"),
+        os.path.join(ROOT, "tests", "test_oracle_prefill.py")]
 
 # (name, original text, planted text) -- the first occurrence is replaced
 MUTANTS = [
@@ -75,6 +76,14 @@ MUTANTS = [
     ("swap_reads_destination", "memcpy(dk + kd * elem_bytes, sk + ks * elem_bytes, (size_t)elem_bytes);",
      "memcpy(dk + kd * elem_bytes, sk + kd * elem_bytes, (size_t)elem_bytes);"),
     ("swap_v_skipped", "memcpy(dv + vd * elem_bytes, sv + vs * elem_bytes, (size_t)elem_bytes);", ""),
+    ("prefill_sees_own_position_not", "int64_t p = len - n + i; /* the row's own position",
+     "int64_t p = len - n + i - (i > 0); /* the row's own position"),
+    ("prefill_position_from_chunk_start", "int64_t p = len - n + i; /* the row's own position",
+     "int64_t p = (len - n + i) % (n + 1); /* the row's own position"),
+    ("prefill_gqa_modulo", "int kv_head = h / group;\n        const uint16_t *qrow = q + ((row0",
+     "int kv_head = h % num_kv_heads;\n        const uint16_t *qrow = q + ((row0"),
+    ("prefill_sees_next_token", "int64_t p = len - n + i; /* the row's own position",
+     "int64_t p = len - n + i + (i + 1 < n); /* the row's own position"),
 ]
 # the consistent V-layout mutant also moves the write to token-major order
 EXTRA = {

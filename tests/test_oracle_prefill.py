@@ -1,0 +1,156 @@
+"""Pins of the oracle's chunked prefill ("vLLM core architecture overview",
+4.3; "vLLM framework analysis: how PagedAttention achieves a 20x LLM
+inference speed-up", 4.2) against things other than itself (no GPU):
+
+* torch's scaled_dot_product_attention in fp64 on the logical K and V of
+  each sequence (gathered through the harness's own block tables), causal
+  for a whole prompt and with an explicit mask (row i sees positions up to
+  C + i) for a chunk after C cached tokens; GQA by repeat_interleave;
+* numpy brute force on tiny shapes;
+* chunking invariance: a prompt prefilled in one call or in several chunks
+  (each call with its own context length) gives the same rows, bit for bit;
+* a one-token chunk equals oracle_decode for that position, bit for bit;
+* causality: NaN written into every position after a row's own leaves that
+  row unchanged.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from pagedattention_kv_cache_paged_amd import workloads as W
+
+
+def f64(bits, dtype):
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dtype == W.F16:
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def setup(lengths, chunks, hq, hkv, d, bs, dtype, seed):
+    """A paged layout of `lengths` tokens per sequence (all in the caches)
+    and chunk queries: the last chunks[s] positions of sequence s."""
+    w = W.build("pf", lengths, num_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                dtype=dtype, seed=seed)
+    kc, vc = w.nan_caches()
+    for which in ("hist", "new"):
+        k, v, s = w.write_batch(which)
+        oracle.kv_write(k, v, s, kc, vc, bs)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    g = np.random.default_rng(seed + 1)
+    q = W.normal_bits(g, (int(qs[-1]), hq, d), dtype)
+    return w, kc, vc, q, qs
+
+
+def sdpa_ref(w, q, qs, chunks):
+    out = np.zeros(q.shape, np.float64)
+    G = w.num_heads // w.num_kv_heads
+    for s in range(w.num_seqs):
+        n = chunks[s]
+        if n == 0:
+            continue
+        L = int(w.context_lens[s])
+        K, V = w.seq_kv(s)
+        k = torch.from_numpy(f64(K, w.dtype)).permute(1, 0, 2).repeat_interleave(G, 0)
+        v = torch.from_numpy(f64(V, w.dtype)).permute(1, 0, 2).repeat_interleave(G, 0)
+        qq = torch.from_numpy(f64(q[qs[s]:qs[s] + n], w.dtype)).permute(1, 0, 2)
+        pos = np.arange(L - n, L)
+        mask = torch.from_numpy(np.arange(L)[None, :] <= pos[:, None])
+        o = torch.nn.functional.scaled_dot_product_attention(qq, k, v, attn_mask=mask,
+                                                             scale=w.scale)
+        out[qs[s]:qs[s] + n] = o.permute(1, 0, 2).numpy()
+    return out
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_whole_prompt_equals_causal_sdpa(bs):
+    lengths = [1, 17, 64, 150]
+    w, kc, vc, q, qs = setup(lengths, lengths, 8, 2, 64, bs, W.BF16, 10 + bs)
+    got = oracle.prefill(q, kc, vc, w.block_tables, w.context_lens, qs, w.scale, bs, w.dtype)
+    # whole prompts: torch's own causal flag as an independent second check
+    G = 4
+    for s, L in enumerate(lengths):
+        K, V = w.seq_kv(s)
+        k = torch.from_numpy(f64(K, w.dtype)).permute(1, 0, 2).repeat_interleave(G, 0)
+        v = torch.from_numpy(f64(V, w.dtype)).permute(1, 0, 2).repeat_interleave(G, 0)
+        qq = torch.from_numpy(f64(q[qs[s]:qs[s + 1]], w.dtype)).permute(1, 0, 2)
+        o = torch.nn.functional.scaled_dot_product_attention(qq, k, v, is_causal=True,
+                                                             scale=w.scale)
+        assert np.allclose(got[qs[s]:qs[s + 1]], o.permute(1, 0, 2).numpy(), rtol=1e-12,
+                           atol=1e-13)
+
+
+@pytest.mark.parametrize("G,d,dtype", [(1, 64, W.F16), (4, 128, W.BF16), (3, 64, W.BF16)])
+def test_chunk_after_cached_prefix_equals_masked_sdpa(G, d, dtype):
+    lengths = [40, 200, 33, 97, 16]
+    chunks = [5, 64, 33, 1, 0]
+    w, kc, vc, q, qs = setup(lengths, chunks, 2 * G, 2, d, 16, dtype, 33 + G)
+    got = oracle.prefill(q, kc, vc, w.block_tables, w.context_lens, qs, w.scale, 16, dtype)
+    ref = sdpa_ref(w, q, qs, chunks)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_brute_force_tiny():
+    lengths, chunks = [6, 9], [3, 9]
+    w, kc, vc, q, qs = setup(lengths, chunks, 2, 1, 64, 8, W.F16, 3)
+    got = oracle.prefill(q, kc, vc, w.block_tables, w.context_lens, qs, w.scale, 8, W.F16)
+    for s in range(2):
+        K, V = w.seq_kv(s)
+        K, V = f64(K, W.F16)[:, 0], f64(V, W.F16)[:, 0]
+        L, n = lengths[s], chunks[s]
+        for i in range(n):
+            p = L - n + i
+            for h in range(2):
+                qv = f64(q[qs[s] + i, h], W.F16)
+                x = np.array([w.scale * np.dot(qv, K[t]) for t in range(p + 1)])
+                e = np.exp(x - x.max())
+                ref = (e[:, None] * V[:p + 1]).sum(0) / e.sum()
+                assert np.allclose(got[qs[s] + i, h], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_chunking_invariance():
+    """One call over the whole prompt, or three calls over consecutive
+    chunks, each seeing the context written so far: identical rows."""
+    L = 200
+    w, kc, vc, q, qs = setup([L], [L], 4, 2, 64, 16, W.BF16, 51)
+    whole = oracle.prefill(q, kc, vc, w.block_tables, w.context_lens, qs, w.scale, 16, w.dtype)
+    parts = []
+    start = 0
+    for n in (70, 64, 66):
+        end = start + n
+        parts.append(oracle.prefill(q[start:end], kc, vc, w.block_tables,
+                                    np.array([end], np.int32), np.array([0, n], np.int32),
+                                    w.scale, 16, w.dtype))
+        start = end
+    assert np.array_equal(np.concatenate(parts), whole)
+
+
+def test_one_token_chunk_equals_decode():
+    lengths = [1, 17, 300, 64]
+    w, kc, vc, q, qs = setup(lengths, [1, 1, 1, 1], 8, 2, 128, 16, W.BF16, 61)
+    got = oracle.prefill(q, kc, vc, w.block_tables, w.context_lens, qs, w.scale, 16, w.dtype)
+    ref = oracle.decode(q, kc, vc, w.block_tables, w.context_lens, w.scale, 16, w.dtype)
+    assert np.array_equal(got, ref)
+
+
+def test_causality_ignores_later_positions():
+    L = 90
+    w, kc, vc, q, qs = setup([L], [L], 4, 2, 64, 16, W.BF16, 71)
+    full = oracle.prefill(q, kc, vc, w.block_tables, w.context_lens, qs, w.scale, 16, w.dtype)
+    for p in (0, 15, 16, 47, 88):
+        k2, v2 = kc.copy(), vc.copy()
+        for t in range(p + 1, L):
+            b, o = w.block_tables[0, t // 16], t % 16
+            k2[b, :, o, :] = W.NAN_BITS[W.BF16]
+            v2[b, :, :, o] = W.NAN_BITS[W.BF16]
+        got = oracle.prefill(q[p:p + 1], k2, v2, w.block_tables, np.array([p + 1], np.int32),
+                             np.array([0, 1], np.int32), w.scale, 16, w.dtype)
+        assert np.array_equal(got[0], full[p])
+
+
+def test_refuses_chunk_longer_than_context():
+    w, kc, vc, q, qs = setup([10], [10], 2, 1, 64, 16, W.F16, 80)
+    with pytest.raises(oracle.OracleError):
+        oracle.prefill(q, kc, vc, w.block_tables, np.array([9], np.int32), qs, w.scale, 16,
+                       w.dtype)
