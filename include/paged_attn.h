@@ -239,6 +239,31 @@ int paged_attention_decode_append(void *out, const void *q, const void *k_new,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Paged (chunked) prefill attention ("vLLM core architecture overview"
+ * (5688vip.com), 4.3, and "vLLM framework analysis: how PagedAttention
+ * achieves a 20x LLM inference speed-up" (intelliparadigm.com), 4.2: a long
+ * prompt is processed in chunks).  Sequence s contributes the query rows
+ * query_start[s] .. query_start[s+1]-1 of q and out ([total_rows, num_heads,
+ * head_dim], dtype): its last n_s context positions L-n_s .. L-1, with
+ * L = context_lens[s] counting the chunk, whose K/V are already in the caches
+ * (appended with paged_kv_write).  Row i (position p = L-n_s+i), query head h:
+ *   out[i,h] = softmax(scale * q[i,h] K[0..p]^T) V[0..p]
+ * over KV head h / (num_heads / num_kv_heads), reached through the block
+ * table as in paged_attention_decode (same cache layouts, 16-bit caches).
+ * query_start: device int32 [num_seqs + 1], non-decreasing from 0.
+ * max_query_len: host bound on every n_s (it sizes the grid; rows of a
+ * longer chunk are not computed); 0 is a no-op.  A sequence with n_s > L
+ * gets no rows written.  No workspace; out rows of the chunks are the only
+ * writes.  Asynchronous on `stream`.
+ */
+int paged_attention_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            const int32_t *query_start, float scale, int32_t block_size,
+                            int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                            int32_t head_dim, int32_t max_blocks_per_seq, int64_t num_blocks,
+                            int32_t dtype, int32_t max_query_len, void *stream);
+
+/*
  * Host-side check of metadata (host pointers): every context length in
  * [0, max_blocks_per_seq * block_size]; every table entry a sequence reads,
  * i.e. the first ceil(L / block_size) of its row, in [0, num_blocks); every

@@ -80,6 +80,9 @@ def load() -> ctypes.CDLL:
     lib.paged_attention_decode_append.argtypes = [p, p, p, p, p, p, p, p, f32, f32, f32, i32,
                                                   i32, i32, i32, i32, i32, i64, i32, i32, i32,
                                                   p, sz, p]
+    lib.paged_attention_prefill.restype = ctypes.c_int
+    lib.paged_attention_prefill.argtypes = [p, p, p, p, p, p, p, f32, i32, i32, i32, i32, i32,
+                                            i32, i64, i32, i32, p]
     lib.pa_pool_create.restype = ctypes.c_int
     lib.pa_pool_create.argtypes = [i64, p, ctypes.POINTER(p)]
     lib.pa_pool_destroy.restype = None
@@ -484,3 +487,41 @@ def validate_swap_pairs(pairs, src_num_blocks: int, dst_num_blocks: int) -> int:
     pr = np.ascontiguousarray(np.asarray(pairs), dtype=np.int64).reshape(-1, 2)
     return int(load().paged_validate_swap_pairs(pr.ctypes.data, pr.shape[0], src_num_blocks,
                                                 dst_num_blocks))
+
+
+# ---- paged (chunked) prefill -------------------------------------------------
+
+def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor, block_tables: torch.Tensor,
+                            context_lens: torch.Tensor, query_start: torch.Tensor,
+                            scale: float, block_size: int, num_kv_heads: int,
+                            max_query_len: int) -> torch.Tensor:
+    """Rows query_start[s] .. query_start[s+1]-1 of q / out ([rows, Hq, D])
+    are sequence s's last positions; each attends causally over the paged
+    context up to its own position.  Returns out."""
+    dev = _dev(out, q, k_cache, v_cache, block_tables, context_lens, query_start)
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be [rows, num_heads, head_dim]")
+    rows, hq, d = q.shape
+    B = context_lens.shape[0]
+    if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (num_kv_heads, block_size, d):
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    nb = k_cache.shape[0]
+    if tuple(v_cache.shape) != (nb, num_kv_heads, d, block_size):
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [num_seqs, max_blocks_per_seq]")
+    if context_lens.dtype != torch.int32 or context_lens.dim() != 1:
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    if query_start.dtype != torch.int32 or tuple(query_start.shape) != (B + 1,):
+        raise ValueError("query_start must be int32 [num_seqs + 1]")
+    dt = _dtype(q)
+    if out.dtype != q.dtype or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q, out and the caches must share one dtype")
+    rc = load().paged_attention_prefill(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(), float(scale),
+        block_size, num_kv_heads, B, hq, d, block_tables.shape[1], nb, dt, int(max_query_len),
+        _stream(dev))
+    _check("paged_attention_prefill", rc)
+    return out

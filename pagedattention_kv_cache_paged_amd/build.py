@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libpaged_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["pa_api.cpp", "pa_pool.cpp", "pa_write.hip", "pa_decode.hip", "pa_blocks.hip"]
+SOURCES = ["pa_api.cpp", "pa_pool.cpp", "pa_write.hip", "pa_decode.hip", "pa_blocks.hip",
+           "pa_prefill.hip"]
 ARCH = "gfx950"
 
 

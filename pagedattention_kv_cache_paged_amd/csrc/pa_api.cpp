@@ -260,6 +260,30 @@ int paged_attention_decode(void *out, const void *q, const void *k_cache, const 
                                    workspace_bytes, stream);
 }
 
+int paged_attention_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            const int32_t *query_start, float scale, int32_t block_size,
+                            int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                            int32_t head_dim, int32_t max_blocks_per_seq, int64_t num_blocks,
+                            int32_t dtype, int32_t max_query_len, void *stream) {
+  if (dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (!decode_sizes_ok(num_seqs, num_kv_heads, num_heads, head_dim, max_blocks_per_seq,
+                       block_size) ||
+      num_blocks <= 0 || num_blocks > INT32_MAX || !std::isfinite(scale) || max_query_len < 0 ||
+      (int64_t)max_query_len > (int64_t)max_blocks_per_seq * block_size)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 8) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
+    return PA_ERR_ALIGN;
+  pa::PrefillArgs a{out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                    block_size, num_kv_heads, num_seqs, num_heads, head_dim,
+                    max_blocks_per_seq, num_blocks, dtype, max_query_len, stream};
+  return pa::launch_prefill(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
 int paged_validate_metadata(const int32_t *block_tables, const int32_t *context_lens,
                             int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
                             int64_t num_blocks, const int64_t *slot_mapping, int64_t num_tokens) {

@@ -83,9 +83,31 @@ struct CopyArgs {
   void *stream;
 };
 
+struct PrefillArgs {
+  void *out;
+  const void *q;
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  const int32_t *query_start;  // [num_seqs + 1] chunk row offsets
+  float scale;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t max_blocks_per_seq;
+  int64_t num_blocks;
+  int32_t dtype;
+  int32_t max_query_len;        // bound on any sequence's chunk length (grid size)
+  void *stream;
+};
+
 // Return 0 on success, a nonzero HIP error code otherwise.
 int launch_decode(const DecodeArgs &a);
 int launch_kv_write(const WriteArgs &a);
 int launch_copy_blocks(const CopyArgs &a);
+int launch_prefill(const PrefillArgs &a);
 
 }  // namespace pa

@@ -1,0 +1,397 @@
+// Paged (chunked) prefill attention for gfx950.
+//
+// "vLLM core architecture overview" (5688vip.com), 4.3, and "vLLM framework
+// analysis: how PagedAttention achieves a 20x LLM inference speed-up"
+// (intelliparadigm.com), 4.2: a long prompt is processed in chunks.  Each
+// chunk token (context position p) attends over positions 0 .. p of its
+// sequence, reached through the block table as in decode ("vLLM memory
+// management and continuous batching from the source", part 2, 2.3); the
+// chunk's own K/V are already in the caches (appended before the call).
+//
+// Unlike decode this is a dense contraction: every K/V tile meets many query
+// rows, so the bound is the MFMA rate, not HBM.  Work split:
+//   workgroup = (64 query tokens of one sequence) x (up to HC query heads of
+//   one KV head); four waves, each 16 tokens x HC heads (16*HC query rows).
+//   The workgroup walks the keys 0 .. its last position in tiles of 32: K
+//   and V tiles go through double-buffered LDS (each of the 256 lanes moves
+//   four 16-byte pieces), so a tile is read from memory once per 64*HC rows.
+//   Workgroups run heaviest-first (last query block first) and the blocks of
+//   one (sequence, KV head) land on one XCD, sharing its L2.
+// Per wave and 32-key tile, with q held in registers as the B operand:
+//   S^T[32 keys x 16 tokens] per head = K[keys x D] q^T  (16x16x32 MFMAs,
+//     A = K rows from LDS), so lane (token l%16, quarter l/16) holds the
+//     scores of keys 4*(l/16)+r and 16+4*(l/16)+r;
+//   O^T[D x 16 tokens] += V^T[D x 32 keys] P^T  (16x16x32 MFMAs over the 32
+//     keys, A = the dim-major V tile from LDS, B = P in the registers the QK
+//     MFMA wrote: the k index of both operands runs over the same eight keys
+//     per lane, so no shuffle is needed).
+// Online softmax per (head, token) with a lazily raised reference max, as in
+// decode; bfloat16 weights enter P.V as hi + lo parts (binary16 ones as
+// they are); the causal mask runs only on tiles that reach past a wave's
+// first position.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kQT = 16;          // query tokens per wave
+constexpr int kWaves = 4;        // waves per workgroup
+constexpr int kQB = kQT * kWaves;  // query tokens per workgroup
+constexpr int kKT = 32;          // keys per tile
+constexpr int kThreads = kWaves * kWave;
+
+template <int DT>
+struct PElem;
+// kSplitP: bfloat16 weights go in as a hi and a lo part (two MFMAs), so P
+// keeps about 16 significant bits; binary16 weights already carry 11.
+template <>
+struct PElem<1> {
+  static constexpr bool kSplitP = true;
+  static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  }
+};
+template <>
+struct PElem<0> {
+  static constexpr bool kSplitP = false;
+  static __device__ __forceinline__ float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(f16x2, w)[0];
+  }
+  static __device__ __forceinline__ float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(f16x2, w)[1];
+  }
+  static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+  }
+};
+
+__device__ __forceinline__ float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// LDS tile layouts (16-bit elements), rows padded by 16 bytes so that the
+// 16 rows one MFMA operand reads fall in different banks:
+//   K tile [32 keys][D + 8]  (token-major, as in the cache)
+//   V tile [D][32 + 8]       (dim-major, as in the cache)
+template <int D>
+struct Tile {
+  static constexpr int kRow = D + 8;        // K row, in elements
+  static constexpr int vRow = kKT + 8;      // V row, in elements
+  static constexpr int kElems = kKT * kRow;
+  static constexpr int vElems = D * vRow;
+  static constexpr int elems = kElems + vElems;
+};
+
+// HC query heads per wave (1, 2 or 4).  q rows beyond the chunk and padded
+// heads compute on clamped inputs and are never stored.
+template <int DT, int D, int HC>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(
+    uint16_t *__restrict__ out, const uint16_t *__restrict__ q,
+    const uint16_t *__restrict__ k_cache, const uint16_t *__restrict__ v_cache,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
+    const int32_t *__restrict__ query_start, float scale_log2, int log2_bs, int num_seqs,
+    int num_kv_heads, int num_heads, int group, int chunks, int max_blocks,
+    int64_t num_blocks, int nqb) {
+  using E = PElem<DT>;
+  constexpr int KSTEPS = D / 32;   // 16x16x32 MFMAs per QK product
+  constexpr int DTILES = D / 16;   // 16-dim output tiles
+  using T = Tile<D>;
+  __shared__ __align__(16) uint16_t lds[2 * T::elems];
+
+  // workgroup -> (query block, sequence, KV head, head chunk); heaviest first
+  const int per_qb = num_seqs * num_kv_heads * chunks;
+  const int qb = nqb - 1 - (int)(blockIdx.x / per_qb);
+  const int rest = blockIdx.x % per_qb;
+  const int chunk = rest % chunks;
+  const int kvh = (rest / chunks) % num_kv_heads;
+  const int seq = rest / (chunks * num_kv_heads);
+  const int q0 = query_start[seq];
+  const int n = query_start[seq + 1] - q0;
+  const int bs = 1 << log2_bs;
+  const int len = min(context_lens[seq], max_blocks * bs);
+  if (qb * kQB >= n || n > len) return;  // no rows here (or an invalid chunk)
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int col = lane & 15;   // token within the wave's 16 (B column / C column)
+  const int grp = lane >> 4;   // quarter: k slice of the operands, 4-row group of C
+  const int first_pos = len - n;                      // position of chunk row 0
+  const int wt0 = qb * kQB + wave * kQT;              // wave's first chunk row
+  const int tok = min(wt0 + col, n - 1);              // this lane's chunk row (clamped)
+  const int pos = first_pos + tok;                    // its context position
+  const int wave_lo = first_pos + min(wt0, n - 1);    // wave's first / last positions
+  const int wave_hi = first_pos + min(wt0 + kQT - 1, n - 1);
+  const int wg_hi = first_pos + min(qb * kQB + kQB - 1, n - 1);
+  const int ntiles = wg_hi / kKT + 1;                 // keys 0 .. wg_hi
+  const int32_t *tbl = block_tables + (int64_t)seq * max_blocks;
+  const int64_t blk_stride = (int64_t)num_kv_heads * bs * D;  // elements per block
+  const uint16_t *kbase = k_cache + (int64_t)kvh * bs * D;
+  const uint16_t *vbase = v_cache + (int64_t)kvh * D * bs;
+
+  // q of this lane's token for the HC heads, as B operands (dims 32ks+8grp..+8)
+  u32x4 qf[HC][KSTEPS];
+#pragma unroll
+  for (int c = 0; c < HC; ++c) {
+    const int h = kvh * group + min(chunk * HC + c, group - 1);
+    const uint16_t *qp = q + ((int64_t)(q0 + tok) * num_heads + h) * D + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[c][ks] = *(const u32x4 *)(qp + ks * 32);
+  }
+
+  // Tile loads: a tile is 4*D 16-byte pieces of K (piece p: key p / (D/8),
+  // dims 8*(p % (D/8)) ..) and 4*D of V (piece p: dim p / 4, keys 8*(p%4) ..);
+  // lane tid moves pieces tid + 256*j of each, j < D/64.
+  constexpr int KPR = D / 8;  // 16-byte pieces per K row
+  constexpr int NP = D / 64;  // pieces of each cache per lane
+  u32x4 st_k[NP], st_v[NP];
+  auto fetch = [&](int tile) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int p = tid + j * kThreads;
+      const int key = p / KPR;
+      const int t = min(tile * kKT + key, len - 1);  // past the context: any valid token
+      const int64_t b = tbl[t >> log2_bs];
+      const int64_t bb = (b >= 0 && b < num_blocks) ? b : 0;
+      st_k[j] = __builtin_nontemporal_load(
+          (const u32x4 *)(kbase + bb * blk_stride + (int64_t)(t & (bs - 1)) * D + (p % KPR) * 8));
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int p = tid + j * kThreads;
+      const int d = p / 4;
+      const int k8 = (p % 4) * 8;
+      const int t = min(tile * kKT + k8, (len - 1) & ~7);
+      const int64_t b = tbl[t >> log2_bs];
+      const int64_t bb = (b >= 0 && b < num_blocks) ? b : 0;
+      st_v[j] = __builtin_nontemporal_load(
+          (const u32x4 *)(vbase + bb * blk_stride + (int64_t)d * bs + (t & (bs - 1))));
+    }
+  };
+  // Into LDS; V of keys at or past the context length is zeroed there (those
+  // slots may hold anything, NaN included, and meet weight 0).
+  auto stash = [&](int buf, int tile) {
+    uint16_t *kl = lds + buf * T::elems;
+    uint16_t *vl = kl + T::kElems;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int p = tid + j * kThreads;
+      *(u32x4 *)(kl + (p / KPR) * T::kRow + (p % KPR) * 8) = st_k[j];
+      const int valid = len - (tile * kKT + (p % 4) * 8);  // keys of the piece below len
+      u32x4 v = st_v[j];
+      if (valid < 8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = valid - 2 * e;
+          v[e] &= c >= 2 ? 0xffffffffu : (c == 1 ? 0x0000ffffu : 0u);
+        }
+      }
+      *(u32x4 *)(vl + (p / 4) * T::vRow + (p % 4) * 8) = v;
+    }
+  };
+
+  constexpr float kSlack = 8.f;
+  float m_ref[HC], l_run[HC];
+  f32x4 acc[HC][DTILES];
+#pragma unroll
+  for (int c = 0; c < HC; ++c) {
+    m_ref[c] = -INFINITY;
+    l_run[c] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt) acc[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  fetch(0);
+  stash(0, 0);
+  __syncthreads();
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    if (tile + 1 < ntiles) fetch(tile + 1);  // in flight while this tile is used
+    const int t0 = tile * kKT;
+    if (t0 <= wave_hi) {  // the wave sees at least one key of this tile
+      const uint16_t *kl = lds + buf * T::elems;
+      const uint16_t *vl = kl + T::kElems;
+      // scores: two 16-key row blocks x HC heads
+      f32x4 sc[2][HC];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        u32x4 ka[KSTEPS];
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+          ka[ks] = *(const u32x4 *)(kl + (rb * 16 + col) * T::kRow + ks * 32 + grp * 8);
+#pragma unroll
+        for (int c = 0; c < HC; ++c) {
+          f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KSTEPS; ++ks) s = E::mfma(ka[ks], qf[c][ks], s);
+          sc[rb][c] = s * scale_log2;
+        }
+      }
+      if (t0 + kKT - 1 > wave_lo) {  // causal edge: keys past a row's position
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool ok = t0 + rb * 16 + grp * 4 + r <= pos;
+#pragma unroll
+            for (int c = 0; c < HC; ++c) sc[rb][c][r] = ok ? sc[rb][c][r] : -INFINITY;
+          }
+      }
+      u32x4 pb[HC], pl[HC];  // P^T as the B operand: keys 4grp..+3 then 16+4grp..+3
+#pragma unroll
+      for (int c = 0; c < HC; ++c) {
+        float mx = fmaxf(fmaxf(fmaxf(sc[0][c][0], sc[0][c][1]), fmaxf(sc[0][c][2], sc[0][c][3])),
+                         fmaxf(fmaxf(sc[1][c][0], sc[1][c][1]), fmaxf(sc[1][c][2], sc[1][c][3])));
+        mx = rows_max(mx);  // every row of the tile has key 0 <= its position, or is all -inf
+        if (__ballot(mx > m_ref[c] + kSlack)) {
+          const float m_new = fmaxf(m_ref[c], mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_ref[c] - m_new);
+          l_run[c] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DTILES; ++dt) acc[c][dt] *= alpha;
+          m_ref[c] = m_new;
+        }
+        float p[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = __builtin_amdgcn_exp2f(sc[0][c][r] - m_ref[c]);
+          p[4 + r] = __builtin_amdgcn_exp2f(sc[1][c][r] - m_ref[c]);
+        }
+        pb[c] = u32x4{E::pack(p[0], p[1]), E::pack(p[2], p[3]), E::pack(p[4], p[5]),
+                      E::pack(p[6], p[7])};
+        if constexpr (E::kSplitP) {
+          // residuals are exact in fp32; the sum is taken over the full weights
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pl[c][e] = E::pack(p[2 * e] - E::lo(pb[c][e]), p[2 * e + 1] - E::hi(pb[c][e]));
+          l_run[c] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        } else {
+          // the sum uses the rounded weights the MFMA multiplies with
+          float r = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r += E::lo(pb[c][e]) + E::hi(pb[c][e]);
+          l_run[c] += r;
+        }
+      }
+      // O^T += V^T P^T over the 32 keys, in the key order of pb
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt) {
+        const uint16_t *vr = vl + (dt * 16 + col) * T::vRow + grp * 4;
+        const u32x2 lo = *(const u32x2 *)vr;          // keys 4grp .. +3
+        const u32x2 hi = *(const u32x2 *)(vr + 16);   // keys 16+4grp .. +3
+        const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+        for (int c = 0; c < HC; ++c) {
+          acc[c][dt] = E::mfma(va, pb[c], acc[c][dt]);
+          if constexpr (E::kSplitP) acc[c][dt] = E::mfma(va, pl[c], acc[c][dt]);
+        }
+      }
+    }
+    if (tile + 1 < ntiles) {
+      // The other buffer was last read in the previous iteration, before its
+      // barrier, so it can be filled now; the barrier after makes the fill
+      // visible before anyone reads it (and keeps any wave from refilling
+      // this buffer while another still reads it).
+      stash(buf ^ 1, tile + 1);
+      __syncthreads();
+    }
+  }
+
+  // rows of this lane: token col of the wave, heads c; lane holds dims
+  // 16*dt + 4*grp + 0..3
+  float inv[HC];
+#pragma unroll
+  for (int c = 0; c < HC; ++c) inv[c] = 1.0f / rows_sum(l_run[c]);  // whole wave
+  const int row = wt0 + col;
+  if (row < n) {
+#pragma unroll
+    for (int c = 0; c < HC; ++c) {
+      const int hg = chunk * HC + c;
+      if (hg >= group) continue;
+      uint16_t *op = out + ((int64_t)(q0 + row) * num_heads + kvh * group + hg) * D + grp * 4;
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt) {
+        u32x2 w;
+        w.x = E::pack(acc[c][dt][0] * inv[c], acc[c][dt][1] * inv[c]);
+        w.y = E::pack(acc[c][dt][2] * inv[c], acc[c][dt][3] * inv[c]);
+        *(u32x2 *)(op + dt * 16) = w;
+      }
+    }
+  }
+}
+
+template <int DT, int D, int HC>
+int launch_hc(const PrefillArgs &a) {
+  const int group = a.num_heads / a.num_kv_heads;
+  const int chunks = (group + HC - 1) / HC;
+  const int nqb = (a.max_query_len + kQB - 1) / kQB;
+  const int64_t groups = (int64_t)nqb * a.num_seqs * a.num_kv_heads * chunks;
+  if (groups == 0) return 0;
+  if (groups > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
+  int log2_bs = 0;
+  while ((1 << log2_bs) < a.block_size) ++log2_bs;
+  const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+  prefill_kernel<DT, D, HC><<<dim3((unsigned)groups), kThreads, 0, (hipStream_t)a.stream>>>(
+      (uint16_t *)a.out, (const uint16_t *)a.q, (const uint16_t *)a.k_cache,
+      (const uint16_t *)a.v_cache, a.block_tables, a.context_lens, a.query_start, scale_log2,
+      log2_bs, a.num_seqs, a.num_kv_heads, a.num_heads, group, chunks, a.max_blocks_per_seq,
+      a.num_blocks, nqb);
+  return (int)hipGetLastError();
+}
+
+template <int DT, int D>
+int launch_d(const PrefillArgs &a) {
+  const int group = a.num_heads / a.num_kv_heads;
+  if (group == 1) return launch_hc<DT, D, 1>(a);
+  if (group == 2) return launch_hc<DT, D, 2>(a);
+  return launch_hc<DT, D, 4>(a);
+}
+
+template <int DT>
+int launch_dt(const PrefillArgs &a) {
+  return a.head_dim == 64 ? launch_d<DT, 64>(a) : launch_d<DT, 128>(a);
+}
+
+}  // namespace
+
+int launch_prefill(const PrefillArgs &a) {
+  return a.dtype == 1 ? launch_dt<1>(a) : launch_dt<0>(a);
+}
+
+}  // namespace pa

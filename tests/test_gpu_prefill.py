@@ -1,0 +1,141 @@
+"""GPU parity of paged_attention_prefill (chunked prefill) through the C ABI
+against oracle_prefill: |gpu - oracle| <= 2e-3 + 1e-2 * |oracle| element by
+element, on ragged batches mixing whole prompts, chunks after a cached
+prefix (prefix and chunk lengths off tile and block edges), one-row chunks
+and empty chunks, over head_dim, block size, GQA group (1 to 16) and dtype;
+and a Llama-3-8B-shaped chunk batch (sampled rows).  Rows outside the
+chunks are never written."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from pagedattention_kv_cache_paged_amd import binding as B
+from pagedattention_kv_cache_paged_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TD = {W.F16: torch.float16, W.BF16: torch.bfloat16}
+ATOL, RTOL = 2e-3, 1e-2
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def f64(bits, dtype):
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dtype == W.F16:
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def dev_bits(bits, dtype):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(TD[dtype])
+
+
+def run(lengths, chunks, G, hkv, d, bs, dtype, seed, rows=None):
+    w = W.build("pf", lengths, num_heads=G * hkv, num_kv_heads=hkv, head_dim=d,
+                block_size=bs, dtype=dtype, seed=seed)
+    ksh, vsh = w.cache_shapes()
+    nan = int(np.array([W.NAN_BITS[dtype]], np.uint16).view(np.int16)[0])
+    kc = torch.full(ksh, nan, dtype=torch.int16, device=DEV).view(TD[dtype])
+    vc = torch.full(vsh, nan, dtype=torch.int16, device=DEV).view(TD[dtype])
+    okc, ovc = w.nan_caches()
+    for which in ("hist", "new"):
+        k, v, s = w.write_batch(which)
+        B.paged_kv_write(dev_bits(k, dtype), dev_bits(v, dtype), torch.from_numpy(s).to(DEV),
+                         kc, vc)
+        oracle.kv_write(k, v, s, okc, ovc, bs)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    g = np.random.default_rng(seed + 7)
+    q = W.normal_bits(g, (int(qs[-1]), w.num_heads, d), dtype)
+    qd = dev_bits(q, dtype)
+    out = torch.full_like(qd, float("nan"))
+    say(f"prefill B={len(lengths)} G={G} hkv={hkv} D={d} bs={bs} {dtype} rows={qs[-1]}")
+    B.paged_attention_prefill(out, qd, kc, vc, torch.from_numpy(w.block_tables).to(DEV),
+                              torch.from_numpy(w.context_lens).to(DEV),
+                              torch.from_numpy(qs).to(DEV), w.scale, bs, hkv,
+                              max(chunks) if len(chunks) else 0)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    if rows is None:
+        ref = oracle.prefill(q, okc, ovc, w.block_tables, w.context_lens, qs, w.scale, bs,
+                             dtype)
+        return got, ref, None
+    # sampled rows: the oracle over those rows only (each row on its own)
+    ref = np.zeros((len(rows), w.num_heads, d))
+    seq_of = np.searchsorted(qs, rows, side="right") - 1
+    for j, (r, s) in enumerate(zip(rows, seq_of)):
+        L = int(w.context_lens[s])
+        p = L - (qs[s + 1] - qs[s]) + (r - qs[s])
+        ref[j] = oracle.prefill(q[r:r + 1], okc, ovc, w.block_tables[s:s + 1],
+                                np.array([p + 1], np.int32), np.array([0, 1], np.int32),
+                                w.scale, bs, dtype)[0]
+    return got[rows], ref, None
+
+
+def check(got, ref, dtype, what):
+    g = f64(got, dtype)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    bad = ~(err <= ATOL + RTOL * np.abs(ref))
+    say(f"  {what} max_abs={err.max():.3e} n={ref.size}")
+    assert not bad.any(), f"{what}: {bad.sum()} out of tolerance, worst {err[bad].max():.3e}"
+
+
+CASES = []
+for i, (G, d, bs, dt) in enumerate([(1, 64, 16, W.F16), (2, 128, 8, W.BF16), (3, 64, 32, W.BF16),
+                                    (4, 128, 16, W.BF16), (5, 64, 8, W.F16), (8, 128, 32, W.F16),
+                                    (16, 64, 16, W.BF16), (4, 64, 32, W.F16), (1, 128, 8, W.BF16)]):
+    CASES.append((i, G, d, bs, dt))
+
+
+@pytest.mark.parametrize("i,G,d,bs,dt", CASES)
+def test_prefill_ragged(i, G, d, bs, dt):
+    g = np.random.default_rng(900 + i)
+    lengths = [1, 17, 64, 130, 200, 97, 33, 300]
+    chunks = [1, 17, 64, 66, 1, 0, 20, 129]   # whole prompts, prefix + chunk, one row, none
+    hkv = int(g.integers(1, 3))
+    got, ref, _ = run(lengths, chunks, G, hkv, d, bs, dt, 1000 + i)
+    check(got, ref, dt, f"ragged{i}")
+
+
+def test_prefill_long_prompt_and_edges():
+    """A whole 1000-token prompt (many key tiles, 16 query blocks), a chunk
+    that starts mid-tile, and chunk lengths one either side of 64."""
+    got, ref, _ = run([1000, 511, 95, 65], [1000, 200, 63, 65], 4, 2, 128, 16, W.BF16, 77)
+    check(got, ref, W.BF16, "long")
+
+
+def test_prefill_llama8b_chunks():
+    """Llama-3-8B shape: 4 sequences, 512-token chunks after 1536 cached
+    tokens (32 q / 8 kv heads, head_dim 128, bf16, block 16); sampled rows."""
+    g = np.random.default_rng(5)
+    rows = np.sort(g.choice(4 * 512, 48, replace=False))
+    got, ref, _ = run([2048] * 4, [512] * 4, 4, 8, 128, 16, W.BF16, 55, rows=rows)
+    check(got, ref, W.BF16, "llama8b chunks")
+
+
+def test_prefill_leaves_other_rows():
+    """Rows past every chunk (the tail of q / out) are not written, and a
+    chunk longer than its context gets no rows."""
+    w = W.build("pfx", [40, 30], num_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
+                dtype=W.F16, seed=3)
+    ksh, vsh = w.cache_shapes()
+    kc = torch.zeros(ksh, dtype=torch.float16, device=DEV)
+    vc = torch.zeros(vsh, dtype=torch.float16, device=DEV)
+    for which in ("hist", "new"):
+        k, v, s = w.write_batch(which)
+        B.paged_kv_write(dev_bits(k, W.F16), dev_bits(v, W.F16), torch.from_numpy(s).to(DEV),
+                         kc, vc)
+    q = torch.randn(80, 4, 64, dtype=torch.float16, device=DEV)
+    out = torch.full_like(q, 7.0)
+    qs = torch.tensor([0, 10, 45], dtype=torch.int32, device=DEV)   # seq 1: 35 rows > 30 tokens
+    B.paged_attention_prefill(out, q, kc, vc, torch.from_numpy(w.block_tables).to(DEV),
+                              torch.from_numpy(w.context_lens).to(DEV), qs, w.scale, 16, 2, 35)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    assert np.all(o[10:] == 7.0)
+    assert np.all(np.isfinite(o[:10])) and not np.all(o[:10] == 7.0)
