@@ -309,6 +309,100 @@ def bench_swap_blocks(args, torch, B, dev, lib):
     print(json.dumps(result), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 MFMA, MI355X
+PREFILL_KERNEL = "prefill_kernel"
+
+
+def bench_prefill(args, torch, B, W, dev, lib):
+    """Chunked prefill at the Llama-3-8B shape: 8 sequences, each with 1536
+    cached tokens and a 512-token chunk (32 q / 8 kv heads, head_dim 128,
+    block 16, bf16, random block placement).  Algorithmic flops: for each
+    chunk row at position p and each query head, 2*D*(p+1) for q K^T and the
+    same for P V."""
+    nseq, cached, chunk = 8, 1536, 512
+    w = W.build("prefill", [cached + chunk] * nseq, num_heads=32, num_kv_heads=8,
+                head_dim=128, block_size=16, dtype=W.BF16, seed=61)
+    tdt = torch.bfloat16
+
+    def dev_bits(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(tdt)
+
+    ks, vs = w.cache_shapes()
+    kc = torch.zeros(ks, dtype=tdt, device=dev)
+    vc = torch.zeros(vs, dtype=tdt, device=dev)
+    for which in ("hist", "new"):
+        k, v, sl = w.write_batch(which)
+        B.paged_kv_write(dev_bits(k), dev_bits(v), torch.from_numpy(sl).to(dev), kc, vc)
+    qs_np = (np.arange(nseq + 1) * chunk).astype(np.int32)
+    g = np.random.default_rng(62)
+    q_bits = W.normal_bits(g, (nseq * chunk, 32, 128), W.BF16)
+    q = dev_bits(q_bits)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    cl = torch.from_numpy(w.context_lens).to(dev)
+    qs = torch.from_numpy(qs_np).to(dev)
+    sp = torch.cuda.current_stream().cuda_stream
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        rc = lib.paged_attention_prefill(out.data_ptr(), q.data_ptr(), kc.data_ptr(),
+                                         vc.data_ptr(), bt.data_ptr(), cl.data_ptr(),
+                                         qs.data_ptr(), w.scale, 16, 8, nseq, 32, 128,
+                                         w.max_blocks_per_seq, w.num_blocks, 1, chunk, sp)
+        assert rc == 0, rc
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    K = args.steps
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(K):
+        launch()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / K * 1e3
+    positions = np.arange(cached, cached + chunk, dtype=np.float64)
+    flops = nseq * 32 * float(np.sum(4.0 * 128 * (positions + 1)))
+    tflops = flops / (us * 1e-6) / 1e12
+    result = {
+        "metric": "paged chunked-prefill attention TFLOP/s (% of MFMA peak), Llama-3-8B shape",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(us * 1e-3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"chunked prefill: {nseq} sequences x {chunk}-token chunk after "
+                               f"{cached} cached tokens; 32 q / 8 kv heads, head_dim 128, "
+                               f"block 16, bf16", "rows": nseq * chunk,
+                   "context_tokens": nseq * (cached + chunk)},
+        "tokens_per_s": round(nseq * chunk / (us * 1e-6), 1),
+        "roofline": {"kernel": PREFILL_KERNEL, "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "avg_launch_us": round(us, 3),
+                     "traffic": None, "flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        okc, ovc = w.nan_caches()
+        for which in ("hist", "new"):
+            k, v, sl = w.write_batch(which)
+            oracle.kv_write(k, v, sl, okc, ovc, 16)
+        done, fl, t_total = 0, 0.0, 0.0
+        while done < chunk and t_total < min(args.cpu_seconds, 15.0):
+            p = cached + done   # rows of sequence 0, one at a time
+            t0 = time.perf_counter()
+            oracle.prefill(q_bits[done:done + 1], okc, ovc, w.block_tables[:1],
+                           np.array([p + 1], np.int32), np.array([0, 1], np.int32), w.scale,
+                           16, W.BF16)
+            t_total += time.perf_counter() - t0
+            fl += 32 * 4.0 * 128 * (p + 1)
+            done += 1
+        result["cpu_baseline"] = {"value": round(fl / t_total / 1e12, 9), "unit": "TFLOP/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"the first {done} chunk rows of sequence 0, all 32 "
+                                            f"heads, fp64 C oracle, single thread, "
+                                            f"{t_total:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,10 +415,12 @@ def main():
                     help="physical block placement of the llama8b workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="decode", choices=("decode", "copy_blocks", "swap_blocks"),
+    ap.add_argument("--op", default="decode",
+                    choices=("decode", "copy_blocks", "swap_blocks", "prefill"),
                     help="decode: the decode step (default); copy_blocks: the copy-on-write "
                          "block copy of 128 forks of a shared prompt (prefix-sharing shape); "
-                         "swap_blocks: swap 1024 blocks out to pinned host memory and back")
+                         "swap_blocks: swap 1024 blocks out to pinned host memory and back; "
+                         "prefill: 512-token chunks after 1536 cached tokens, 8 sequences")
     ap.add_argument("--step", default="fused", choices=("fused", "separate"),
                     help="fused: paged_attention_decode_append (two launches); separate: "
                          "paged_kv_write + paged_attention_decode (three launches)")
@@ -365,6 +461,8 @@ def main():
         return bench_copy_blocks(args, torch, B, W, dev, lib)
     if args.op == "swap_blocks":
         return bench_swap_blocks(args, torch, B, dev, lib)
+    if args.op == "prefill":
+        return bench_prefill(args, torch, B, W, dev, lib)
     w = make_workload(args.workload, args.placement)
     tdt = {W.F16: torch.float16, W.BF16: torch.bfloat16}[w.dtype]
 

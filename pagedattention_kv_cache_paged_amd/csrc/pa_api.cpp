@@ -269,8 +269,9 @@ int paged_attention_prefill(void *out, const void *q, const void *k_cache, const
   if (dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_DTYPE;
   if (!decode_sizes_ok(num_seqs, num_kv_heads, num_heads, head_dim, max_blocks_per_seq,
                        block_size) ||
-      num_blocks <= 0 || num_blocks > INT32_MAX || !std::isfinite(scale) || max_query_len < 0 ||
-      (int64_t)max_query_len > (int64_t)max_blocks_per_seq * block_size)
+      num_blocks <= 0 || num_blocks > INT32_MAX || !std::isfinite(scale) || !(scale > 0.0f) ||
+      max_query_len < 0 || (int64_t)max_query_len > (int64_t)max_blocks_per_seq * block_size ||
+      max_blocks_per_seq > pa::kPrefillMaxBlocks)
     return PA_ERR_SHAPE;
   if (num_seqs == 0 || max_query_len == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)

@@ -14,6 +14,7 @@ constexpr int kWorkspaceAlign = 256;
 constexpr int kMaxTilesPerWave = 64; // one tile per lane of the wave's tile map
 constexpr int kTargetWaves = 1024;   // default split: one wave per SIMD of 256 CUs
 constexpr int kMaxSeqs = 8192;       // tile prefix and lengths live in LDS
+constexpr int kPrefillMaxBlocks = 4096;  // prefill keeps a sequence's block ids in LDS
 
 struct DecodeArgs {
   void *out;

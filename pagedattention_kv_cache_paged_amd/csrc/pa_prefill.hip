@@ -10,11 +10,12 @@
 //
 // Unlike decode this is a dense contraction: every K/V tile meets many query
 // rows, so the bound is the MFMA rate, not HBM.  Work split:
-//   workgroup = (64 query tokens of one sequence) x (up to HC query heads of
-//   one KV head); four waves, each 16 tokens x HC heads (16*HC query rows).
+//   workgroup = (64 query tokens of one sequence) x (up to 4 query heads of
+//   one KV head); waves of 16 tokens x up to 2 heads (at most 32 query rows,
+//   under 256 registers, two waves per SIMD).
 //   The workgroup walks the keys 0 .. its last position in tiles of 32: K
-//   and V tiles go through double-buffered LDS (each of the 256 lanes moves
-//   four 16-byte pieces), so a tile is read from memory once per 64*HC rows.
+//   and V tiles go through double-buffered LDS (the lanes move 16-byte
+//   pieces), so a tile is read from memory once per 64 tokens x 4 heads.
 //   Workgroups run heaviest-first (last query block first) and the blocks of
 //   one (sequence, KV head) land on one XCD, sharing its L2.
 // Per wave and 32-key tile, with q held in registers as the B operand:
@@ -49,10 +50,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kQT = 16;          // query tokens per wave
-constexpr int kWaves = 4;        // waves per workgroup
-constexpr int kQB = kQT * kWaves;  // query tokens per workgroup
+constexpr int kTG = 4;           // token groups per workgroup
+constexpr int kQB = kQT * kTG;   // query tokens per workgroup
 constexpr int kKT = 32;          // keys per tile
-constexpr int kThreads = kWaves * kWave;
 
 template <int DT>
 struct PElem;
@@ -118,10 +118,13 @@ struct Tile {
   static constexpr int elems = kElems + vElems;
 };
 
-// HC query heads per wave (1, 2 or 4).  q rows beyond the chunk and padded
+// HW query heads per wave (1 or 2) and NWH head groups per workgroup (1 or
+// 2): a workgroup is 4 * NWH waves serving 64 tokens x HW * NWH heads, and a
+// wave stays under 256 registers, so two waves share each SIMD and one's
+// softmax overlaps the other's MFMAs.  q rows beyond the chunk and padded
 // heads compute on clamped inputs and are never stored.
-template <int DT, int D, int HC>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(
+template <int DT, int D, int HW, int NWH>
+__global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
     uint16_t *__restrict__ out, const uint16_t *__restrict__ q,
     const uint16_t *__restrict__ k_cache, const uint16_t *__restrict__ v_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
@@ -129,10 +132,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     int num_kv_heads, int num_heads, int group, int chunks, int max_blocks,
     int64_t num_blocks, int nqb) {
   using E = PElem<DT>;
+  constexpr int HC = HW * NWH;     // query heads per workgroup
+  constexpr int kThreads = kWave * kTG * NWH;
   constexpr int KSTEPS = D / 32;   // 16x16x32 MFMAs per QK product
   constexpr int DTILES = D / 16;   // 16-dim output tiles
   using T = Tile<D>;
-  __shared__ __align__(16) uint16_t lds[2 * T::elems];
+  // LDS: two K/V tile buffers, then the sequence's block ids (clamped into
+  // the pool), so that tile addresses never wait on a global load.
+  extern __shared__ __align__(16) uint16_t lds[];
+  int32_t *tbl_lds = reinterpret_cast<int32_t *>(lds + 2 * T::elems);
 
   // workgroup -> (query block, sequence, KV head, head chunk); heaviest first
   const int per_qb = num_seqs * num_kv_heads * chunks;
@@ -148,7 +156,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   if (qb * kQB >= n || n > len) return;  // no rows here (or an invalid chunk)
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = (tid / kWave) % kTG;   // token group
+  const int hgrp = tid / (kWave * kTG);   // head group
   const int lane = tid % kWave;
   const int col = lane & 15;   // token within the wave's 16 (B column / C column)
   const int grp = lane >> 4;   // quarter: k slice of the operands, 4-row group of C
@@ -161,15 +170,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   const int wg_hi = first_pos + min(qb * kQB + kQB - 1, n - 1);
   const int ntiles = wg_hi / kKT + 1;                 // keys 0 .. wg_hi
   const int32_t *tbl = block_tables + (int64_t)seq * max_blocks;
+  const int nent = (wg_hi >> log2_bs) + 1;  // table entries of keys 0 .. wg_hi
+  for (int i = tid; i < nent; i += kThreads) {
+    const int b = tbl[i];
+    tbl_lds[i] = (b >= 0 && b < num_blocks) ? b : 0;
+  }
+  __syncthreads();
   const int64_t blk_stride = (int64_t)num_kv_heads * bs * D;  // elements per block
   const uint16_t *kbase = k_cache + (int64_t)kvh * bs * D;
   const uint16_t *vbase = v_cache + (int64_t)kvh * D * bs;
 
-  // q of this lane's token for the HC heads, as B operands (dims 32ks+8grp..+8)
-  u32x4 qf[HC][KSTEPS];
+  // q of this lane's token for the wave's HW heads, as B operands (dims
+  // 32ks+8grp..+8)
+  u32x4 qf[HW][KSTEPS];
 #pragma unroll
-  for (int c = 0; c < HC; ++c) {
-    const int h = kvh * group + min(chunk * HC + c, group - 1);
+  for (int c = 0; c < HW; ++c) {
+    const int h = kvh * group + min(chunk * HC + hgrp * HW + c, group - 1);
     const uint16_t *qp = q + ((int64_t)(q0 + tok) * num_heads + h) * D + grp * 8;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qf[c][ks] = *(const u32x4 *)(qp + ks * 32);
@@ -179,42 +195,46 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   // dims 8*(p % (D/8)) ..) and 4*D of V (piece p: dim p / 4, keys 8*(p%4) ..);
   // lane tid moves pieces tid + 256*j of each, j < D/64.
   constexpr int KPR = D / 8;  // 16-byte pieces per K row
-  constexpr int NP = D / 64;  // pieces of each cache per lane
-  u32x4 st_k[NP], st_v[NP];
-  auto fetch = [&](int tile) {
+  constexpr int NP = (4 * D + kThreads - 1) / kThreads;  // pieces of each cache per lane
+  constexpr bool kAllLoad = NP * kThreads == 4 * D;       // every lane has NP pieces
+  // A ring of kStages register stages: a tile's loads are issued
+  // kStages - 1 tiles before they go into LDS, so the wait for them is
+  // covered by that many tiles of compute.
+  constexpr int kStages = 3;
+  u32x4 st_k[kStages][NP], st_v[kStages][NP];
+  auto fetch = [&](int stage, int tile) {
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
-      const int p = tid + j * kThreads;
+      const int p = min(tid + j * kThreads, 4 * D - 1);
       const int key = p / KPR;
-      const int t = min(tile * kKT + key, len - 1);  // past the context: any valid token
-      const int64_t b = tbl[t >> log2_bs];
-      const int64_t bb = (b >= 0 && b < num_blocks) ? b : 0;
-      st_k[j] = __builtin_nontemporal_load(
+      const int t = min(tile * kKT + key, wg_hi);  // past the rows' reach: any seen token
+      const int64_t bb = tbl_lds[t >> log2_bs];
+      st_k[stage][j] = __builtin_nontemporal_load(
           (const u32x4 *)(kbase + bb * blk_stride + (int64_t)(t & (bs - 1)) * D + (p % KPR) * 8));
     }
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
-      const int p = tid + j * kThreads;
+      const int p = min(tid + j * kThreads, 4 * D - 1);
       const int d = p / 4;
       const int k8 = (p % 4) * 8;
-      const int t = min(tile * kKT + k8, (len - 1) & ~7);
-      const int64_t b = tbl[t >> log2_bs];
-      const int64_t bb = (b >= 0 && b < num_blocks) ? b : 0;
-      st_v[j] = __builtin_nontemporal_load(
+      const int t = min(tile * kKT + k8, wg_hi & ~7);
+      const int64_t bb = tbl_lds[t >> log2_bs];
+      st_v[stage][j] = __builtin_nontemporal_load(
           (const u32x4 *)(vbase + bb * blk_stride + (int64_t)d * bs + (t & (bs - 1))));
     }
   };
-  // Into LDS; V of keys at or past the context length is zeroed there (those
-  // slots may hold anything, NaN included, and meet weight 0).
-  auto stash = [&](int buf, int tile) {
+  // Into LDS; V of keys past the workgroup's last position is zeroed there
+  // (those keys are not loaded, or lie past the context, and meet weight 0).
+  auto stash = [&](int stage, int buf, int tile) {
     uint16_t *kl = lds + buf * T::elems;
     uint16_t *vl = kl + T::kElems;
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       const int p = tid + j * kThreads;
-      *(u32x4 *)(kl + (p / KPR) * T::kRow + (p % KPR) * 8) = st_k[j];
-      const int valid = len - (tile * kKT + (p % 4) * 8);  // keys of the piece below len
-      u32x4 v = st_v[j];
+      if (!kAllLoad && p >= 4 * D) break;
+      *(u32x4 *)(kl + (p / KPR) * T::kRow + (p % KPR) * 8) = st_k[stage][j];
+      const int valid = wg_hi + 1 - (tile * kKT + (p % 4) * 8);  // keys the rows can see
+      u32x4 v = st_v[stage][j];
       if (valid < 8) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -227,122 +247,133 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   };
 
   constexpr float kSlack = 8.f;
-  float m_ref[HC], l_run[HC];
-  f32x4 acc[HC][DTILES];
+  float m_ref[HW], l_run[HW];
+  f32x4 acc[HW][DTILES];
 #pragma unroll
-  for (int c = 0; c < HC; ++c) {
+  for (int c = 0; c < HW; ++c) {
     m_ref[c] = -INFINITY;
     l_run[c] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) acc[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  fetch(0);
-  stash(0, 0);
+  // Tiles go LDS buffer (tile % 2); tile t's registers sit in stage t % kStages.
+#pragma unroll
+  for (int b = 0; b < kStages - 1; ++b) fetch(b, min(b, ntiles - 1));
+  stash(0, 0, 0);
   __syncthreads();
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < ntiles) fetch(tile + 1);  // in flight while this tile is used
-    const int t0 = tile * kKT;
-    if (t0 <= wave_hi) {  // the wave sees at least one key of this tile
-      const uint16_t *kl = lds + buf * T::elems;
-      const uint16_t *vl = kl + T::kElems;
-      // scores: two 16-key row blocks x HC heads
-      f32x4 sc[2][HC];
+  for (int tb = 0; tb < ntiles; tb += kStages) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        u32x4 ka[KSTEPS];
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
-          ka[ks] = *(const u32x4 *)(kl + (rb * 16 + col) * T::kRow + ks * 32 + grp * 8);
-#pragma unroll
-        for (int c = 0; c < HC; ++c) {
-          f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KSTEPS; ++ks) s = E::mfma(ka[ks], qf[c][ks], s);
-          sc[rb][c] = s * scale_log2;
-        }
-      }
-      if (t0 + kKT - 1 > wave_lo) {  // causal edge: keys past a row's position
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bool ok = t0 + rb * 16 + grp * 4 + r <= pos;
-#pragma unroll
-            for (int c = 0; c < HC; ++c) sc[rb][c][r] = ok ? sc[rb][c][r] : -INFINITY;
+    for (int b = 0; b < kStages; ++b) {
+      const int tile = tb + b;
+      // past the last tile the ring reloads the last tile (cache hits), so
+      // no load sits behind a branch and every wait stays exact
+      fetch((b + kStages - 1) % kStages, min(tile + kStages - 1, ntiles - 1));
+      if (tile < ntiles) {
+        const int buf = tile & 1;
+        const int t0 = tile * kKT;
+        if (t0 <= wave_hi) {  // the wave sees at least one key of this tile
+          const uint16_t *kl = lds + buf * T::elems;
+          const uint16_t *vl = kl + T::kElems;
+          // raw scores q.k: two 16-key row blocks x HW heads; the scale (> 0,
+          // in log2 units) joins in the exponent's FMA and on the tile max
+          f32x4 sc[2][HW];
+    #pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            u32x4 ka[KSTEPS];
+    #pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+              ka[ks] = *(const u32x4 *)(kl + (rb * 16 + col) * T::kRow + ks * 32 + grp * 8);
+    #pragma unroll
+            for (int c = 0; c < HW; ++c) {
+              f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+              for (int ks = 0; ks < KSTEPS; ++ks) s = E::mfma(ka[ks], qf[c][ks], s);
+              sc[rb][c] = s;
+            }
           }
+          if (t0 + kKT - 1 > wave_lo) {  // causal edge: keys past a row's position
+    #pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+    #pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const bool ok = t0 + rb * 16 + grp * 4 + r <= pos;
+    #pragma unroll
+                for (int c = 0; c < HW; ++c) sc[rb][c][r] = ok ? sc[rb][c][r] : -INFINITY;
+              }
+          }
+          u32x4 pb[HW], pl[HW];  // P^T as the B operand: keys 4grp..+3 then 16+4grp..+3
+    #pragma unroll
+          for (int c = 0; c < HW; ++c) {
+            float mx = fmaxf(fmaxf(fmaxf(sc[0][c][0], sc[0][c][1]), fmaxf(sc[0][c][2], sc[0][c][3])),
+                             fmaxf(fmaxf(sc[1][c][0], sc[1][c][1]), fmaxf(sc[1][c][2], sc[1][c][3])));
+            mx = rows_max(mx) * scale_log2;  // a row whose keys all lie past it gives -inf
+            if (__ballot(mx > m_ref[c] + kSlack)) {
+              const float m_new = fmaxf(m_ref[c], mx);
+              const float alpha = __builtin_amdgcn_exp2f(m_ref[c] - m_new);
+              l_run[c] *= alpha;
+    #pragma unroll
+              for (int dt = 0; dt < DTILES; ++dt) acc[c][dt] *= alpha;
+              m_ref[c] = m_new;
+            }
+            float p[8];
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              p[r] = __builtin_amdgcn_exp2f(fmaf(sc[0][c][r], scale_log2, -m_ref[c]));
+              p[4 + r] = __builtin_amdgcn_exp2f(fmaf(sc[1][c][r], scale_log2, -m_ref[c]));
+            }
+            pb[c] = u32x4{E::pack(p[0], p[1]), E::pack(p[2], p[3]), E::pack(p[4], p[5]),
+                          E::pack(p[6], p[7])};
+            if constexpr (E::kSplitP) {
+              // residuals are exact in fp32; the sum is taken over the full weights
+    #pragma unroll
+              for (int e = 0; e < 4; ++e)
+                pl[c][e] = E::pack(p[2 * e] - E::lo(pb[c][e]), p[2 * e + 1] - E::hi(pb[c][e]));
+              l_run[c] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            } else {
+              // the sum uses the rounded weights the MFMA multiplies with
+              float r = 0.f;
+    #pragma unroll
+              for (int e = 0; e < 4; ++e) r += E::lo(pb[c][e]) + E::hi(pb[c][e]);
+              l_run[c] += r;
+            }
+          }
+          // O^T += V^T P^T over the 32 keys, in the key order of pb
+    #pragma unroll
+          for (int dt = 0; dt < DTILES; ++dt) {
+            const uint16_t *vr = vl + (dt * 16 + col) * T::vRow + grp * 4;
+            const u32x2 lo = *(const u32x2 *)vr;          // keys 4grp .. +3
+            const u32x2 hi = *(const u32x2 *)(vr + 16);   // keys 16+4grp .. +3
+            const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
+    #pragma unroll
+            for (int c = 0; c < HW; ++c) {
+              acc[c][dt] = E::mfma(va, pb[c], acc[c][dt]);
+              if constexpr (E::kSplitP) acc[c][dt] = E::mfma(va, pl[c], acc[c][dt]);
+            }
+          }
+        }
+        if (tile + 1 < ntiles) {
+          // The other buffer was last read in the previous tile, before its
+          // barrier, so it can be filled now; the barrier after makes the
+          // fill visible before anyone reads it (and keeps any wave from
+          // refilling this buffer while another still reads it).
+          stash((b + 1) % kStages, buf ^ 1, tile + 1);
+          __syncthreads();
+        }
       }
-      u32x4 pb[HC], pl[HC];  // P^T as the B operand: keys 4grp..+3 then 16+4grp..+3
-#pragma unroll
-      for (int c = 0; c < HC; ++c) {
-        float mx = fmaxf(fmaxf(fmaxf(sc[0][c][0], sc[0][c][1]), fmaxf(sc[0][c][2], sc[0][c][3])),
-                         fmaxf(fmaxf(sc[1][c][0], sc[1][c][1]), fmaxf(sc[1][c][2], sc[1][c][3])));
-        mx = rows_max(mx);  // every row of the tile has key 0 <= its position, or is all -inf
-        if (__ballot(mx > m_ref[c] + kSlack)) {
-          const float m_new = fmaxf(m_ref[c], mx);
-          const float alpha = __builtin_amdgcn_exp2f(m_ref[c] - m_new);
-          l_run[c] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DTILES; ++dt) acc[c][dt] *= alpha;
-          m_ref[c] = m_new;
-        }
-        float p[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(sc[0][c][r] - m_ref[c]);
-          p[4 + r] = __builtin_amdgcn_exp2f(sc[1][c][r] - m_ref[c]);
-        }
-        pb[c] = u32x4{E::pack(p[0], p[1]), E::pack(p[2], p[3]), E::pack(p[4], p[5]),
-                      E::pack(p[6], p[7])};
-        if constexpr (E::kSplitP) {
-          // residuals are exact in fp32; the sum is taken over the full weights
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            pl[c][e] = E::pack(p[2 * e] - E::lo(pb[c][e]), p[2 * e + 1] - E::hi(pb[c][e]));
-          l_run[c] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        } else {
-          // the sum uses the rounded weights the MFMA multiplies with
-          float r = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r += E::lo(pb[c][e]) + E::hi(pb[c][e]);
-          l_run[c] += r;
-        }
-      }
-      // O^T += V^T P^T over the 32 keys, in the key order of pb
-#pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt) {
-        const uint16_t *vr = vl + (dt * 16 + col) * T::vRow + grp * 4;
-        const u32x2 lo = *(const u32x2 *)vr;          // keys 4grp .. +3
-        const u32x2 hi = *(const u32x2 *)(vr + 16);   // keys 16+4grp .. +3
-        const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-        for (int c = 0; c < HC; ++c) {
-          acc[c][dt] = E::mfma(va, pb[c], acc[c][dt]);
-          if constexpr (E::kSplitP) acc[c][dt] = E::mfma(va, pl[c], acc[c][dt]);
-        }
-      }
-    }
-    if (tile + 1 < ntiles) {
-      // The other buffer was last read in the previous iteration, before its
-      // barrier, so it can be filled now; the barrier after makes the fill
-      // visible before anyone reads it (and keeps any wave from refilling
-      // this buffer while another still reads it).
-      stash(buf ^ 1, tile + 1);
-      __syncthreads();
     }
   }
 
   // rows of this lane: token col of the wave, heads c; lane holds dims
   // 16*dt + 4*grp + 0..3
-  float inv[HC];
+  float inv[HW];
 #pragma unroll
-  for (int c = 0; c < HC; ++c) inv[c] = 1.0f / rows_sum(l_run[c]);  // whole wave
+  for (int c = 0; c < HW; ++c) inv[c] = 1.0f / rows_sum(l_run[c]);  // whole wave
   const int row = wt0 + col;
   if (row < n) {
 #pragma unroll
-    for (int c = 0; c < HC; ++c) {
-      const int hg = chunk * HC + c;
+    for (int c = 0; c < HW; ++c) {
+      const int hg = chunk * HC + hgrp * HW + c;
       if (hg >= group) continue;
       uint16_t *op = out + ((int64_t)(q0 + row) * num_heads + kvh * group + hg) * D + grp * 4;
 #pragma unroll
@@ -356,8 +387,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   }
 }
 
-template <int DT, int D, int HC>
+template <int DT, int D, int HW, int NWH>
 int launch_hc(const PrefillArgs &a) {
+  constexpr int HC = HW * NWH;
   const int group = a.num_heads / a.num_kv_heads;
   const int chunks = (group + HC - 1) / HC;
   const int nqb = (a.max_query_len + kQB - 1) / kQB;
@@ -367,20 +399,22 @@ int launch_hc(const PrefillArgs &a) {
   int log2_bs = 0;
   while ((1 << log2_bs) < a.block_size) ++log2_bs;
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-  prefill_kernel<DT, D, HC><<<dim3((unsigned)groups), kThreads, 0, (hipStream_t)a.stream>>>(
-      (uint16_t *)a.out, (const uint16_t *)a.q, (const uint16_t *)a.k_cache,
-      (const uint16_t *)a.v_cache, a.block_tables, a.context_lens, a.query_start, scale_log2,
-      log2_bs, a.num_seqs, a.num_kv_heads, a.num_heads, group, chunks, a.max_blocks_per_seq,
-      a.num_blocks, nqb);
+  const size_t lds = 2 * sizeof(uint16_t) * Tile<D>::elems + sizeof(int32_t) * a.max_blocks_per_seq;
+  prefill_kernel<DT, D, HW, NWH>
+      <<<dim3((unsigned)groups), kWave * kTG * NWH, lds, (hipStream_t)a.stream>>>(
+          (uint16_t *)a.out, (const uint16_t *)a.q, (const uint16_t *)a.k_cache,
+          (const uint16_t *)a.v_cache, a.block_tables, a.context_lens, a.query_start,
+          scale_log2, log2_bs, a.num_seqs, a.num_kv_heads, a.num_heads, group, chunks,
+          a.max_blocks_per_seq, a.num_blocks, nqb);
   return (int)hipGetLastError();
 }
 
 template <int DT, int D>
 int launch_d(const PrefillArgs &a) {
   const int group = a.num_heads / a.num_kv_heads;
-  if (group == 1) return launch_hc<DT, D, 1>(a);
-  if (group == 2) return launch_hc<DT, D, 2>(a);
-  return launch_hc<DT, D, 4>(a);
+  if (group == 1) return launch_hc<DT, D, 1, 1>(a);
+  if (group == 2) return launch_hc<DT, D, 2, 1>(a);
+  return launch_hc<DT, D, 2, 2>(a);
 }
 
 template <int DT>
