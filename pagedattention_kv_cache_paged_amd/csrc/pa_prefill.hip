@@ -27,9 +27,8 @@
 //     MFMA wrote: the k index of both operands runs over the same eight keys
 //     per lane, so no shuffle is needed).
 // Online softmax per (head, token) with a lazily raised reference max, as in
-// decode; bfloat16 weights enter P.V as hi + lo parts (binary16 ones as
-// they are); the causal mask runs only on tiles that reach past a wave's
-// first position.
+// decode; P.V runs in binary16 (see Elem below); the causal mask runs only
+// on tiles that reach past a wave's first position.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,15 +53,18 @@ constexpr int kTG = 4;           // token groups per workgroup
 constexpr int kQB = kQT * kTG;   // query tokens per workgroup
 constexpr int kKT = 32;          // keys per tile
 
+// QK runs in the caches' own 16-bit type; P.V always runs in binary16: the
+// weights lie in [0, 2^8] (the reference max lags by at most kSlack), where
+// binary16 keeps 11 significant bits, and a bfloat16 V tile is converted to
+// binary16 as it is stored to LDS.  That conversion is exact for every
+// bfloat16 value of magnitude 2^-17 .. 65504 (8 significant bits fit in 11),
+// rounds smaller ones by less than 2^-24, and saturates larger ones at
+// +-65504 (round toward zero never overflows).
+// Elem<DT>: the QK product and the output in the caches' type.
 template <int DT>
-struct PElem;
-// kSplitP: bfloat16 weights go in as a hi and a lo part (two MFMAs), so P
-// keeps about 16 significant bits; binary16 weights already carry 11.
+struct Elem;
 template <>
-struct PElem<1> {
-  static constexpr bool kSplitP = true;
-  static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
-  static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+struct Elem<1> {
   static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -73,14 +75,7 @@ struct PElem<1> {
   }
 };
 template <>
-struct PElem<0> {
-  static constexpr bool kSplitP = false;
-  static __device__ __forceinline__ float lo(uint32_t w) {
-    return (float)__builtin_bit_cast(f16x2, w)[0];
-  }
-  static __device__ __forceinline__ float hi(uint32_t w) {
-    return (float)__builtin_bit_cast(f16x2, w)[1];
-  }
+struct Elem<0> {
   static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -90,6 +85,23 @@ struct PElem<0> {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
   }
 };
+
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {  // round to nearest even
+  f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
+// two bfloat16 values -> two binary16 values (toward zero: exact in range,
+// saturating beyond it)
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16),
+                                                                 __uint_as_float(w & 0xffff0000u)));
+}
 
 __device__ __forceinline__ float rows_max(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -105,14 +117,15 @@ __device__ __forceinline__ float rows_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// LDS tile layouts (16-bit elements), rows padded by 16 bytes so that the
-// 16 rows one MFMA operand reads fall in different banks:
+// LDS tile layouts (16-bit elements), rows padded so that the 16 rows one
+// MFMA operand reads spread over the banks:
 //   K tile [32 keys][D + 8]  (token-major, as in the cache)
-//   V tile [D][32 + 8]       (dim-major, as in the cache)
+//   V tile [D][32 + 12]      (dim-major, as in the cache; a 22-dword row
+//                             measured fastest of the 8-byte-aligned paddings)
 template <int D>
 struct Tile {
   static constexpr int kRow = D + 8;        // K row, in elements
-  static constexpr int vRow = kKT + 8;      // V row, in elements
+  static constexpr int vRow = kKT + 12;     // V row, in elements
   static constexpr int kElems = kKT * kRow;
   static constexpr int vElems = D * vRow;
   static constexpr int elems = kElems + vElems;
@@ -131,7 +144,7 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
     const int32_t *__restrict__ query_start, float scale_log2, int log2_bs, int num_seqs,
     int num_kv_heads, int num_heads, int group, int chunks, int max_blocks,
     int64_t num_blocks, int nqb) {
-  using E = PElem<DT>;
+  using E = Elem<DT>;
   constexpr int HC = HW * NWH;     // query heads per workgroup
   constexpr int kThreads = kWave * kTG * NWH;
   constexpr int KSTEPS = D / 32;   // 16x16x32 MFMAs per QK product
@@ -192,11 +205,19 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
   }
 
   // Tile loads: a tile is 4*D 16-byte pieces of K (piece p: key p / (D/8),
-  // dims 8*(p % (D/8)) ..) and 4*D of V (piece p: dim p / 4, keys 8*(p%4) ..);
-  // lane tid moves pieces tid + 256*j of each, j < D/64.
+  // dims 8*(p % (D/8)) ..) and 4*D of V (piece p: keys 8*(p / D) .. +7 of
+  // dim p % D).  Wave w's load j moves pieces w*64 + j*threads .. +63 of each:
+  // 64 / (D/8) whole K rows, or 64 dims of one key octet, so every piece of
+  // one load lies in one cache block (blocks hold at least 8 tokens).  The
+  // block base is then a scalar and each lane adds a fixed offset.
   constexpr int KPR = D / 8;  // 16-byte pieces per K row
   constexpr int NP = (4 * D + kThreads - 1) / kThreads;  // pieces of each cache per lane
   constexpr bool kAllLoad = NP * kThreads == 4 * D;       // every lane has NP pieces
+  constexpr int KPL = kWave / KPR;  // keys per K load (4 at D = 128, 8 at D = 64)
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const uint32_t koff = (uint32_t)((lane / KPR) * D + (lane % KPR) * 8) * 2;  // bytes
+  const uint32_t voff = (uint32_t)(lane * bs) * 2;
+  const int64_t blk_bytes = blk_stride * 2;
   // A ring of kStages register stages: a tile's loads are issued
   // kStages - 1 tiles before they go into LDS, so the wait for them is
   // covered by that many tiles of compute.
@@ -205,22 +226,23 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
   auto fetch = [&](int stage, int tile) {
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
-      const int p = min(tid + j * kThreads, 4 * D - 1);
-      const int key = p / KPR;
-      const int t = min(tile * kKT + key, wg_hi);  // past the rows' reach: any seen token
-      const int64_t bb = tbl_lds[t >> log2_bs];
-      st_k[stage][j] = __builtin_nontemporal_load(
-          (const u32x4 *)(kbase + bb * blk_stride + (int64_t)(t & (bs - 1)) * D + (p % KPR) * 8));
+      const int pw = min(wv * kWave + j * kThreads, 4 * D - kWave);  // first piece (uniform)
+      // the load's keys; past the rows' reach it rereads the group of the
+      // last key seen (same block, in bounds)
+      const int key0 = min(tile * kKT + pw / KPR, wg_hi & ~(KPL - 1));
+      const int blk = __builtin_amdgcn_readfirstlane(tbl_lds[key0 >> log2_bs]);
+      const char *src = reinterpret_cast<const char *>(kbase) + blk * blk_bytes +
+                        (int64_t)((key0 & (bs - 1)) * D * 2);
+      st_k[stage][j] = __builtin_nontemporal_load((const u32x4 *)(src + koff));
     }
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
-      const int p = min(tid + j * kThreads, 4 * D - 1);
-      const int d = p / 4;
-      const int k8 = (p % 4) * 8;
-      const int t = min(tile * kKT + k8, wg_hi & ~7);
-      const int64_t bb = tbl_lds[t >> log2_bs];
-      st_v[stage][j] = __builtin_nontemporal_load(
-          (const u32x4 *)(vbase + bb * blk_stride + (int64_t)d * bs + (t & (bs - 1))));
+      const int pw = min(wv * kWave + j * kThreads, 4 * D - kWave);
+      const int key0 = min(tile * kKT + (pw / D) * 8, wg_hi & ~7);  // the load's key octet
+      const int blk = __builtin_amdgcn_readfirstlane(tbl_lds[key0 >> log2_bs]);
+      const char *src = reinterpret_cast<const char *>(vbase) + blk * blk_bytes +
+                        (int64_t)(((pw % D) * bs + (key0 & (bs - 1))) * 2);
+      st_v[stage][j] = __builtin_nontemporal_load((const u32x4 *)(src + voff));
     }
   };
   // Into LDS; V of keys past the workgroup's last position is zeroed there
@@ -230,11 +252,17 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
     uint16_t *vl = kl + T::kElems;
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
-      const int p = tid + j * kThreads;
-      if (!kAllLoad && p >= 4 * D) break;
+      const int pw = wv * kWave + j * kThreads;
+      if (!kAllLoad && pw >= 4 * D) break;
+      const int p = pw + lane;
       *(u32x4 *)(kl + (p / KPR) * T::kRow + (p % KPR) * 8) = st_k[stage][j];
-      const int valid = wg_hi + 1 - (tile * kKT + (p % 4) * 8);  // keys the rows can see
+      const int k8 = (pw / D) * 8;
+      const int valid = wg_hi + 1 - (tile * kKT + k8);  // keys the rows can see
       u32x4 v = st_v[stage][j];
+      if constexpr (DT == 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
+      }
       if (valid < 8) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -242,7 +270,12 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
           v[e] &= c >= 2 ? 0xffffffffu : (c == 1 ? 0x0000ffffu : 0u);
         }
       }
-      *(u32x4 *)(vl + (p / 4) * T::vRow + (p % 4) * 8) = v;
+      if constexpr ((T::vRow * 2) % 16 == 0) {
+        *(u32x4 *)(vl + (p % D) * T::vRow + k8) = v;
+      } else {
+        *(u32x2 *)(vl + (p % D) * T::vRow + k8) = u32x2{v.x, v.y};
+        *(u32x2 *)(vl + (p % D) * T::vRow + k8 + 4) = u32x2{v.z, v.w};
+      }
     }
   };
 
@@ -302,7 +335,7 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
                 for (int c = 0; c < HW; ++c) sc[rb][c][r] = ok ? sc[rb][c][r] : -INFINITY;
               }
           }
-          u32x4 pb[HW], pl[HW];  // P^T as the B operand: keys 4grp..+3 then 16+4grp..+3
+          u32x4 pb[HW];  // P^T as the B operand: keys 4grp..+3 then 16+4grp..+3
     #pragma unroll
           for (int c = 0; c < HW; ++c) {
             float mx = fmaxf(fmaxf(fmaxf(sc[0][c][0], sc[0][c][1]), fmaxf(sc[0][c][2], sc[0][c][3])),
@@ -322,21 +355,12 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
               p[r] = __builtin_amdgcn_exp2f(fmaf(sc[0][c][r], scale_log2, -m_ref[c]));
               p[4 + r] = __builtin_amdgcn_exp2f(fmaf(sc[1][c][r], scale_log2, -m_ref[c]));
             }
-            pb[c] = u32x4{E::pack(p[0], p[1]), E::pack(p[2], p[3]), E::pack(p[4], p[5]),
-                          E::pack(p[6], p[7])};
-            if constexpr (E::kSplitP) {
-              // residuals are exact in fp32; the sum is taken over the full weights
-    #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                pl[c][e] = E::pack(p[2 * e] - E::lo(pb[c][e]), p[2 * e + 1] - E::hi(pb[c][e]));
-              l_run[c] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-            } else {
-              // the sum uses the rounded weights the MFMA multiplies with
-              float r = 0.f;
-    #pragma unroll
-              for (int e = 0; e < 4; ++e) r += E::lo(pb[c][e]) + E::hi(pb[c][e]);
-              l_run[c] += r;
-            }
+            pb[c] = u32x4{pack_f16(p[0], p[1]), pack_f16(p[2], p[3]), pack_f16(p[4], p[5]),
+                          pack_f16(p[6], p[7])};
+            // the sum uses the rounded weights the MFMA multiplies with, so each
+            // output row is a convex combination of V rows
+            l_run[c] += ((f16_lo(pb[c][0]) + f16_hi(pb[c][0])) + (f16_lo(pb[c][1]) + f16_hi(pb[c][1]))) +
+                        ((f16_lo(pb[c][2]) + f16_hi(pb[c][2])) + (f16_lo(pb[c][3]) + f16_hi(pb[c][3])));
           }
           // O^T += V^T P^T over the 32 keys, in the key order of pb
     #pragma unroll
@@ -346,10 +370,7 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
             const u32x2 hi = *(const u32x2 *)(vr + 16);   // keys 16+4grp .. +3
             const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
     #pragma unroll
-            for (int c = 0; c < HW; ++c) {
-              acc[c][dt] = E::mfma(va, pb[c], acc[c][dt]);
-              if constexpr (E::kSplitP) acc[c][dt] = E::mfma(va, pl[c], acc[c][dt]);
-            }
+            for (int c = 0; c < HW; ++c) acc[c][dt] = mfma_f16(va, pb[c], acc[c][dt]);
           }
         }
         if (tile + 1 < ntiles) {

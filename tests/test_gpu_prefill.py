@@ -35,9 +35,12 @@ def dev_bits(bits, dtype):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(TD[dtype])
 
 
-def run(lengths, chunks, G, hkv, d, bs, dtype, seed, rows=None):
+def run(lengths, chunks, G, hkv, d, bs, dtype, seed, rows=None, v_scale=None):
     w = W.build("pf", lengths, num_heads=G * hkv, num_kv_heads=hkv, head_dim=d,
                 block_size=bs, dtype=dtype, seed=seed)
+    if v_scale is not None:  # V values times v_scale, kept inside +-65000
+        v = np.clip(f64(w.token_v, dtype) * v_scale, -65000.0, 65000.0)
+        w.token_v = W.to_bits(v.astype(np.float32), dtype).reshape(w.token_v.shape)
     ksh, vsh = w.cache_shapes()
     nan = int(np.array([W.NAN_BITS[dtype]], np.uint16).view(np.int16)[0])
     kc = torch.full(ksh, nan, dtype=torch.int16, device=DEV).view(TD[dtype])
@@ -76,11 +79,11 @@ def run(lengths, chunks, G, hkv, d, bs, dtype, seed, rows=None):
     return got[rows], ref, None
 
 
-def check(got, ref, dtype, what):
+def check(got, ref, dtype, what, atol=ATOL):
     g = f64(got, dtype)
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
     err = np.abs(g - ref)
-    bad = ~(err <= ATOL + RTOL * np.abs(ref))
+    bad = ~(err <= atol + RTOL * np.abs(ref))
     say(f"  {what} max_abs={err.max():.3e} n={ref.size}")
     assert not bad.any(), f"{what}: {bad.sum()} out of tolerance, worst {err[bad].max():.3e}"
 
@@ -116,6 +119,18 @@ def test_prefill_llama8b_chunks():
     rows = np.sort(g.choice(4 * 512, 48, replace=False))
     got, ref, _ = run([2048] * 4, [512] * 4, 4, 8, 128, 16, W.BF16, 55, rows=rows)
     check(got, ref, W.BF16, "llama8b chunks")
+
+
+@pytest.mark.parametrize("log2s", [14, -20])
+def test_prefill_bf16_v_range(log2s):
+    """bfloat16 V runs through binary16 in P.V: V scaled by 2^14 (values up to
+    about 65000, converted exactly) keeps the tolerance in units of V's
+    scale; V scaled by 2^-20 (binary16 subnormals, rounded by < 2^-24) keeps
+    the absolute one."""
+    s = 2.0 ** log2s
+    got, ref, _ = run([300, 77, 129], [300, 40, 1], 4, 2, 128, 16, W.BF16, 91 + log2s,
+                      v_scale=s)
+    check(got, ref, W.BF16, f"v x 2^{log2s}", atol=ATOL * max(s, 1.0))
 
 
 def test_prefill_leaves_other_rows():
