@@ -254,8 +254,12 @@ int paged_attention_decode_append(void *out, const void *q, const void *k_new,
  * max_query_len: host bound on every n_s (it sizes the grid; rows of a
  * longer chunk are not computed); 0 is a no-op.  A sequence with n_s > L
  * gets no rows written.  scale > 0 and max_blocks_per_seq <= 4096 (a
- * workgroup keeps its sequence's block ids on chip), else PA_ERR_SHAPE.  No workspace; out rows
- * of the chunks are the only writes.  Asynchronous on `stream`.
+ * workgroup keeps its sequence's block ids on chip), else PA_ERR_SHAPE.
+ * Numerics: scores and the softmax in fp32; P.V in binary16 weights times
+ * binary16 V with fp32 accumulation.  With bfloat16 caches, V is converted
+ * to binary16 on chip: exact for magnitudes 2^-17 .. 65504, rounded by less
+ * than 2^-24 below, saturated at +-65504 above.  No workspace; out rows of
+ * the chunks are the only writes.  Asynchronous on `stream`.
  */
 int paged_attention_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
                             const int32_t *block_tables, const int32_t *context_lens,
