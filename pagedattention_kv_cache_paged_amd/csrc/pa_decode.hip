@@ -583,28 +583,49 @@ __global__ __launch_bounds__(kWave) void decode_merge_append_kernel(
   uint16_t *op = out + ((int64_t)seq * num_heads + head) * D + lane * PER;
   const int n_tiles = ws_cu[num_seqs];
   const int c0 = ws_cu[seq], c1 = ws_cu[seq + 1];
-  // Running combination: M the max so far (log2 units), den = sum c_p,
-  // num = sum c_p o_p, with c_p = l_p * 2^(m_p - M).
-  float big = -INFINITY, den = 0.f;
-  float num[PER];
+  const int len = min(max(context_lens[seq], 0), max_blocks * block_size);
+  const int kvh = head / group;
+  // Every load that does not depend on another is issued here, before any
+  // branch, so the kernel waits on one round trip instead of a chain: the
+  // q / k_new / v_new rows, the new token's table entry and the first
+  // partial.  All stay in bounds for any lengths (the table index is
+  // clamped to the sequence's row; the partial index to the head's slots).
+  const int64_t src = ((int64_t)seq * num_kv_heads + kvh) * D + lane * PER;
+  uint32_t qc[PER], kc[PER], vc[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) num[i] = 0.f;
+  for (int i = 0; i < PER; ++i) {
+    qc[i] = q[((int64_t)seq * num_heads + head) * D + lane * PER + i];
+    kc[i] = k_new[src + i];
+    vc[i] = v_new[src + i];
+  }
+  const int pos = max(len, 1) - 1;  // the new token's position
+  const int64_t blk = block_tables[(int64_t)seq * max_blocks + pos / block_size];
+  const int nt = max(n_tiles, 1);
+  const int wv = max(min(waves, n_tiles), 1);  // as in the split pass: all ranges non-empty
+  const int jf = wave_of(c0, nt, wv);
+  const int64_t base = (int64_t)head * slots + jf + seq;
+  const f32x2 *ml = (const f32x2 *)(ws_ml + base * 2);
+  const float *o = ws_o + base * D + lane * PER;
+  const f32x2 ml0 = ml[0];
+  float o0[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o0[i] = o[i];
+
+  if (len == 0) {  // nothing to attend and nothing to append
+    if constexpr (PER == 2) *(uint32_t *)op = 0u;
+    else op[0] = 0;
+    return;
+  }
+  // The new token opens the running combination: M the max so far (log2
+  // units), den = sum c_p, num = sum c_p o_p, with c_p = l_p * 2^(m_p - M);
+  // the new token enters with m = its score, l = 1, o = V.
+  float big, den = 1.f;
+  float num[PER];
   {
-    const int len = min(max(context_lens[seq], 0), max_blocks * block_size);
-    if (len == 0) {  // nothing to attend and nothing to append
-      if constexpr (PER == 2) *(uint32_t *)op = 0u;
-      else op[0] = 0;
-      return;
-    }
-    const int kvh = head / group;
-    const int64_t src = ((int64_t)seq * num_kv_heads + kvh) * D + lane * PER;
     float qe[PER], ke[PER], ve[PER];
-    uint32_t kc[PER], vc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      qe[i] = elem_to_float<DT>(q[((int64_t)seq * num_heads + head) * D + lane * PER + i]);
-      kc[i] = k_new[src + i];
-      vc[i] = v_new[src + i];
+      qe[i] = elem_to_float<DT>(qc[i]);
       if constexpr (KV8) {
         kc[i] = e4m3_code(elem_to_float<DT>(kc[i]) * k_inv);
         vc[i] = e4m3_code(elem_to_float<DT>(vc[i]) * v_inv);
@@ -619,65 +640,56 @@ __global__ __launch_bounds__(kWave) void decode_merge_append_kernel(
 #pragma unroll
     for (int i = 0; i < PER; ++i) dot = fmaf(qe[i], ke[i], dot);
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
-    big = dot * scale_log2;  // the new token: m = its score, l = 1, o = V
-    den = 1.f;
+    for (int m = kWave / 2; m > 0; m >>= 1) dot += __shfl_xor(dot, m);
+    big = dot * scale_log2;
 #pragma unroll
     for (int i = 0; i < PER; ++i) num[i] = ve[i];
-    if (head % group == 0) {  // one writer per KV head
-      const int pos = len - 1;
-      const int64_t blk = block_tables[(int64_t)seq * max_blocks + pos / block_size];
-      if (blk >= 0 && blk < num_blocks) {
-        const int64_t bh = blk * num_kv_heads + kvh;
-        const int off = pos % block_size;
-        const int d0 = lane * PER;
-        if constexpr (KV8) {
-          uint8_t *kd = (uint8_t *)k_cache + (bh * block_size + off) * D + d0;
-          uint8_t *vd = (uint8_t *)v_cache + (bh * D + d0) * block_size + off;
+    if (head % group == 0 && blk >= 0 && blk < num_blocks) {  // one writer per KV head
+      const int64_t bh = blk * num_kv_heads + kvh;
+      const int off = pos % block_size;
+      const int d0 = lane * PER;
+      if constexpr (KV8) {
+        uint8_t *kd = (uint8_t *)k_cache + (bh * block_size + off) * D + d0;
+        uint8_t *vd = (uint8_t *)v_cache + (bh * D + d0) * block_size + off;
 #pragma unroll
-          for (int i = 0; i < PER; ++i) {
-            kd[i] = (uint8_t)kc[i];
-            vd[i * block_size] = (uint8_t)vc[i];
-          }
-        } else {
-          uint16_t *kd = (uint16_t *)k_cache + (bh * block_size + off) * D + d0;
-          uint16_t *vd = (uint16_t *)v_cache + (bh * D + d0) * block_size + off;
+        for (int i = 0; i < PER; ++i) {
+          kd[i] = (uint8_t)kc[i];
+          vd[i * block_size] = (uint8_t)vc[i];
+        }
+      } else {
+        uint16_t *kd = (uint16_t *)k_cache + (bh * block_size + off) * D + d0;
+        uint16_t *vd = (uint16_t *)v_cache + (bh * D + d0) * block_size + off;
 #pragma unroll
-          for (int i = 0; i < PER; ++i) {
-            kd[i] = (uint16_t)kc[i];
-            vd[i * block_size] = (uint16_t)vc[i];
-          }
+        for (int i = 0; i < PER; ++i) {
+          kd[i] = (uint16_t)kc[i];
+          vd[i * block_size] = (uint16_t)vc[i];
         }
       }
     }
-    if (c1 <= c0) goto done;  // the new token is the whole context
   }
-  {
-    const int wv = min(waves, n_tiles);  // as in the split pass: all ranges non-empty
-    const int jf = wave_of(c0, n_tiles, wv);
-    const int jl = wave_of(c1 - 1, n_tiles, wv);
-    const int np = jl - jf + 1;
-    const int64_t base = (int64_t)head * slots + jf + seq;
-    const f32x2 *ml = (const f32x2 *)(ws_ml + base * 2);
-    const float *o = ws_o + base * D + lane * PER;
+  if (c1 > c0) {  // the partials of positions 0 .. L-2 (none when the new token is all)
+    const int np = wave_of(c1 - 1, nt, wv) - jf + 1;
     // One pass with a running maximum, so each partial's (m, l) and o are
-    // loaded together: c_p = l_p * 2^(m_p - M) rescaled as M grows.
-#pragma unroll 4
-    for (int p = 0; p < np; ++p) {
-      const f32x2 v = ml[p];
-      float opv[PER];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) opv[i] = o[(int64_t)p * D + i];
+    // used together: c_p = l_p * 2^(m_p - M) rescaled as M grows.
+    auto combine = [&](f32x2 v, const float (&opv)[PER]) {
       const float m_new = fmaxf(big, v.x);
-      const float a = __builtin_amdgcn_exp2f(big - m_new);  // 0 while nothing is held
+      const float a = __builtin_amdgcn_exp2f(big - m_new);
       const float c = v.y * __builtin_amdgcn_exp2f(v.x - m_new);
       den = den * a + c;
 #pragma unroll
       for (int i = 0; i < PER; ++i) num[i] = num[i] * a + c * opv[i];
       big = m_new;
+    };
+    combine(ml0, o0);
+#pragma unroll 4
+    for (int p = 1; p < np; ++p) {
+      const f32x2 v = ml[p];
+      float opv[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) opv[i] = o[(int64_t)p * D + i];
+      combine(v, opv);
     }
   }
-done:
   const float inv = 1.0f / den;
   if constexpr (PER == 2) {
     *(uint32_t *)op = E::pack(num[0] * inv, num[1] * inv);
