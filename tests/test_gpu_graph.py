@@ -1,0 +1,119 @@
+"""The decode step and the chunked prefill under HIP graph capture.
+
+A serving loop replays a captured step instead of launching its kernels one
+by one.  The library allocates nothing, records no memset, and takes the
+caller's stream and workspace, so its launches can be captured.  Each graph
+here is replayed several times, with new query values copied into its
+static inputs and with eager work between the replays; every replay must
+equal the same call made eagerly on the same inputs, bit for bit (outputs
+and caches)."""
+import numpy as np
+import pytest
+import torch
+
+from pagedattention_kv_cache_paged_amd import binding as B
+from pagedattention_kv_cache_paged_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def dev_bits(bits, tdt):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(tdt)
+
+
+def filled_caches(w, tdt):
+    ksh, vsh = w.cache_shapes()
+    kc = torch.zeros(ksh, dtype=tdt, device=DEV)
+    vc = torch.zeros(vsh, dtype=tdt, device=DEV)
+    k, v, s = w.write_batch("hist")
+    B.paged_kv_write(dev_bits(k, tdt), dev_bits(v, tdt), torch.from_numpy(s).to(DEV), kc, vc)
+    return kc, vc
+
+
+def test_fused_decode_step_graph_replay():
+    w = W.build("graph", list(np.random.default_rng(5).integers(1, 700, size=24)),
+                num_heads=16, num_kv_heads=4, head_dim=128, block_size=16, dtype=W.BF16,
+                seed=17)
+    tdt = torch.bfloat16
+    nk, nv, _ = w.write_batch("new")
+    k_new, v_new = dev_bits(nk, tdt), dev_bits(nv, tdt)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    cl = torch.from_numpy(w.context_lens).to(DEV)
+    need = B.workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                             w.max_blocks_per_seq, w.block_size)
+    ws_graph = torch.empty(need, dtype=torch.uint8, device=DEV)
+    ws_eager = torch.empty(need, dtype=torch.uint8, device=DEV)
+    kc_g, vc_g = filled_caches(w, tdt)
+    kc_e, vc_e = filled_caches(w, tdt)
+    q = dev_bits(w.q, tdt)
+    out = torch.empty_like(q)
+
+    def step(o, kc, vc, ws):
+        B.paged_attention_decode_append(o, q, k_new, v_new, kc, vc, bt, cl, w.scale,
+                                        w.block_size, w.num_kv_heads, workspace_tensor=ws)
+
+    step(out, kc_g, vc_g, ws_graph)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(out, kc_g, vc_g, ws_graph)
+    gen = torch.Generator(device="cpu").manual_seed(3)
+    for r in range(4):
+        say(f"graph replay {r}")
+        q.copy_(torch.randn(q.shape, generator=gen).to(tdt).to(DEV))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = torch.empty_like(out)
+        step(ref, kc_e, vc_e, ws_eager)  # eager work between replays, and the reference
+        junk = torch.empty_like(out)
+        step(junk, kc_e, vc_e, ws_graph)  # eager use of the graph's own workspace
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {r}"
+        assert torch.equal(kc_g.view(torch.int16), kc_e.view(torch.int16))
+        assert torch.equal(vc_g.view(torch.int16), vc_e.view(torch.int16))
+
+
+def test_prefill_graph_replay():
+    lengths, chunks = [300, 97, 512, 40], [300, 33, 128, 1]
+    w = W.build("graphpf", lengths, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                dtype=W.F16, seed=23)
+    tdt = torch.float16
+    ksh, vsh = w.cache_shapes()
+    kc = torch.zeros(ksh, dtype=tdt, device=DEV)
+    vc = torch.zeros(vsh, dtype=tdt, device=DEV)
+    for which in ("hist", "new"):
+        k, v, s = w.write_batch(which)
+        B.paged_kv_write(dev_bits(k, tdt), dev_bits(v, tdt), torch.from_numpy(s).to(DEV), kc, vc)
+    qs = torch.tensor(np.concatenate([[0], np.cumsum(chunks)]), dtype=torch.int32, device=DEV)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    cl = torch.from_numpy(w.context_lens).to(DEV)
+    rows = int(sum(chunks))
+    q = torch.zeros(rows, 8, 128, dtype=tdt, device=DEV)
+    out = torch.empty_like(q)
+
+    def call(o):
+        B.paged_attention_prefill(o, q, kc, vc, bt, cl, qs, w.scale, 16, 2, max(chunks))
+
+    call(out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out)
+    gen = torch.Generator(device="cpu").manual_seed(4)
+    for r in range(4):
+        say(f"prefill graph replay {r}")
+        q.copy_(torch.randn(q.shape, generator=gen).to(tdt).to(DEV))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = torch.empty_like(out)
+        call(ref)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {r}"
