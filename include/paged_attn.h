@@ -281,6 +281,17 @@ int paged_validate_metadata(const int32_t *block_tables, const int32_t *context_
                             int32_t block_size, int64_t num_blocks,
                             const int64_t *slot_mapping, int64_t num_tokens);
 
+/*
+ * Host-side check of chunked-prefill metadata (host pointers), the device
+ * contract paged_attention_prefill does not check: query_start[0] == 0,
+ * non-decreasing, query_start[num_seqs] <= total_rows (the rows of q and
+ * out); every chunk length n_s at most max_query_len and at most its context
+ * length context_lens[s].  Returns PA_OK, PA_ERR_METADATA on a violation,
+ * PA_ERR_NULL / PA_ERR_SHAPE for bad arguments.
+ */
+int paged_validate_prefill(const int32_t *query_start, const int32_t *context_lens,
+                           int32_t num_seqs, int32_t max_query_len, int64_t total_rows);
+
 #ifdef __cplusplus
 }
 #endif

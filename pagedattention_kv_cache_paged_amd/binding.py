@@ -109,6 +109,8 @@ def load() -> ctypes.CDLL:
     lib.paged_validate_copy_pairs.argtypes = [p, i64, i64]
     lib.paged_validate_metadata.restype = ctypes.c_int
     lib.paged_validate_metadata.argtypes = [p, p, i32, i32, i32, i64, p, i64]
+    lib.paged_validate_prefill.restype = ctypes.c_int
+    lib.paged_validate_prefill.argtypes = [p, p, i32, i32, i64]
     _lib = lib
     return lib
 
@@ -245,6 +247,18 @@ def validate_metadata(block_tables, context_lens, block_size: int, num_blocks: i
     return int(load().paged_validate_metadata(
         bt.ctypes.data, cl.ctypes.data, cl.size, bt.shape[1], block_size, num_blocks,
         None if sm is None else sm.ctypes.data, 0 if sm is None else sm.size))
+
+
+def validate_prefill(query_start, context_lens, max_query_len: int, total_rows: int) -> int:
+    """Host check of chunked-prefill offsets against the context lengths
+    (numpy or CPU tensors); returns the library's code (0 = valid)."""
+    import numpy as np
+    qs = np.ascontiguousarray(np.asarray(query_start), dtype=np.int32)
+    cl = np.ascontiguousarray(np.asarray(context_lens), dtype=np.int32)
+    if qs.size != cl.size + 1:
+        raise ValueError("query_start must hold num_seqs + 1 offsets")
+    return int(load().paged_validate_prefill(qs.ctypes.data, cl.ctypes.data, cl.size,
+                                             max_query_len, total_rows))
 
 
 # ---- FP8 (E4M3) caches -----------------------------------------------------

@@ -74,7 +74,7 @@ bool decode_sizes_ok(int32_t num_seqs, int32_t num_kv_heads, int32_t num_heads,
 
 extern "C" {
 
-int pa_abi_version(void) { return 4; }
+int pa_abi_version(void) { return 5; }
 
 const char *pa_strerror(int code) {
   switch (code) {
@@ -312,6 +312,18 @@ int paged_validate_metadata(const int32_t *block_tables, const int32_t *context_
     }
   }
   return PA_OK;
+}
+
+int paged_validate_prefill(const int32_t *query_start, const int32_t *context_lens,
+                           int32_t num_seqs, int32_t max_query_len, int64_t total_rows) {
+  if (num_seqs < 0 || max_query_len < 0 || total_rows < 0) return PA_ERR_SHAPE;
+  if (!query_start || (num_seqs > 0 && !context_lens)) return PA_ERR_NULL;
+  if (query_start[0] != 0) return PA_ERR_METADATA;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t n = (int64_t)query_start[s + 1] - query_start[s];
+    if (n < 0 || n > max_query_len || n > (int64_t)context_lens[s]) return PA_ERR_METADATA;
+  }
+  return (int64_t)query_start[num_seqs] <= total_rows ? PA_OK : PA_ERR_METADATA;
 }
 
 }  // extern "C"

@@ -31,10 +31,11 @@ def test_library_exports_every_declared_symbol():
             "paged_attention_decode_stages", "paged_attention_workspace_bytes",
             "paged_attention_split_waves", "paged_validate_metadata", "pa_strerror",
             "pa_abi_version", "paged_kv_write_fp8", "paged_attention_decode_fp8",
-            "paged_attention_decode_append"} <= set(names)
+            "paged_attention_decode_append", "paged_attention_prefill",
+            "paged_validate_prefill"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 4
+    assert lib.pa_abi_version() == 5
 
 
 def test_single_hip_runtime():
@@ -226,3 +227,54 @@ def test_append_binding_checks_shapes():
     q = torch.zeros(2, 4, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         B.paged_attention_decode_append(q, q, q, q, q, q, q, q, 0.1, 16, 2)
+
+
+def _prefill(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, scale=0.125, bs=16,
+             hkv=8, B=4, hq=32, d=128, mb=128, nb=1000, dtype=1, mq=512, stream=None)
+    a.update(kw)
+    return B.load().paged_attention_prefill(
+        a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["qs"], a["scale"], a["bs"],
+        a["hkv"], a["B"], a["hq"], a["d"], a["mb"], a["nb"], a["dtype"], a["mq"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -2),
+    (dict(d=96), -3), (dict(bs=12), -3), (dict(hq=30), -3), (dict(B=-1), -3),
+    (dict(scale=0.0), -3), (dict(scale=-0.125), -3), (dict(scale=float("nan")), -3),
+    (dict(scale=float("inf")), -3),
+    (dict(mb=4097), -3),                 # block ids of a sequence live on chip: at most 4096
+    (dict(mq=-1), -3), (dict(mq=128 * 16 + 1), -3),   # longer than any context
+    (dict(nb=0), -3),
+    (dict(out=None), -1), (dict(qs=None), -1), (dict(bt=None), -1),
+    (dict(q=FAKE + 8), -7), (dict(out=FAKE + 4), -7), (dict(qs=FAKE + 2), -7),
+])
+def test_prefill_rejects_before_launch(kw, code):
+    assert _prefill(**kw) == code
+
+
+def test_prefill_empty_is_noop():
+    assert _prefill(B=0, out=None, q=None) == 0
+    assert _prefill(mq=0, out=None, q=None) == 0
+
+
+@pytest.mark.parametrize("qs,cl,mq,rows,code", [
+    ([0, 3, 3, 10], [5, 1, 7], 7, 10, 0),          # an empty chunk in the middle
+    ([0, 3, 3, 10], [5, 1, 7], 7, 12, 0),          # q may hold more rows
+    ([0, 3, 3, 10], [5, 1, 7], 6, 10, -6),         # chunk of 7 > max_query_len
+    ([0, 3, 3, 10], [5, 1, 6], 7, 10, -6),         # chunk longer than its context
+    ([1, 3, 3, 10], [5, 1, 7], 7, 10, -6),         # must start at 0
+    ([0, 3, 2, 10], [5, 1, 8], 8, 10, -6),         # decreasing
+    ([0, 3, 3, 10], [5, 1, 7], 7, 9, -6),          # rows past q
+    ([0], [], 0, 0, 0),                            # no sequences
+])
+def test_validate_prefill(qs, cl, mq, rows, code):
+    assert B.validate_prefill(np.array(qs), np.array(cl), mq, rows) == code
+
+
+def test_validate_prefill_shape_errors():
+    lib = B.load()
+    assert lib.paged_validate_prefill(None, None, 1, 4, 4) == -1
+    assert lib.paged_validate_prefill(FAKE, FAKE, -1, 4, 4) == -3
+    with pytest.raises(ValueError):
+        B.validate_prefill(np.array([0, 1]), np.array([1, 1]), 1, 1)
