@@ -35,9 +35,9 @@ def dev_bits(bits, dtype):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(TD[dtype])
 
 
-def run(lengths, chunks, G, hkv, d, bs, dtype, seed, rows=None, v_scale=None):
+def run(lengths, chunks, G, hkv, d, bs, dtype, seed, rows=None, v_scale=None, **wkw):
     w = W.build("pf", lengths, num_heads=G * hkv, num_kv_heads=hkv, head_dim=d,
-                block_size=bs, dtype=dtype, seed=seed)
+                block_size=bs, dtype=dtype, seed=seed, **wkw)
     if v_scale is not None:  # V values times v_scale, kept inside +-65000
         v = np.clip(f64(w.token_v, dtype) * v_scale, -65000.0, 65000.0)
         w.token_v = W.to_bits(v.astype(np.float32), dtype).reshape(w.token_v.shape)
@@ -119,6 +119,17 @@ def test_prefill_llama8b_chunks():
     rows = np.sort(g.choice(4 * 512, 48, replace=False))
     got, ref, _ = run([2048] * 4, [512] * 4, 4, 8, 128, 16, W.BF16, 55, rows=rows)
     check(got, ref, W.BF16, "llama8b chunks")
+
+
+def test_prefill_table_at_limit():
+    """A 32768-token context at block size 8 fills the 4096 block ids a
+    workgroup keeps on chip; a 70-row chunk at its end (sampled rows) and a
+    short whole prompt beside it."""
+    g = np.random.default_rng(8)
+    rows = np.sort(np.concatenate([g.choice(70, 10, replace=False), [70, 71, 75]]))
+    got, ref, _ = run([32768, 6], [70, 6], 2, 1, 64, 8, W.F16, 31, rows=rows,
+                      max_blocks_per_seq=4096)
+    check(got, ref, W.F16, "table at limit")
 
 
 @pytest.mark.parametrize("log2s", [14, -20])
