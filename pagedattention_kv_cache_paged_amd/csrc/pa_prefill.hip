@@ -13,17 +13,18 @@
 //   workgroup = (64 query tokens of one sequence) x (up to 4 query heads of
 //   one KV head); waves of 16 tokens x up to 2 heads (at most 32 query rows,
 //   under 256 registers, two waves per SIMD).
-//   The workgroup walks the keys 0 .. its last position in tiles of 32: K
-//   and V tiles go through double-buffered LDS (the lanes move 16-byte
-//   pieces), so a tile is read from memory once per 64 tokens x 4 heads.
+//   The workgroup walks the keys 0 .. its last position in tiles of 64 (one
+//   barrier, one max reduction and one round of staging per 64 keys): K and
+//   V tiles go through double-buffered LDS (the lanes move 16-byte pieces),
+//   so a tile is read from memory once per 64 tokens x 4 heads.
 //   Workgroups run heaviest-first (last query block first) and the blocks of
 //   one (sequence, KV head) land on one XCD, sharing its L2.
-// Per wave and 32-key tile, with q held in registers as the B operand:
-//   S^T[32 keys x 16 tokens] per head = K[keys x D] q^T  (16x16x32 MFMAs,
-//     A = K rows from LDS), so lane (token l%16, quarter l/16) holds the
-//     scores of keys 4*(l/16)+r and 16+4*(l/16)+r;
-//   O^T[D x 16 tokens] += V^T[D x 32 keys] P^T  (16x16x32 MFMAs over the 32
-//     keys, A = the dim-major V tile from LDS, B = P in the registers the QK
+// Per wave and 64-key tile, with q held in registers as the B operand:
+//   S^T[64 keys x 16 tokens] per head = K[keys x D] q^T  (16x16x32 MFMAs, A =
+//     K rows from LDS, four 16-key row blocks), so lane (token l%16, quarter
+//     l/16) holds the scores of keys 16*rb + 4*(l/16) + r;
+//   O^T[D x 16 tokens] += V^T[D x 32 keys] P^T for each 32-key half (16x16x32
+//     MFMAs, A = the dim-major V tile from LDS, B = P in the registers the QK
 //     MFMA wrote: the k index of both operands runs over the same eight keys
 //     per lane, so no shuffle is needed).
 // Online softmax per (head, token) with a lazily raised reference max, as in
@@ -51,7 +52,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 constexpr int kQT = 16;          // query tokens per wave
 constexpr int kTG = 4;           // token groups per workgroup
 constexpr int kQB = kQT * kTG;   // query tokens per workgroup
-constexpr int kKT = 32;          // keys per tile
+constexpr int kKT = 64;          // keys per tile
+constexpr int kRB = kKT / 16;    // 16-key row blocks per tile (QK)
+constexpr int kNH = kKT / 32;    // 32-key halves per tile (PV)
 
 // QK runs in the caches' own 16-bit type; P.V always runs in binary16: the
 // weights lie in [0, 2^8] (the reference max lags by at most kSlack), where
@@ -119,13 +122,13 @@ __device__ __forceinline__ float rows_sum(float x) {
 
 // LDS tile layouts (16-bit elements), rows padded so that the 16 rows one
 // MFMA operand reads spread over the banks:
-//   K tile [32 keys][D + 8]  (token-major, as in the cache)
-//   V tile [D][32 + 12]      (dim-major, as in the cache; a 22-dword row
-//                             measured fastest of the 8-byte-aligned paddings)
+//   K tile [64 keys][D + 8]  (token-major, as in the cache)
+//   V tile [D][64 + 4]       (dim-major, as in the cache; a 34-dword row, the
+//                             fastest measured of a few 8-byte-aligned ones)
 template <int D>
 struct Tile {
   static constexpr int kRow = D + 8;        // K row, in elements
-  static constexpr int vRow = kKT + 12;     // V row, in elements
+  static constexpr int vRow = kKT + 4;      // V row, in elements
   static constexpr int kElems = kKT * kRow;
   static constexpr int vElems = D * vRow;
   static constexpr int elems = kElems + vElems;
@@ -204,15 +207,16 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
     for (int ks = 0; ks < KSTEPS; ++ks) qf[c][ks] = *(const u32x4 *)(qp + ks * 32);
   }
 
-  // Tile loads: a tile is 4*D 16-byte pieces of K (piece p: key p / (D/8),
-  // dims 8*(p % (D/8)) ..) and 4*D of V (piece p: keys 8*(p / D) .. +7 of
+  // Tile loads: a tile is 8*D 16-byte pieces of K (piece p: key p / (D/8),
+  // dims 8*(p % (D/8)) ..) and 8*D of V (piece p: keys 8*(p / D) .. +7 of
   // dim p % D).  Wave w's load j moves pieces w*64 + j*threads .. +63 of each:
   // 64 / (D/8) whole K rows, or 64 dims of one key octet, so every piece of
   // one load lies in one cache block (blocks hold at least 8 tokens).  The
   // block base is then a scalar and each lane adds a fixed offset.
   constexpr int KPR = D / 8;  // 16-byte pieces per K row
-  constexpr int NP = (4 * D + kThreads - 1) / kThreads;  // pieces of each cache per lane
-  constexpr bool kAllLoad = NP * kThreads == 4 * D;       // every lane has NP pieces
+  constexpr int PIECES = kKT * D / 8;  // 16-byte pieces of one cache per tile
+  constexpr int NP = (PIECES + kThreads - 1) / kThreads;  // pieces of each cache per lane
+  constexpr bool kAllLoad = NP * kThreads == PIECES;      // every lane has NP pieces
   constexpr int KPL = kWave / KPR;  // keys per K load (4 at D = 128, 8 at D = 64)
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const uint32_t koff = (uint32_t)((lane / KPR) * D + (lane % KPR) * 8) * 2;  // bytes
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
   auto fetch = [&](int stage, int tile) {
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
-      const int pw = min(wv * kWave + j * kThreads, 4 * D - kWave);  // first piece (uniform)
+      const int pw = min(wv * kWave + j * kThreads, PIECES - kWave);  // first piece (uniform)
       // the load's keys; past the rows' reach it rereads the group of the
       // last key seen (same block, in bounds)
       const int key0 = min(tile * kKT + pw / KPR, wg_hi & ~(KPL - 1));
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
     }
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
-      const int pw = min(wv * kWave + j * kThreads, 4 * D - kWave);
+      const int pw = min(wv * kWave + j * kThreads, PIECES - kWave);
       const int key0 = min(tile * kKT + (pw / D) * 8, wg_hi & ~7);  // the load's key octet
       const int blk = __builtin_amdgcn_readfirstlane(tbl_lds[key0 >> log2_bs]);
       const char *src = reinterpret_cast<const char *>(vbase) + blk * blk_bytes +
@@ -253,7 +257,7 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       const int pw = wv * kWave + j * kThreads;
-      if (!kAllLoad && pw >= 4 * D) break;
+      if (!kAllLoad && pw >= PIECES) break;
       const int p = pw + lane;
       *(u32x4 *)(kl + (p / KPR) * T::kRow + (p % KPR) * 8) = st_k[stage][j];
       const int k8 = (pw / D) * 8;
@@ -271,7 +275,12 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
         }
       }
       if constexpr ((T::vRow * 2) % 16 == 0) {
+        if constexpr ((T::vRow * 2) % 16 == 0) {
         *(u32x4 *)(vl + (p % D) * T::vRow + k8) = v;
+      } else {
+        *(u32x2 *)(vl + (p % D) * T::vRow + k8) = u32x2{v.x, v.y};
+        *(u32x2 *)(vl + (p % D) * T::vRow + k8 + 4) = u32x2{v.z, v.w};
+      }
       } else {
         *(u32x2 *)(vl + (p % D) * T::vRow + k8) = u32x2{v.x, v.y};
         *(u32x2 *)(vl + (p % D) * T::vRow + k8 + 4) = u32x2{v.z, v.w};
@@ -308,11 +317,11 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
         if (t0 <= wave_hi) {  // the wave sees at least one key of this tile
           const uint16_t *kl = lds + buf * T::elems;
           const uint16_t *vl = kl + T::kElems;
-          // raw scores q.k: two 16-key row blocks x HW heads; the scale (> 0,
+          // raw scores q.k: kRB 16-key row blocks x HW heads; the scale (> 0,
           // in log2 units) joins in the exponent's FMA and on the tile max
-          f32x4 sc[2][HW];
+          f32x4 sc[kRB][HW];
     #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
+          for (int rb = 0; rb < kRB; ++rb) {
             u32x4 ka[KSTEPS];
     #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks)
@@ -327,7 +336,7 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
           }
           if (t0 + kKT - 1 > wave_lo) {  // causal edge: keys past a row's position
     #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < kRB; ++rb)
     #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const bool ok = t0 + rb * 16 + grp * 4 + r <= pos;
@@ -335,11 +344,15 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
                 for (int c = 0; c < HW; ++c) sc[rb][c][r] = ok ? sc[rb][c][r] : -INFINITY;
               }
           }
-          u32x4 pb[HW];  // P^T as the B operand: keys 4grp..+3 then 16+4grp..+3
+          // P^T as B operands, one per 32-key half h: keys 32h+4grp..+3, then
+          // 32h+16+4grp..+3 (row blocks 2h and 2h+1)
+          u32x4 pb[kNH][HW];
     #pragma unroll
           for (int c = 0; c < HW; ++c) {
-            float mx = fmaxf(fmaxf(fmaxf(sc[0][c][0], sc[0][c][1]), fmaxf(sc[0][c][2], sc[0][c][3])),
-                             fmaxf(fmaxf(sc[1][c][0], sc[1][c][1]), fmaxf(sc[1][c][2], sc[1][c][3])));
+            float mx = -INFINITY;
+    #pragma unroll
+            for (int rb = 0; rb < kRB; ++rb)
+              mx = fmaxf(mx, fmaxf(fmaxf(sc[rb][c][0], sc[rb][c][1]), fmaxf(sc[rb][c][2], sc[rb][c][3])));
             mx = rows_max(mx) * scale_log2;  // a row whose keys all lie past it gives -inf
             if (__ballot(mx > m_ref[c] + kSlack)) {
               const float m_new = fmaxf(m_ref[c], mx);
@@ -349,29 +362,37 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
               for (int dt = 0; dt < DTILES; ++dt) acc[c][dt] *= alpha;
               m_ref[c] = m_new;
             }
-            float p[8];
+            float lsum = 0.f;
     #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              p[r] = __builtin_amdgcn_exp2f(fmaf(sc[0][c][r], scale_log2, -m_ref[c]));
-              p[4 + r] = __builtin_amdgcn_exp2f(fmaf(sc[1][c][r], scale_log2, -m_ref[c]));
+            for (int h = 0; h < kNH; ++h) {
+              float p[8];
+    #pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                p[r] = __builtin_amdgcn_exp2f(fmaf(sc[2 * h][c][r], scale_log2, -m_ref[c]));
+                p[4 + r] = __builtin_amdgcn_exp2f(fmaf(sc[2 * h + 1][c][r], scale_log2, -m_ref[c]));
+              }
+              const u32x4 w = {pack_f16(p[0], p[1]), pack_f16(p[2], p[3]), pack_f16(p[4], p[5]),
+                               pack_f16(p[6], p[7])};
+              pb[h][c] = w;
+              // the sum uses the rounded weights the MFMA multiplies with, so
+              // each output row is a convex combination of V rows
+              lsum += ((f16_lo(w[0]) + f16_hi(w[0])) + (f16_lo(w[1]) + f16_hi(w[1]))) +
+                      ((f16_lo(w[2]) + f16_hi(w[2])) + (f16_lo(w[3]) + f16_hi(w[3])));
             }
-            pb[c] = u32x4{pack_f16(p[0], p[1]), pack_f16(p[2], p[3]), pack_f16(p[4], p[5]),
-                          pack_f16(p[6], p[7])};
-            // the sum uses the rounded weights the MFMA multiplies with, so each
-            // output row is a convex combination of V rows
-            l_run[c] += ((f16_lo(pb[c][0]) + f16_hi(pb[c][0])) + (f16_lo(pb[c][1]) + f16_hi(pb[c][1]))) +
-                        ((f16_lo(pb[c][2]) + f16_hi(pb[c][2])) + (f16_lo(pb[c][3]) + f16_hi(pb[c][3])));
+            l_run[c] += lsum;
           }
-          // O^T += V^T P^T over the 32 keys, in the key order of pb
+          // O^T += V^T P^T over each 32-key half, in the key order of pb
     #pragma unroll
-          for (int dt = 0; dt < DTILES; ++dt) {
-            const uint16_t *vr = vl + (dt * 16 + col) * T::vRow + grp * 4;
-            const u32x2 lo = *(const u32x2 *)vr;          // keys 4grp .. +3
-            const u32x2 hi = *(const u32x2 *)(vr + 16);   // keys 16+4grp .. +3
-            const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
+          for (int h = 0; h < kNH; ++h)
     #pragma unroll
-            for (int c = 0; c < HW; ++c) acc[c][dt] = mfma_f16(va, pb[c], acc[c][dt]);
-          }
+            for (int dt = 0; dt < DTILES; ++dt) {
+              const uint16_t *vr = vl + (dt * 16 + col) * T::vRow + 32 * h + grp * 4;
+              const u32x2 lo = *(const u32x2 *)vr;          // keys 32h+4grp .. +3
+              const u32x2 hi = *(const u32x2 *)(vr + 16);   // keys 32h+16+4grp .. +3
+              const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
+    #pragma unroll
+              for (int c = 0; c < HW; ++c) acc[c][dt] = mfma_f16(va, pb[h][c], acc[c][dt]);
+            }
         }
         if (tile + 1 < ntiles) {
           // The other buffer was last read in the previous tile, before its
