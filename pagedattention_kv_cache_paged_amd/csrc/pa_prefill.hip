@@ -97,8 +97,6 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {  // round to 
   f32x2 f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
 }
-__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
-__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
 // two bfloat16 values -> two binary16 values (toward zero: exact in range,
 // saturating beyond it)
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
@@ -374,10 +372,11 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
               const u32x4 w = {pack_f16(p[0], p[1]), pack_f16(p[2], p[3]), pack_f16(p[4], p[5]),
                                pack_f16(p[6], p[7])};
               pb[h][c] = w;
-              // the sum uses the rounded weights the MFMA multiplies with, so
-              // each output row is a convex combination of V rows
-              lsum += ((f16_lo(w[0]) + f16_hi(w[0])) + (f16_lo(w[1]) + f16_hi(w[1]))) +
-                      ((f16_lo(w[2]) + f16_hi(w[2])) + (f16_lo(w[3]) + f16_hi(w[3])));
+              // the row sum takes the fp32 weights; the MFMA multiplies their
+              // binary16 roundings (relative error <= 2^-11 each), so an
+              // output row is off a convex combination of V rows by at most
+              // 2^-11 * max |V|
+              lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
             }
             l_run[c] += lsum;
           }
