@@ -258,7 +258,8 @@ int paged_attention_decode_append(void *out, const void *q, const void *k_new,
  * Numerics: scores and the softmax in fp32; P.V in binary16 weights times
  * binary16 V with fp32 accumulation.  With bfloat16 caches, V is converted
  * to binary16 on chip: exact for magnitudes 2^-17 .. 65504, rounded by less
- * than 2^-24 below, saturated at +-65504 above.  No workspace; out rows of
+ * than 2^-24 below, saturated at +-65504 above.  NaN in q, K or V gives
+ * unspecified values in the rows that see it.  No workspace; out rows of
  * the chunks are the only writes.  Asynchronous on `stream`.
  */
 int paged_attention_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
