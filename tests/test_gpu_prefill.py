@@ -121,15 +121,17 @@ def test_prefill_llama8b_chunks():
     check(got, ref, W.BF16, "llama8b chunks")
 
 
-def test_prefill_table_at_limit():
+@pytest.mark.parametrize("d,dt", [(64, W.F16), (128, W.BF16)])
+def test_prefill_table_at_limit(d, dt):
     """A 32768-token context at block size 8 fills the 4096 block ids a
-    workgroup keeps on chip; a 70-row chunk at its end (sampled rows) and a
-    short whole prompt beside it."""
+    workgroup keeps on chip (with D = 128 the workgroup's LDS is then 84 KB);
+    a 70-row chunk at its end (sampled rows) and a short whole prompt beside
+    it."""
     g = np.random.default_rng(8)
     rows = np.sort(np.concatenate([g.choice(70, 10, replace=False), [70, 71, 75]]))
-    got, ref, _ = run([32768, 6], [70, 6], 2, 1, 64, 8, W.F16, 31, rows=rows,
+    got, ref, _ = run([32768, 6], [70, 6], 2, 1, d, 8, dt, 31, rows=rows,
                       max_blocks_per_seq=4096)
-    check(got, ref, W.F16, "table at limit")
+    check(got, ref, dt, f"table at limit D={d}")
 
 
 @pytest.mark.parametrize("log2s", [14, -20])
