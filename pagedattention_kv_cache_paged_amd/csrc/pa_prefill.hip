@@ -134,9 +134,9 @@ struct Tile {
 
 // HW query heads per wave (1 or 2) and NWH head groups per workgroup (1 or
 // 2): a workgroup is 4 * NWH waves serving 64 tokens x HW * NWH heads, and a
-// wave stays under 256 registers, so two waves share each SIMD and one's
-// softmax overlaps the other's MFMAs.  q rows beyond the chunk and padded
-// heads compute on clamped inputs and are never stored.
+// wave stays under 256 registers, so two waves share each SIMD.  q rows
+// beyond the chunk and padded heads compute on clamped inputs and are never
+// stored.
 template <int DT, int D, int HW, int NWH>
 __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
     uint16_t *__restrict__ out, const uint16_t *__restrict__ q,
@@ -272,16 +272,12 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
           v[e] &= c >= 2 ? 0xffffffffu : (c == 1 ? 0x0000ffffu : 0u);
         }
       }
+      uint16_t *vd = vl + (p % D) * T::vRow + k8;
       if constexpr ((T::vRow * 2) % 16 == 0) {
-        if constexpr ((T::vRow * 2) % 16 == 0) {
-        *(u32x4 *)(vl + (p % D) * T::vRow + k8) = v;
-      } else {
-        *(u32x2 *)(vl + (p % D) * T::vRow + k8) = u32x2{v.x, v.y};
-        *(u32x2 *)(vl + (p % D) * T::vRow + k8 + 4) = u32x2{v.z, v.w};
-      }
-      } else {
-        *(u32x2 *)(vl + (p % D) * T::vRow + k8) = u32x2{v.x, v.y};
-        *(u32x2 *)(vl + (p % D) * T::vRow + k8 + 4) = u32x2{v.z, v.w};
+        *(u32x4 *)vd = v;
+      } else {  // V rows are 8-byte aligned only
+        *(u32x2 *)vd = u32x2{v.x, v.y};
+        *(u32x2 *)(vd + 4) = u32x2{v.z, v.w};
       }
     }
   };
