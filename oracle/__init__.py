@@ -107,6 +107,9 @@ def _load():
     lib.oracle_prefill.argtypes = [p, p, p, p, p, p, p, dbl, i32, i32, i32, i32, i32, i32, i64,
                                    i32]
     lib.oracle_prefill.restype = i32
+    lib.oracle_prefill_fp8.argtypes = [p, p, p, p, p, p, p, dbl, i32, i32, i32, i32, i32, i32,
+                                       i64, i32, dbl, dbl]
+    lib.oracle_prefill_fp8.restype = i32
     _lib = lib
     return lib
 
@@ -339,4 +342,26 @@ def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
     _check(_load().oracle_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt),
                                   _ptr(cl), _ptr(qs), float(scale), bs, hkv, cl.size, hq, d,
                                   bt.shape[1], nb, dtype_code(dtype)), "oracle_prefill")
+    return out
+
+
+def prefill_fp8(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                block_size: int, q_dtype, k_scale: float, v_scale: float) -> np.ndarray:
+    """Chunked prefill over E4M3 caches (uint8 codes; K = code * k_scale,
+    V = code * v_scale); q [total_q, Hq, D] bits of q_dtype.  Returns float64
+    [total_q, Hq, D]."""
+    q = _u16(q)
+    k_cache = np.ascontiguousarray(k_cache, dtype=np.uint8)
+    v_cache = np.ascontiguousarray(v_cache, dtype=np.uint8)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    total, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    assert bs == block_size and qs.size == cl.size + 1 and qs[-1] == total
+    out = np.zeros((total, hq, d), dtype=np.float64)
+    _check(_load().oracle_prefill_fp8(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(bt), _ptr(cl), _ptr(qs), float(scale), bs, hkv,
+                                      cl.size, hq, d, bt.shape[1], nb, dtype_code(q_dtype),
+                                      float(k_scale), float(v_scale)), "oracle_prefill_fp8")
     return out

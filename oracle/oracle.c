@@ -664,14 +664,18 @@ int oracle_swap_blocks(void *dst_k, void *dst_v, int64_t dst_num_blocks, const v
  *     out[d] = sum_t exp(x[t] - max x) V[t,d] / sum_t exp(x[t] - max x)
  * reaching token t through block_tables[s][t / bs] at offset t % bs, with
  * KV head h / (num_heads / num_kv_heads).  n_s > L is an error
- * (ORACLE_ELEN); n_s = 0 contributes nothing.  16-bit caches only. */
-int oracle_prefill(double *out, const uint16_t *q, const uint16_t *k_cache,
-                   const uint16_t *v_cache, const int32_t *block_tables,
-                   const int32_t *context_lens, const int32_t *query_start, double scale,
-                   int block_size, int num_kv_heads, int num_seqs, int num_heads, int head_dim,
-                   int max_blocks_per_seq, int64_t num_blocks, int dtype) {
+ * (ORACLE_ELEN); n_s = 0 contributes nothing.  The cache elements are 16-bit
+ * values of q's type, or E4M3 codes times k_scale / v_scale (cache_dtype
+ * ORACLE_FP8, as in oracle_decode_fp8). */
+static int prefill_any(double *out, const uint16_t *q, const void *k_cache,
+                       const void *v_cache, const int32_t *block_tables,
+                       const int32_t *context_lens, const int32_t *query_start, double scale,
+                       int block_size, int num_kv_heads, int num_seqs, int num_heads,
+                       int head_dim, int max_blocks_per_seq, int64_t num_blocks, int dtype,
+                       int cache_dtype, double k_scale, double v_scale) {
   if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || num_seqs < 0 ||
-      block_size <= 0 || head_dim <= 0 || (dtype != ORACLE_F16 && dtype != ORACLE_BF16))
+      block_size <= 0 || head_dim <= 0 || (dtype != ORACLE_F16 && dtype != ORACLE_BF16) ||
+      (cache_dtype != dtype && cache_dtype != ORACLE_FP8))
     return ORACLE_EARG;
   int group = num_heads / num_kv_heads;
   for (int s = 0; s < num_seqs; ++s) {
@@ -697,7 +701,7 @@ int oracle_prefill(double *out, const uint16_t *q, const uint16_t *k_cache,
                           (int)(t % block_size)) * head_dim;
           double dot = 0.0;
           for (int d = 0; d < head_dim; ++d)
-            dot += decode(qrow[d], dtype) * decode(k_cache[krow + d], dtype);
+            dot += decode(qrow[d], dtype) * cache_value(k_cache, krow + d, cache_dtype, k_scale);
           x[t] = scale * dot;
         }
         double m = x[0];
@@ -715,7 +719,7 @@ int oracle_prefill(double *out, const uint16_t *q, const uint16_t *k_cache,
           for (int d = 0; d < head_dim; ++d) {
             int64_t vi = ((block * num_kv_heads + kv_head) * (int64_t)head_dim + d) *
                              block_size + offset;
-            orow[d] += x[t] * decode(v_cache[vi], dtype);
+            orow[d] += x[t] * cache_value(v_cache, vi, cache_dtype, v_scale);
           }
         }
         for (int d = 0; d < head_dim; ++d) orow[d] /= z;
@@ -724,4 +728,29 @@ int oracle_prefill(double *out, const uint16_t *q, const uint16_t *k_cache,
     free(x);
   }
   return ORACLE_OK;
+}
+
+/* Chunked prefill over 16-bit caches of q's type. */
+int oracle_prefill(double *out, const uint16_t *q, const uint16_t *k_cache,
+                   const uint16_t *v_cache, const int32_t *block_tables,
+                   const int32_t *context_lens, const int32_t *query_start, double scale,
+                   int block_size, int num_kv_heads, int num_seqs, int num_heads, int head_dim,
+                   int max_blocks_per_seq, int64_t num_blocks, int dtype) {
+  return prefill_any(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                     block_size, num_kv_heads, num_seqs, num_heads, head_dim,
+                     max_blocks_per_seq, num_blocks, dtype, dtype, 1.0, 1.0);
+}
+
+/* Chunked prefill over E4M3 caches (the FP8 reading of oracle_kv_write_fp8):
+ * K = code * k_scale, V = code * v_scale, exact in double; q (type q_dtype)
+ * and the result as for the 16-bit caches. */
+int oracle_prefill_fp8(double *out, const uint16_t *q, const uint8_t *k_cache,
+                       const uint8_t *v_cache, const int32_t *block_tables,
+                       const int32_t *context_lens, const int32_t *query_start, double scale,
+                       int block_size, int num_kv_heads, int num_seqs, int num_heads,
+                       int head_dim, int max_blocks_per_seq, int64_t num_blocks, int q_dtype,
+                       double k_scale, double v_scale) {
+  return prefill_any(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                     block_size, num_kv_heads, num_seqs, num_heads, head_dim,
+                     max_blocks_per_seq, num_blocks, q_dtype, ORACLE_FP8, k_scale, v_scale);
 }

@@ -20,7 +20,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = [os.path.join(ROOT, "tests", "test_oracle_pins.py"),
         os.path.join(ROOT, "tests", "test_oracle_fp8.py"),
         os.path.join(ROOT, "tests", "test_oracle_blocks.py"),
-        os.path.join(ROOT, "tests", "test_oracle_prefill.py")]
+        os.path.join(ROOT, "tests", "test_oracle_prefill.py"),
+        os.path.join(ROOT, "tests", "test_oracle_prefill_fp8.py")]
 
 # (name, original text, planted text) -- the first occurrence is replaced
 MUTANTS = [
@@ -84,6 +85,12 @@ MUTANTS = [
      "int kv_head = h % num_kv_heads;\n        const uint16_t *qrow = q + ((row0"),
     ("prefill_sees_next_token", "int64_t p = len - n + i; /* the row's own position",
      "int64_t p = len - n + i + (i + 1 < n); /* the row's own position"),
+    ("prefill_fp8_v_takes_k_scale",
+     "orow[d] += x[t] * cache_value(v_cache, vi, cache_dtype, v_scale);",
+     "orow[d] += x[t] * cache_value(v_cache, vi, cache_dtype, k_scale);"),
+    ("prefill_fp8_k_scale_dropped",
+     "dot += decode(qrow[d], dtype) * cache_value(k_cache, krow + d, cache_dtype, k_scale);",
+     "dot += decode(qrow[d], dtype) * cache_value(k_cache, krow + d, cache_dtype, 1.0);"),
 ]
 # the consistent V-layout mutant also moves the write to token-major order
 EXTRA = {
