@@ -313,12 +313,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 MFMA, MI355X
 PREFILL_KERNEL = "prefill_kernel"
 
 
-def bench_prefill(args, torch, B, W, dev, lib):
+def bench_prefill(args, torch, B, W, dev, lib, fp8=False):
     """Chunked prefill at the Llama-3-8B shape: 8 sequences, each with 1536
     cached tokens and a 512-token chunk (32 q / 8 kv heads, head_dim 128,
-    block 16, bf16, random block placement).  Algorithmic flops: for each
-    chunk row at position p and each query head, 2*D*(p+1) for q K^T and the
-    same for P V."""
+    block 16, bf16, random block placement; with fp8, E4M3 caches and bf16
+    q / out).  Algorithmic flops: for each chunk row at position p and each
+    query head, 2*D*(p+1) for q K^T and the same for P V."""
     nseq, cached, chunk = 8, 1536, 512
     w = W.build("prefill", [cached + chunk] * nseq, num_heads=32, num_kv_heads=8,
                 head_dim=128, block_size=16, dtype=W.BF16, seed=61)
@@ -328,11 +328,15 @@ def bench_prefill(args, torch, B, W, dev, lib):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(tdt)
 
     ks, vs = w.cache_shapes()
-    kc = torch.zeros(ks, dtype=tdt, device=dev)
-    vc = torch.zeros(vs, dtype=tdt, device=dev)
+    kc = torch.zeros(ks, dtype=torch.uint8 if fp8 else tdt, device=dev)
+    vc = torch.zeros(vs, dtype=torch.uint8 if fp8 else tdt, device=dev)
     for which in ("hist", "new"):
         k, v, sl = w.write_batch(which)
-        B.paged_kv_write(dev_bits(k), dev_bits(v), torch.from_numpy(sl).to(dev), kc, vc)
+        if fp8:
+            B.paged_kv_write_fp8(dev_bits(k), dev_bits(v), torch.from_numpy(sl).to(dev), kc, vc,
+                                 FP8_K_SCALE, FP8_V_SCALE)
+        else:
+            B.paged_kv_write(dev_bits(k), dev_bits(v), torch.from_numpy(sl).to(dev), kc, vc)
     qs_np = (np.arange(nseq + 1) * chunk).astype(np.int32)
     g = np.random.default_rng(62)
     q_bits = W.normal_bits(g, (nseq * chunk, 32, 128), W.BF16)
@@ -345,10 +349,16 @@ def bench_prefill(args, torch, B, W, dev, lib):
     stream = torch.cuda.current_stream()
 
     def launch():
-        rc = lib.paged_attention_prefill(out.data_ptr(), q.data_ptr(), kc.data_ptr(),
-                                         vc.data_ptr(), bt.data_ptr(), cl.data_ptr(),
-                                         qs.data_ptr(), w.scale, 16, 8, nseq, 32, 128,
-                                         w.max_blocks_per_seq, w.num_blocks, 1, chunk, sp)
+        if fp8:
+            rc = lib.paged_attention_prefill_fp8(
+                out.data_ptr(), q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bt.data_ptr(),
+                cl.data_ptr(), qs.data_ptr(), w.scale, FP8_K_SCALE, FP8_V_SCALE, 16, 8, nseq,
+                32, 128, w.max_blocks_per_seq, w.num_blocks, 1, chunk, sp)
+        else:
+            rc = lib.paged_attention_prefill(out.data_ptr(), q.data_ptr(), kc.data_ptr(),
+                                             vc.data_ptr(), bt.data_ptr(), cl.data_ptr(),
+                                             qs.data_ptr(), w.scale, 16, 8, nseq, 32, 128,
+                                             w.max_blocks_per_seq, w.num_blocks, 1, chunk, sp)
         assert rc == 0, rc
     # untimed warm-up long enough (~50 ms of launches) for the clocks to settle
     nwarm = max(args.warmup, 300)
@@ -373,7 +383,8 @@ def bench_prefill(args, torch, B, W, dev, lib):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"chunked prefill: {nseq} sequences x {chunk}-token chunk after "
                                f"{cached} cached tokens; 32 q / 8 kv heads, head_dim 128, "
-                               f"block 16, bf16", "rows": nseq * chunk,
+                               f"block 16, bf16" + (", E4M3 KV cache" if fp8 else ""),
+                   "rows": nseq * chunk, "kv_dtype": "e4m3" if fp8 else "bf16",
                    "context_tokens": nseq * (cached + chunk)},
         "tokens_per_s": round(nseq * chunk / (us * 1e-6), 1),
         "roofline": {"kernel": PREFILL_KERNEL, "bound": "mfma", "achieved": round(tflops, 2),
@@ -383,17 +394,23 @@ def bench_prefill(args, torch, B, W, dev, lib):
     }
     if not args.no_cpu_baseline:
         import oracle
-        okc, ovc = w.nan_caches()
+        okc, ovc = w.nan_caches_fp8() if fp8 else w.nan_caches()
         for which in ("hist", "new"):
             k, v, sl = w.write_batch(which)
-            oracle.kv_write(k, v, sl, okc, ovc, 16)
+            if fp8:
+                oracle.kv_write_fp8(k, v, sl, okc, ovc, 16, W.BF16, FP8_K_SCALE, FP8_V_SCALE)
+            else:
+                oracle.kv_write(k, v, sl, okc, ovc, 16)
         done, fl, t_total = 0, 0.0, 0.0
         while done < chunk and t_total < min(args.cpu_seconds, 15.0):
             p = cached + done   # rows of sequence 0, one at a time
             t0 = time.perf_counter()
-            oracle.prefill(q_bits[done:done + 1], okc, ovc, w.block_tables[:1],
-                           np.array([p + 1], np.int32), np.array([0, 1], np.int32), w.scale,
-                           16, W.BF16)
+            one = (q_bits[done:done + 1], okc, ovc, w.block_tables[:1],
+                   np.array([p + 1], np.int32), np.array([0, 1], np.int32), w.scale, 16, W.BF16)
+            if fp8:
+                oracle.prefill_fp8(*one, FP8_K_SCALE, FP8_V_SCALE)
+            else:
+                oracle.prefill(*one)
             t_total += time.perf_counter() - t0
             fl += 32 * 4.0 * 128 * (p + 1)
             done += 1
@@ -464,7 +481,7 @@ def main():
     if args.op == "swap_blocks":
         return bench_swap_blocks(args, torch, B, dev, lib)
     if args.op == "prefill":
-        return bench_prefill(args, torch, B, W, dev, lib)
+        return bench_prefill(args, torch, B, W, dev, lib, fp8)
     w = make_workload(args.workload, args.placement)
     tdt = {W.F16: torch.float16, W.BF16: torch.bfloat16}[w.dtype]
 

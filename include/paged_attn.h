@@ -270,6 +270,26 @@ int paged_attention_prefill(void *out, const void *q, const void *k_cache, const
                             int32_t dtype, int32_t max_query_len, void *stream);
 
 /*
+ * paged_attention_prefill over E4M3 caches (the FP8 reading of
+ * paged_kv_write_fp8: uint8 codes in the same layouts, a code c standing for
+ * c * k_scale in K and c * v_scale in V; "vLLM framework analysis: how
+ * PagedAttention speeds up LLM inference 20x", 7).  q and out stay in
+ * `dtype`.  The codes are converted exactly (K to q's type, V to binary16)
+ * as the kernel stores them to its tiles; k_scale joins the score scale and
+ * v_scale multiplies the output.  k_scale, v_scale: finite, normal, > 0,
+ * else PA_ERR_SHAPE.  Every other argument, check and limit is that of
+ * paged_attention_prefill.
+ */
+int paged_attention_prefill_fp8(void *out, const void *q, const void *k_cache,
+                                const void *v_cache, const int32_t *block_tables,
+                                const int32_t *context_lens, const int32_t *query_start,
+                                float scale, float k_scale, float v_scale, int32_t block_size,
+                                int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                                int32_t head_dim, int32_t max_blocks_per_seq,
+                                int64_t num_blocks, int32_t dtype, int32_t max_query_len,
+                                void *stream);
+
+/*
  * Host-side check of metadata (host pointers): every context length in
  * [0, max_blocks_per_seq * block_size]; every table entry a sequence reads,
  * i.e. the first ceil(L / block_size) of its row, in [0, num_blocks); every

@@ -83,6 +83,9 @@ def load() -> ctypes.CDLL:
     lib.paged_attention_prefill.restype = ctypes.c_int
     lib.paged_attention_prefill.argtypes = [p, p, p, p, p, p, p, f32, i32, i32, i32, i32, i32,
                                             i32, i64, i32, i32, p]
+    lib.paged_attention_prefill_fp8.restype = ctypes.c_int
+    lib.paged_attention_prefill_fp8.argtypes = [p, p, p, p, p, p, p, f32, f32, f32, i32, i32,
+                                                i32, i32, i32, i32, i64, i32, i32, p]
     lib.pa_pool_create.restype = ctypes.c_int
     lib.pa_pool_create.argtypes = [i64, p, ctypes.POINTER(p)]
     lib.pa_pool_destroy.restype = None
@@ -505,14 +508,8 @@ def validate_swap_pairs(pairs, src_num_blocks: int, dst_num_blocks: int) -> int:
 
 # ---- paged (chunked) prefill -------------------------------------------------
 
-def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
-                            v_cache: torch.Tensor, block_tables: torch.Tensor,
-                            context_lens: torch.Tensor, query_start: torch.Tensor,
-                            scale: float, block_size: int, num_kv_heads: int,
-                            max_query_len: int) -> torch.Tensor:
-    """Rows query_start[s] .. query_start[s+1]-1 of q / out ([rows, Hq, D])
-    are sequence s's last positions; each attends causally over the paged
-    context up to its own position.  Returns out."""
+def _prefill_shapes(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                    block_size, num_kv_heads):
     dev = _dev(out, q, k_cache, v_cache, block_tables, context_lens, query_start)
     if q.dim() != 3 or out.shape != q.shape:
         raise ValueError("q and out must be [rows, num_heads, head_dim]")
@@ -530,7 +527,23 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
     if query_start.dtype != torch.int32 or tuple(query_start.shape) != (B + 1,):
         raise ValueError("query_start must be int32 [num_seqs + 1]")
     dt = _dtype(q)
-    if out.dtype != q.dtype or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+    if out.dtype != q.dtype:
+        raise ValueError("q and out must share one dtype")
+    return dev, B, hq, d, nb, dt
+
+
+def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor, block_tables: torch.Tensor,
+                            context_lens: torch.Tensor, query_start: torch.Tensor,
+                            scale: float, block_size: int, num_kv_heads: int,
+                            max_query_len: int) -> torch.Tensor:
+    """Rows query_start[s] .. query_start[s+1]-1 of q / out ([rows, Hq, D])
+    are sequence s's last positions; each attends causally over the paged
+    context up to its own position.  Returns out."""
+    dev, B, hq, d, nb, dt = _prefill_shapes(out, q, k_cache, v_cache, block_tables,
+                                            context_lens, query_start, block_size,
+                                            num_kv_heads)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise ValueError("q, out and the caches must share one dtype")
     rc = load().paged_attention_prefill(
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -538,4 +551,26 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
         block_size, num_kv_heads, B, hq, d, block_tables.shape[1], nb, dt, int(max_query_len),
         _stream(dev))
     _check("paged_attention_prefill", rc)
+    return out
+
+
+def paged_attention_prefill_fp8(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                                v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                context_lens: torch.Tensor, query_start: torch.Tensor,
+                                scale: float, k_scale: float, v_scale: float,
+                                block_size: int, num_kv_heads: int,
+                                max_query_len: int) -> torch.Tensor:
+    """paged_attention_prefill over E4M3 caches (uint8 tensors, layouts as
+    for the 16-bit caches) with K = code * k_scale, V = code * v_scale."""
+    dev, B, hq, d, nb, dt = _prefill_shapes(out, q, k_cache, v_cache, block_tables,
+                                            context_lens, query_start, block_size,
+                                            num_kv_heads)
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("FP8 caches are uint8 tensors of E4M3 codes")
+    rc = load().paged_attention_prefill_fp8(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(), float(scale),
+        float(k_scale), float(v_scale), block_size, num_kv_heads, B, hq, d,
+        block_tables.shape[1], nb, dt, int(max_query_len), _stream(dev))
+    _check("paged_attention_prefill_fp8", rc)
     return out

@@ -74,7 +74,7 @@ bool decode_sizes_ok(int32_t num_seqs, int32_t num_kv_heads, int32_t num_heads,
 
 extern "C" {
 
-int pa_abi_version(void) { return 5; }
+int pa_abi_version(void) { return 6; }
 
 const char *pa_strerror(int code) {
   switch (code) {
@@ -260,12 +260,13 @@ int paged_attention_decode(void *out, const void *q, const void *k_cache, const 
                                    workspace_bytes, stream);
 }
 
-int paged_attention_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
-                            const int32_t *block_tables, const int32_t *context_lens,
-                            const int32_t *query_start, float scale, int32_t block_size,
-                            int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
-                            int32_t head_dim, int32_t max_blocks_per_seq, int64_t num_blocks,
-                            int32_t dtype, int32_t max_query_len, void *stream) {
+static int prefill_common(void *out, const void *q, const void *k_cache, const void *v_cache,
+                          const int32_t *block_tables, const int32_t *context_lens,
+                          const int32_t *query_start, float scale, int32_t block_size,
+                          int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                          int32_t head_dim, int32_t max_blocks_per_seq, int64_t num_blocks,
+                          int32_t dtype, int32_t max_query_len, int kv_fp8, float k_scale,
+                          float v_scale, void *stream) {
   if (dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_DTYPE;
   if (!decode_sizes_ok(num_seqs, num_kv_heads, num_heads, head_dim, max_blocks_per_seq,
                        block_size) ||
@@ -273,6 +274,7 @@ int paged_attention_prefill(void *out, const void *q, const void *k_cache, const
       max_query_len < 0 || (int64_t)max_query_len > (int64_t)max_blocks_per_seq * block_size ||
       max_blocks_per_seq > pa::kPrefillMaxBlocks)
     return PA_ERR_SHAPE;
+  if (kv_fp8 && !(valid_scale(k_scale) && valid_scale(v_scale))) return PA_ERR_SHAPE;
   if (num_seqs == 0 || max_query_len == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
     return PA_ERR_NULL;
@@ -281,8 +283,35 @@ int paged_attention_prefill(void *out, const void *q, const void *k_cache, const
     return PA_ERR_ALIGN;
   pa::PrefillArgs a{out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
                     block_size, num_kv_heads, num_seqs, num_heads, head_dim,
-                    max_blocks_per_seq, num_blocks, dtype, max_query_len, stream};
+                    max_blocks_per_seq, num_blocks, dtype, max_query_len, kv_fp8,
+                    kv_fp8 ? k_scale : 1.0f, kv_fp8 ? v_scale : 1.0f, stream};
   return pa::launch_prefill(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int paged_attention_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            const int32_t *query_start, float scale, int32_t block_size,
+                            int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                            int32_t head_dim, int32_t max_blocks_per_seq, int64_t num_blocks,
+                            int32_t dtype, int32_t max_query_len, void *stream) {
+  return prefill_common(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                        scale, block_size, num_kv_heads, num_seqs, num_heads, head_dim,
+                        max_blocks_per_seq, num_blocks, dtype, max_query_len, 0, 1.0f, 1.0f,
+                        stream);
+}
+
+int paged_attention_prefill_fp8(void *out, const void *q, const void *k_cache,
+                                const void *v_cache, const int32_t *block_tables,
+                                const int32_t *context_lens, const int32_t *query_start,
+                                float scale, float k_scale, float v_scale, int32_t block_size,
+                                int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                                int32_t head_dim, int32_t max_blocks_per_seq,
+                                int64_t num_blocks, int32_t dtype, int32_t max_query_len,
+                                void *stream) {
+  return prefill_common(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                        scale, block_size, num_kv_heads, num_seqs, num_heads, head_dim,
+                        max_blocks_per_seq, num_blocks, dtype, max_query_len, 1, k_scale,
+                        v_scale, stream);
 }
 
 int paged_validate_metadata(const int32_t *block_tables, const int32_t *context_lens,

@@ -102,6 +102,9 @@ struct PrefillArgs {
   int64_t num_blocks;
   int32_t dtype;
   int32_t max_query_len;        // bound on any sequence's chunk length (grid size)
+  int32_t kv_fp8;               // 1: caches hold E4M3 codes (k_scale, v_scale apply)
+  float k_scale;
+  float v_scale;
   void *stream;
 };
 

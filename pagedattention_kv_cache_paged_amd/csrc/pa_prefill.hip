@@ -104,6 +104,26 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
                                                                  __uint_as_float(w & 0xffff0000u)));
 }
 
+// four E4M3 codes (bytes 0..3) -> four values of the caller's 16-bit type
+// (DT 0 binary16, DT 1 bfloat16), exact: every E4M3 value fits both
+template <int DT>
+__device__ __forceinline__ u32x2 e4m3x4_to(uint32_t c) {
+  if constexpr (DT == 1)
+    return u32x2{
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, true))};
+  else
+    return u32x2{
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c, 1.0f, true))};
+}
+// eight E4M3 codes -> eight 16-bit values
+template <int DT>
+__device__ __forceinline__ u32x4 e4m3x8_to(u32x2 c) {
+  const u32x2 a = e4m3x4_to<DT>(c.x), b = e4m3x4_to<DT>(c.y);
+  return u32x4{a.x, a.y, b.x, b.y};
+}
+
 __device__ __forceinline__ float rows_max(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
@@ -136,14 +156,16 @@ struct Tile {
 // 2): a workgroup is 4 * NWH waves serving 64 tokens x HW * NWH heads, and a
 // wave stays under 256 registers, so two waves share each SIMD.  q rows
 // beyond the chunk and padded heads compute on clamped inputs and are never
-// stored.
-template <int DT, int D, int HW, int NWH>
+// stored.  KV8: the caches hold E4M3 codes, converted exactly to q's type
+// (K) and binary16 (V) as they are stored to LDS; scale_log2 then carries
+// k_scale and out_scale is v_scale.
+template <int DT, int D, int HW, int NWH, bool KV8>
 __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
     uint16_t *__restrict__ out, const uint16_t *__restrict__ q,
-    const uint16_t *__restrict__ k_cache, const uint16_t *__restrict__ v_cache,
+    const void *__restrict__ k_cache, const void *__restrict__ v_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    const int32_t *__restrict__ query_start, float scale_log2, int log2_bs, int num_seqs,
-    int num_kv_heads, int num_heads, int group, int chunks, int max_blocks,
+    const int32_t *__restrict__ query_start, float scale_log2, float out_scale, int log2_bs,
+    int num_seqs, int num_kv_heads, int num_heads, int group, int chunks, int max_blocks,
     int64_t num_blocks, int nqb) {
   using E = Elem<DT>;
   constexpr int HC = HW * NWH;     // query heads per workgroup
@@ -190,9 +212,10 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
     tbl_lds[i] = (b >= 0 && b < num_blocks) ? b : 0;
   }
   __syncthreads();
-  const int64_t blk_stride = (int64_t)num_kv_heads * bs * D;  // elements per block
-  const uint16_t *kbase = k_cache + (int64_t)kvh * bs * D;
-  const uint16_t *vbase = v_cache + (int64_t)kvh * D * bs;
+  constexpr int EB = KV8 ? 1 : 2;  // bytes per cache element
+  const int64_t blk_bytes = (int64_t)num_kv_heads * bs * D * EB;  // one block of one cache
+  const char *kbase = (const char *)k_cache + (int64_t)kvh * bs * D * EB;
+  const char *vbase = (const char *)v_cache + (int64_t)kvh * D * bs * EB;
 
   // q of this lane's token for the wave's HW heads, as B operands (dims
   // 32ks+8grp..+8)
@@ -205,26 +228,26 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
     for (int ks = 0; ks < KSTEPS; ++ks) qf[c][ks] = *(const u32x4 *)(qp + ks * 32);
   }
 
-  // Tile loads: a tile is 8*D 16-byte pieces of K (piece p: key p / (D/8),
-  // dims 8*(p % (D/8)) ..) and 8*D of V (piece p: keys 8*(p / D) .. +7 of
-  // dim p % D).  Wave w's load j moves pieces w*64 + j*threads .. +63 of each:
+  // Tile loads: a tile is 8*D pieces of 8 elements (16 bytes, or 8 with E4M3
+  // codes) of K (piece p: key p / (D/8), dims 8*(p % (D/8)) ..) and 8*D of V
+  // (piece p: keys 8*(p / D) .. +7 of dim p % D).  Wave w's load j moves pieces w*64 + j*threads .. +63 of each:
   // 64 / (D/8) whole K rows, or 64 dims of one key octet, so every piece of
   // one load lies in one cache block (blocks hold at least 8 tokens).  The
   // block base is then a scalar and each lane adds a fixed offset.
   constexpr int KPR = D / 8;  // 16-byte pieces per K row
-  constexpr int PIECES = kKT * D / 8;  // 16-byte pieces of one cache per tile
+  constexpr int PIECES = kKT * D / 8;  // 8-element pieces of one cache per tile
   constexpr int NP = (PIECES + kThreads - 1) / kThreads;  // pieces of each cache per lane
   constexpr bool kAllLoad = NP * kThreads == PIECES;      // every lane has NP pieces
   constexpr int KPL = kWave / KPR;  // keys per K load (4 at D = 128, 8 at D = 64)
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const uint32_t koff = (uint32_t)((lane / KPR) * D + (lane % KPR) * 8) * 2;  // bytes
-  const uint32_t voff = (uint32_t)(lane * bs) * 2;
-  const int64_t blk_bytes = blk_stride * 2;
+  const uint32_t koff = (uint32_t)((lane / KPR) * D + (lane % KPR) * 8) * EB;  // bytes
+  const uint32_t voff = (uint32_t)(lane * bs) * EB;
+  using Piece = std::conditional_t<KV8, u32x2, u32x4>;
   // A ring of kStages register stages: a tile's loads are issued
   // kStages - 1 tiles before they go into LDS, so the wait for them is
   // covered by that many tiles of compute.
   constexpr int kStages = 3;
-  u32x4 st_k[kStages][NP], st_v[kStages][NP];
+  Piece st_k[kStages][NP], st_v[kStages][NP];
   auto fetch = [&](int stage, int tile) {
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
@@ -233,18 +256,17 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
       // last key seen (same block, in bounds)
       const int key0 = min(tile * kKT + pw / KPR, wg_hi & ~(KPL - 1));
       const int blk = __builtin_amdgcn_readfirstlane(tbl_lds[key0 >> log2_bs]);
-      const char *src = reinterpret_cast<const char *>(kbase) + blk * blk_bytes +
-                        (int64_t)((key0 & (bs - 1)) * D * 2);
-      st_k[stage][j] = __builtin_nontemporal_load((const u32x4 *)(src + koff));
+      const char *src = kbase + blk * blk_bytes + (int64_t)((key0 & (bs - 1)) * D * EB);
+      st_k[stage][j] = __builtin_nontemporal_load((const Piece *)(src + koff));
     }
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       const int pw = min(wv * kWave + j * kThreads, PIECES - kWave);
       const int key0 = min(tile * kKT + (pw / D) * 8, wg_hi & ~7);  // the load's key octet
       const int blk = __builtin_amdgcn_readfirstlane(tbl_lds[key0 >> log2_bs]);
-      const char *src = reinterpret_cast<const char *>(vbase) + blk * blk_bytes +
-                        (int64_t)(((pw % D) * bs + (key0 & (bs - 1))) * 2);
-      st_v[stage][j] = __builtin_nontemporal_load((const u32x4 *)(src + voff));
+      const char *src =
+          vbase + blk * blk_bytes + (int64_t)(((pw % D) * bs + (key0 & (bs - 1))) * EB);
+      st_v[stage][j] = __builtin_nontemporal_load((const Piece *)(src + voff));
     }
   };
   // Into LDS; V of keys past the workgroup's last position is zeroed there
@@ -257,13 +279,21 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
       const int pw = wv * kWave + j * kThreads;
       if (!kAllLoad && pw >= PIECES) break;
       const int p = pw + lane;
-      *(u32x4 *)(kl + (p / KPR) * T::kRow + (p % KPR) * 8) = st_k[stage][j];
+      u32x4 kv;
+      if constexpr (KV8) kv = e4m3x8_to<DT>(st_k[stage][j]);
+      else kv = st_k[stage][j];
+      *(u32x4 *)(kl + (p / KPR) * T::kRow + (p % KPR) * 8) = kv;
       const int k8 = (pw / D) * 8;
       const int valid = wg_hi + 1 - (tile * kKT + k8);  // keys the rows can see
-      u32x4 v = st_v[stage][j];
-      if constexpr (DT == 1) {
+      u32x4 v;
+      if constexpr (KV8) {
+        v = e4m3x8_to<0>(st_v[stage][j]);  // binary16, exact
+      } else {
+        v = st_v[stage][j];
+        if constexpr (DT == 1) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
+          for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
+        }
       }
       if (valid < 8) {
 #pragma unroll
@@ -405,7 +435,7 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
   // 16*dt + 4*grp + 0..3
   float inv[HW];
 #pragma unroll
-  for (int c = 0; c < HW; ++c) inv[c] = 1.0f / rows_sum(l_run[c]);  // whole wave
+  for (int c = 0; c < HW; ++c) inv[c] = out_scale / rows_sum(l_run[c]);  // whole wave
   const int row = wt0 + col;
   if (row < n) {
 #pragma unroll
@@ -424,7 +454,7 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
   }
 }
 
-template <int DT, int D, int HW, int NWH>
+template <int DT, int D, int HW, int NWH, bool KV8>
 int launch_hc(const PrefillArgs &a) {
   constexpr int HC = HW * NWH;
   const int group = a.num_heads / a.num_kv_heads;
@@ -435,34 +465,38 @@ int launch_hc(const PrefillArgs &a) {
   if (groups > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
   int log2_bs = 0;
   while ((1 << log2_bs) < a.block_size) ++log2_bs;
-  const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+  // log2(e) folds the exponential's base into the score scale; an E4M3
+  // cache's k_scale multiplies every score and its v_scale every output.
+  const float scale_log2 =
+      (float)((double)a.scale * (KV8 ? (double)a.k_scale : 1.0) * 1.4426950408889634);
+  const float out_scale = KV8 ? a.v_scale : 1.0f;
   const size_t lds = 2 * sizeof(uint16_t) * Tile<D>::elems + sizeof(int32_t) * a.max_blocks_per_seq;
-  prefill_kernel<DT, D, HW, NWH>
+  prefill_kernel<DT, D, HW, NWH, KV8>
       <<<dim3((unsigned)groups), kWave * kTG * NWH, lds, (hipStream_t)a.stream>>>(
-          (uint16_t *)a.out, (const uint16_t *)a.q, (const uint16_t *)a.k_cache,
-          (const uint16_t *)a.v_cache, a.block_tables, a.context_lens, a.query_start,
-          scale_log2, log2_bs, a.num_seqs, a.num_kv_heads, a.num_heads, group, chunks,
-          a.max_blocks_per_seq, a.num_blocks, nqb);
+          (uint16_t *)a.out, (const uint16_t *)a.q, a.k_cache, a.v_cache, a.block_tables,
+          a.context_lens, a.query_start, scale_log2, out_scale, log2_bs, a.num_seqs,
+          a.num_kv_heads, a.num_heads, group, chunks, a.max_blocks_per_seq, a.num_blocks, nqb);
   return (int)hipGetLastError();
 }
 
-template <int DT, int D>
+template <int DT, int D, bool KV8>
 int launch_d(const PrefillArgs &a) {
   const int group = a.num_heads / a.num_kv_heads;
-  if (group == 1) return launch_hc<DT, D, 1, 1>(a);
-  if (group == 2) return launch_hc<DT, D, 2, 1>(a);
-  return launch_hc<DT, D, 2, 2>(a);
+  if (group == 1) return launch_hc<DT, D, 1, 1, KV8>(a);
+  if (group == 2) return launch_hc<DT, D, 2, 1, KV8>(a);
+  return launch_hc<DT, D, 2, 2, KV8>(a);
 }
 
-template <int DT>
+template <int DT, bool KV8>
 int launch_dt(const PrefillArgs &a) {
-  return a.head_dim == 64 ? launch_d<DT, 64>(a) : launch_d<DT, 128>(a);
+  return a.head_dim == 64 ? launch_d<DT, 64, KV8>(a) : launch_d<DT, 128, KV8>(a);
 }
 
 }  // namespace
 
 int launch_prefill(const PrefillArgs &a) {
-  return a.dtype == 1 ? launch_dt<1>(a) : launch_dt<0>(a);
+  if (a.kv_fp8) return a.dtype == 1 ? launch_dt<1, true>(a) : launch_dt<0, true>(a);
+  return a.dtype == 1 ? launch_dt<1, false>(a) : launch_dt<0, false>(a);
 }
 
 }  // namespace pa

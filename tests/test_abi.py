@@ -32,10 +32,10 @@ def test_library_exports_every_declared_symbol():
             "paged_attention_split_waves", "paged_validate_metadata", "pa_strerror",
             "pa_abi_version", "paged_kv_write_fp8", "paged_attention_decode_fp8",
             "paged_attention_decode_append", "paged_attention_prefill",
-            "paged_validate_prefill"} <= set(names)
+            "paged_validate_prefill", "paged_attention_prefill_fp8"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 5
+    assert lib.pa_abi_version() == 6
 
 
 def test_single_hip_runtime():
@@ -256,6 +256,33 @@ def test_prefill_rejects_before_launch(kw, code):
 def test_prefill_empty_is_noop():
     assert _prefill(B=0, out=None, q=None) == 0
     assert _prefill(mq=0, out=None, q=None) == 0
+
+
+def _prefill_fp8(ks=0.02, vs=0.03, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, scale=0.125, bs=16,
+             hkv=8, B=4, hq=32, d=128, mb=128, nb=1000, dtype=1, mq=512, stream=None)
+    a.update(kw)
+    return B.load().paged_attention_prefill_fp8(
+        a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["qs"], a["scale"], ks, vs,
+        a["bs"], a["hkv"], a["B"], a["hq"], a["d"], a["mb"], a["nb"], a["dtype"], a["mq"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=0.0), -3), (dict(vs=-1.0), -3), (dict(ks=float("nan")), -3),
+    (dict(vs=float("inf")), -3), (dict(ks=1e-45), -3),     # 1 / k_scale overflows
+    (dict(dtype=2), -2), (dict(d=96), -3), (dict(mb=4097), -3), (dict(mq=-1), -3),
+    (dict(out=None), -1), (dict(kc=None), -1),
+    (dict(kc=FAKE + 8), -7), (dict(q=FAKE + 8), -7),
+])
+def test_prefill_fp8_rejects_before_launch(kw, code):
+    assert _prefill_fp8(**kw) == code
+
+
+def test_prefill_fp8_empty_is_noop():
+    assert _prefill_fp8(B=0, out=None, q=None) == 0
+    assert _prefill_fp8(mq=0, kc=None, vc=None) == 0
+    assert _prefill_fp8(B=0, ks=0.0) == -3     # scales are checked even with no work
 
 
 @pytest.mark.parametrize("qs,cl,mq,rows,code", [

@@ -4,7 +4,10 @@ element, on ragged batches mixing whole prompts, chunks after a cached
 prefix (prefix and chunk lengths off tile and block edges), one-row chunks
 and empty chunks, over head_dim, block size, GQA group (1 to 16) and dtype;
 and a Llama-3-8B-shaped chunk batch (sampled rows).  Rows outside the
-chunks are never written."""
+chunks are never written.  paged_attention_prefill_fp8 is held to the same
+bar against oracle_prefill_fp8 on E4M3 caches that paged_kv_write_fp8
+filled (the reading of "vLLM framework analysis: how PagedAttention speeds
+up LLM inference 20x", 7)."""
 import numpy as np
 import pytest
 import torch
@@ -35,47 +38,65 @@ def dev_bits(bits, dtype):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(TD[dtype])
 
 
-def run(lengths, chunks, G, hkv, d, bs, dtype, seed, rows=None, v_scale=None, **wkw):
+def run(lengths, chunks, G, hkv, d, bs, dtype, seed, rows=None, v_scale=None, kv8=None,
+        **wkw):
+    """kv8 = (k_scale, v_scale): E4M3 caches and paged_attention_prefill_fp8."""
     w = W.build("pf", lengths, num_heads=G * hkv, num_kv_heads=hkv, head_dim=d,
                 block_size=bs, dtype=dtype, seed=seed, **wkw)
     if v_scale is not None:  # V values times v_scale, kept inside +-65000
         v = np.clip(f64(w.token_v, dtype) * v_scale, -65000.0, 65000.0)
         w.token_v = W.to_bits(v.astype(np.float32), dtype).reshape(w.token_v.shape)
     ksh, vsh = w.cache_shapes()
-    nan = int(np.array([W.NAN_BITS[dtype]], np.uint16).view(np.int16)[0])
-    kc = torch.full(ksh, nan, dtype=torch.int16, device=DEV).view(TD[dtype])
-    vc = torch.full(vsh, nan, dtype=torch.int16, device=DEV).view(TD[dtype])
-    okc, ovc = w.nan_caches()
+    if kv8 is None:
+        nan = int(np.array([W.NAN_BITS[dtype]], np.uint16).view(np.int16)[0])
+        kc = torch.full(ksh, nan, dtype=torch.int16, device=DEV).view(TD[dtype])
+        vc = torch.full(vsh, nan, dtype=torch.int16, device=DEV).view(TD[dtype])
+        okc, ovc = w.nan_caches()
+    else:
+        kc = torch.full(ksh, W.FP8_NAN, dtype=torch.uint8, device=DEV)
+        vc = torch.full(vsh, W.FP8_NAN, dtype=torch.uint8, device=DEV)
+        okc, ovc = w.nan_caches_fp8()
     for which in ("hist", "new"):
         k, v, s = w.write_batch(which)
-        B.paged_kv_write(dev_bits(k, dtype), dev_bits(v, dtype), torch.from_numpy(s).to(DEV),
-                         kc, vc)
-        oracle.kv_write(k, v, s, okc, ovc, bs)
+        kd, vd, sd = dev_bits(k, dtype), dev_bits(v, dtype), torch.from_numpy(s).to(DEV)
+        if kv8 is None:
+            B.paged_kv_write(kd, vd, sd, kc, vc)
+            oracle.kv_write(k, v, s, okc, ovc, bs)
+        else:
+            B.paged_kv_write_fp8(kd, vd, sd, kc, vc, *kv8)
+            oracle.kv_write_fp8(k, v, s, okc, ovc, bs, dtype, *kv8)
     qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
     g = np.random.default_rng(seed + 7)
     q = W.normal_bits(g, (int(qs[-1]), w.num_heads, d), dtype)
     qd = dev_bits(q, dtype)
     out = torch.full_like(qd, float("nan"))
-    say(f"prefill B={len(lengths)} G={G} hkv={hkv} D={d} bs={bs} {dtype} rows={qs[-1]}")
-    B.paged_attention_prefill(out, qd, kc, vc, torch.from_numpy(w.block_tables).to(DEV),
-                              torch.from_numpy(w.context_lens).to(DEV),
-                              torch.from_numpy(qs).to(DEV), w.scale, bs, hkv,
-                              max(chunks) if len(chunks) else 0)
+    say(f"prefill{'_fp8' if kv8 else ''} B={len(lengths)} G={G} hkv={hkv} D={d} bs={bs} "
+        f"{dtype} rows={qs[-1]}")
+    meta = (torch.from_numpy(w.block_tables).to(DEV), torch.from_numpy(w.context_lens).to(DEV),
+            torch.from_numpy(qs).to(DEV), w.scale)
+    mq = max(chunks) if len(chunks) else 0
+    if kv8 is None:
+        B.paged_attention_prefill(out, qd, kc, vc, *meta, bs, hkv, mq)
+    else:
+        B.paged_attention_prefill_fp8(out, qd, kc, vc, *meta, *kv8, bs, hkv, mq)
     torch.cuda.synchronize()
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def ref_of(qr, bt, cl, qsr):
+        if kv8 is None:
+            return oracle.prefill(qr, okc, ovc, bt, cl, qsr, w.scale, bs, dtype)
+        return oracle.prefill_fp8(qr, okc, ovc, bt, cl, qsr, w.scale, bs, dtype, *kv8)
+
     if rows is None:
-        ref = oracle.prefill(q, okc, ovc, w.block_tables, w.context_lens, qs, w.scale, bs,
-                             dtype)
-        return got, ref, None
+        return got, ref_of(q, w.block_tables, w.context_lens, qs), None
     # sampled rows: the oracle over those rows only (each row on its own)
     ref = np.zeros((len(rows), w.num_heads, d))
     seq_of = np.searchsorted(qs, rows, side="right") - 1
     for j, (r, s) in enumerate(zip(rows, seq_of)):
         L = int(w.context_lens[s])
         p = L - (qs[s + 1] - qs[s]) + (r - qs[s])
-        ref[j] = oracle.prefill(q[r:r + 1], okc, ovc, w.block_tables[s:s + 1],
-                                np.array([p + 1], np.int32), np.array([0, 1], np.int32),
-                                w.scale, bs, dtype)[0]
+        ref[j] = ref_of(q[r:r + 1], w.block_tables[s:s + 1], np.array([p + 1], np.int32),
+                        np.array([0, 1], np.int32))[0]
     return got[rows], ref, None
 
 
@@ -167,3 +188,35 @@ def test_prefill_leaves_other_rows():
     o = out.float().cpu().numpy()
     assert np.all(o[10:] == 7.0)
     assert np.all(np.isfinite(o[:10])) and not np.all(o[:10] == 7.0)
+
+
+KS8, VS8 = 0.02, 0.03   # N(0, 1) data: codes stay well inside +-448
+
+
+@pytest.mark.parametrize("i,G,d,bs,dt", CASES[:6])
+def test_prefill_fp8_ragged(i, G, d, bs, dt):
+    g = np.random.default_rng(950 + i)
+    lengths = [1, 17, 64, 130, 200, 97, 33, 300]
+    chunks = [1, 17, 64, 66, 1, 0, 20, 129]
+    hkv = int(g.integers(1, 3))
+    got, ref, _ = run(lengths, chunks, G, hkv, d, bs, dt, 2000 + i, kv8=(KS8, VS8))
+    check(got, ref, dt, f"fp8 ragged{i}")
+
+
+def test_prefill_fp8_llama8b_chunks():
+    """The Llama-3-8B chunk batch over E4M3 caches; sampled rows."""
+    g = np.random.default_rng(6)
+    rows = np.sort(g.choice(4 * 512, 48, replace=False))
+    got, ref, _ = run([2048] * 4, [512] * 4, 4, 8, 128, 16, W.BF16, 56, rows=rows,
+                      kv8=(KS8, VS8))
+    check(got, ref, W.BF16, "fp8 llama8b chunks")
+
+
+@pytest.mark.parametrize("ks,vs", [(1.0 / 64, 2.0 ** -6), (0.5, 7.0)])
+def test_prefill_fp8_scales(ks, vs):
+    """Other scales: with 2^-6 the codes reach a few hundred (near E4M3's
+    448); with 0.5 and 7 they are small, and with 7 about a tenth of the V
+    codes are subnormal (below 2^-6).  The dequantized values keep the data's size, and so does
+    out: the tolerance is unchanged."""
+    got, ref, _ = run([150, 77], [150, 9], 2, 2, 64, 16, W.F16, 70, kv8=(ks, vs))
+    check(got, ref, W.F16, f"fp8 ks={ks} vs={vs}")
