@@ -33,14 +33,18 @@ METRIC = "paged decode KV-read HBM GB/s (% of peak) + seq-tokens/s, Llama-3-8B s
 HBM_PEAK_GBS = 8000.0
 WORKLOADS = ("llama8b", "long", "prefix", "short_bs8", "short_bs16", "short_bs32", "tiny")
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SRC = os.path.join(ROOT, "pagedattention_kv_cache_paged_amd", "csrc", "pa_decode.hip")
 SPLIT_KERNEL = "decode_split_kernel"
+PREFILL_KERNEL = "prefill_kernel"
+PREFILL_TAG = "llama8b_chunks"
+# op -> (dominant kernel, its source file)
+KERNELS = {"decode": (SPLIT_KERNEL, "pa_decode.hip"), "prefill": (PREFILL_KERNEL, "pa_prefill.hip")}
 COPY_BYTES = 512 << 20   # plain device copy used to calibrate the byte counters
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(op: str = "decode") -> str:
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
+    src = os.path.join(ROOT, "pagedattention_kv_cache_paged_amd", "csrc", KERNELS[op][1])
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
@@ -53,14 +57,17 @@ def kv_bytes_per_token(w, fp8: bool) -> int:
     return 2 * w.num_kv_heads * w.head_dim * (1 if fp8 else 2)
 
 
-def counters_path(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"{SPLIT_KERNEL}_{workload}_counters.txt")
+def counters_path(tag: str, op: str = "decode") -> str:
+    return os.path.join(ROOT, "profiles", f"{KERNELS[op][0]}_{tag}_counters.txt")
 
 
-def summarize_counters(fetch_dir: str, write_dir: str, workload: str, fp8: bool) -> dict:
-    """Per-launch HBM bytes of the split pass from two rocprofv3 --pmc runs
-    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
-    counter reads for the plain COPY_BYTES device copy of the same run."""
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, fp8: bool,
+                       op: str = "decode") -> dict:
+    """Per-launch HBM bytes of the op's dominant kernel (the decode split
+    pass, or the prefill kernel) from two rocprofv3 --pmc runs (FETCH_SIZE,
+    WRITE_SIZE; KiB per dispatch), each scaled by what the same counter reads
+    for the plain COPY_BYTES device copy of the same run."""
+    kernel = KERNELS[op][0]
     import csv
     import glob
 
@@ -74,21 +81,23 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, fp8: bool)
                 if r["Counter_Name"] != counter:
                     continue
                 v = float(r["Counter_Value"]) * 1024.0
-                if SPLIT_KERNEL in r["Kernel_Name"]:
+                if kernel in r["Kernel_Name"]:
                     split.append(v)
                 elif "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= (1 << 16):
                     copy.append(v)
         if not split or not copy:
-            raise SystemExit(f"{counter}: found {len(split)} split and {len(copy)} copy dispatches")
+            raise SystemExit(f"{counter}: found {len(split)} {kernel} and {len(copy)} copy "
+                             f"dispatches")
         return float(np.mean(split)), float(np.mean(copy))
 
     f_split, f_copy = per_dispatch(fetch_dir, "FETCH_SIZE")
     w_split, w_copy = per_dispatch(write_dir, "WRITE_SIZE")
     f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
-    opts = f"--workload {workload}" + (" --kv-dtype fp8" if fp8 else "")
+    opts = ("--op prefill" if op == "prefill" else f"--workload {workload}") + \
+        (" --kv-dtype fp8" if fp8 else "")
     return {
-        "kernel": SPLIT_KERNEL, "workload": workload + ("_fp8" if fp8 else ""),
-        "source_sha256": kernel_source_hash(),
+        "kernel": kernel, "workload": workload + ("_fp8" if fp8 else ""),
+        "source_sha256": kernel_source_hash(op),
         "fetch_bytes_raw": f_split, "write_bytes_raw": w_split,
         "copy_bytes": COPY_BYTES, "copy_fetch_raw": f_copy, "copy_write_raw": w_copy,
         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
@@ -106,17 +115,29 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, fp8: bool)
     }
 
 
-def recorded_traffic(workload: str):
-    """Counter-measured bytes per split launch, if recorded for this workload
-    and for the kernel source as it is now; else None."""
+def recorded_traffic(tag: str, op: str = "decode"):
+    """Counter-measured bytes per launch of the op's dominant kernel, if
+    recorded for this workload and for the kernel source as it is now; else
+    None."""
     try:
-        with open(counters_path(workload)) as f:
+        with open(counters_path(tag, op)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("source_sha256") != kernel_source_hash():
+    if rec.get("workload") != tag or rec.get("source_sha256") != kernel_source_hash(op):
         return None
     return rec.get("traffic_bytes")
+
+
+def copy_calibration(torch, dev):
+    """Three plain COPY_BYTES device copies: what FETCH_SIZE and WRITE_SIZE
+    read for them scales the kernel's own counts to bytes."""
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def make_workload(name, placement="random"):
@@ -310,7 +331,6 @@ def bench_swap_blocks(args, torch, B, dev, lib):
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 MFMA, MI355X
-PREFILL_KERNEL = "prefill_kernel"
 
 
 def bench_prefill(args, torch, B, W, dev, lib, fp8=False):
@@ -373,6 +393,8 @@ def bench_prefill(args, torch, B, W, dev, lib, fp8=False):
     b.record(stream)
     torch.cuda.synchronize()
     us = a.elapsed_time(b) / K * 1e3
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     positions = np.arange(cached, cached + chunk, dtype=np.float64)
     flops = nseq * 32 * float(np.sum(4.0 * 128 * (positions + 1)))
     tflops = flops / (us * 1e-6) / 1e12
@@ -390,7 +412,9 @@ def bench_prefill(args, torch, B, W, dev, lib, fp8=False):
         "roofline": {"kernel": PREFILL_KERNEL, "bound": "mfma", "achieved": round(tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "avg_launch_us": round(us, 3),
-                     "traffic": None, "flops_per_launch": flops},
+                     "traffic": recorded_traffic(PREFILL_TAG + ("_fp8" if fp8 else ""),
+                                                 "prefill"),
+                     "flops_per_launch": flops},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -448,16 +472,20 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (byte-counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write the split pass's per-launch HBM bytes from two rocprofv3 "
-                         "--pmc runs to profiles/ and exit (no GPU needed)")
+                    help="write the dominant kernel's per-launch HBM bytes (decode split pass or "
+                         "prefill kernel) from two rocprofv3 --pmc runs to profiles/ and exit")
     args = ap.parse_args()
 
     fp8 = args.kv_dtype == "fp8"
-    tag = args.workload + ("_fp8" if fp8 else "")
+    cop = "prefill" if args.op == "prefill" else "decode"
+    base = PREFILL_TAG if cop == "prefill" else args.workload
+    tag = base + ("_fp8" if fp8 else "")
     if args.summarize_counters:
-        rec = summarize_counters(*args.summarize_counters, args.workload, fp8)
-        os.makedirs(os.path.dirname(counters_path(tag)), exist_ok=True)
-        with open(counters_path(tag), "w") as f:
+        if args.op not in ("decode", "prefill"):
+            raise SystemExit("--summarize-counters covers --op decode and --op prefill")
+        rec = summarize_counters(*args.summarize_counters, base, fp8, cop)
+        os.makedirs(os.path.dirname(counters_path(tag, cop)), exist_ok=True)
+        with open(counters_path(tag, cop), "w") as f:
             f.write(json.dumps(rec, indent=1) + "\n")
         print(json.dumps(rec))
         return
@@ -626,12 +654,7 @@ def main():
         e[3].record(stream)
     torch.cuda.synchronize()
     if args.copy_calibration:
-        src = torch.ones(COPY_BYTES // 2, dtype=torch.int16, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(torch, dev)
     t_write = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e3   # us
     t_part = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
     t_merge = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
