@@ -80,17 +80,23 @@ def test_fused_decode_step_graph_replay():
         assert torch.equal(vc_g.view(torch.int16), vc_e.view(torch.int16))
 
 
-def test_prefill_graph_replay():
+@pytest.mark.parametrize("kv8", [False, True], ids=["f16", "e4m3"])
+def test_prefill_graph_replay(kv8):
     lengths, chunks = [300, 97, 512, 40], [300, 33, 128, 1]
     w = W.build("graphpf", lengths, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
                 dtype=W.F16, seed=23)
     tdt = torch.float16
     ksh, vsh = w.cache_shapes()
-    kc = torch.zeros(ksh, dtype=tdt, device=DEV)
-    vc = torch.zeros(vsh, dtype=tdt, device=DEV)
+    ct = torch.uint8 if kv8 else tdt
+    kc = torch.zeros(ksh, dtype=ct, device=DEV)
+    vc = torch.zeros(vsh, dtype=ct, device=DEV)
     for which in ("hist", "new"):
         k, v, s = w.write_batch(which)
-        B.paged_kv_write(dev_bits(k, tdt), dev_bits(v, tdt), torch.from_numpy(s).to(DEV), kc, vc)
+        kd, vd, sd = dev_bits(k, tdt), dev_bits(v, tdt), torch.from_numpy(s).to(DEV)
+        if kv8:
+            B.paged_kv_write_fp8(kd, vd, sd, kc, vc, 0.02, 0.03)
+        else:
+            B.paged_kv_write(kd, vd, sd, kc, vc)
     qs = torch.tensor(np.concatenate([[0], np.cumsum(chunks)]), dtype=torch.int32, device=DEV)
     bt = torch.from_numpy(w.block_tables).to(DEV)
     cl = torch.from_numpy(w.context_lens).to(DEV)
@@ -99,7 +105,11 @@ def test_prefill_graph_replay():
     out = torch.empty_like(q)
 
     def call(o):
-        B.paged_attention_prefill(o, q, kc, vc, bt, cl, qs, w.scale, 16, 2, max(chunks))
+        if kv8:
+            B.paged_attention_prefill_fp8(o, q, kc, vc, bt, cl, qs, w.scale, 0.02, 0.03, 16, 2,
+                                          max(chunks))
+        else:
+            B.paged_attention_prefill(o, q, kc, vc, bt, cl, qs, w.scale, 16, 2, max(chunks))
 
     call(out)
     torch.cuda.synchronize()
@@ -108,7 +118,7 @@ def test_prefill_graph_replay():
         call(out)
     gen = torch.Generator(device="cpu").manual_seed(4)
     for r in range(4):
-        say(f"prefill graph replay {r}")
+        say(f"prefill graph replay {r} kv8={kv8}")
         q.copy_(torch.randn(q.shape, generator=gen).to(tdt).to(DEV))
         g.replay()
         torch.cuda.synchronize()
