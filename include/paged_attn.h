@@ -216,10 +216,12 @@ int paged_attention_decode_fp8(void *out, const void *q, const void *k_cache,
  * at block block_tables[s][(L-1) / block_size], offset (L-1) % block_size,
  * of both caches, and out[s] is the attention of q[s] over all L tokens, the
  * new one included.  That is paged_kv_write with slot_mapping[s] = that slot,
- * followed by paged_attention_decode, in two launches instead of three: the
- * split pass covers positions 0 .. L-2 and the merge pass adds the new token
- * as one more log-sum-exp partial and stores it.  L = 0: out[s] = 0 and no
- * store; a table entry outside [0, num_blocks) for position L-1: no store.
+ * followed by paged_attention_decode, in two launches instead of three, with
+ * the same arithmetic (the outputs and caches are bit-identical to those two
+ * calls): the split pass's wavefront that holds position L-1 takes its K/V
+ * from k_new / v_new rather than the cache and stores them into the slot.
+ * L = 0: out[s] = 0 and no store; a table entry outside [0, num_blocks) for
+ * position L-1: no store (the token still enters the attention).
  *
  * kv_fp8 = 0: 16-bit caches, k_scale / v_scale ignored.  kv_fp8 = 1: E4M3
  * caches as for paged_kv_write_fp8 / paged_attention_decode_fp8; the new

@@ -173,25 +173,35 @@ struct Frag<D, true> {
 constexpr int kBuf = 2;
 
 // KV8: the caches hold E4M3 codes; scale_log2 then carries k_scale and
-// out_scale is v_scale (1 for 16-bit caches).
-template <int DT, int D, int BS, bool KV8>
+// out_scale is v_scale (1 for 16-bit caches).  APPEND: the fused decode
+// step, whose new tokens come from k_new / v_new (position L - 1).
+template <int DT, int D, int BS, bool KV8, bool APPEND>
 __global__ __launch_bounds__(kWave) void decode_split_kernel(
     uint16_t *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml,
     int32_t *__restrict__ ws_cu, const uint16_t *__restrict__ q,
-    const void *__restrict__ k_cache, const void *__restrict__ v_cache,
+    void *__restrict__ k_cache, void *__restrict__ v_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    float scale_log2, float out_scale, int num_seqs, int num_kv_heads, int num_heads,
-    int group, int max_blocks, int64_t num_blocks, int waves, int slots, int append) {
+    const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+    float scale_log2, float out_scale, float k_inv, float v_inv, int num_seqs,
+    int num_kv_heads, int num_heads, int group, int max_blocks, int64_t num_blocks,
+    int waves, int slots) {
   using E = Elem<DT>;
   using CT = std::conditional_t<KV8, uint8_t, uint16_t>;  // cache element
   constexpr int KSTEPS = D / 32;  // 16x16x32 MFMAs per QK tile
   constexpr int DTILES = D / 16;  // 16x16x16 MFMAs per PV tile
+  constexpr int PER = D / kWave;  // elements of a K or V row per lane
   // LDS: cu[num_seqs + 1], lens[num_seqs], then (16-byte aligned) the
-  // current segment's query fragments, lane-major per k-step.
+  // current segment's query fragments, lane-major per k-step; with APPEND
+  // also the new token's K and V rows of the current segment's sequence
+  // (16-bit), and for KV8 their E4M3 codes.
   extern __shared__ __align__(16) int lds[];
   int *cu = lds;
   int *lens = lds + num_seqs + 1;
   u32x4 *q_lds = reinterpret_cast<u32x4 *>(lds + ((2 * num_seqs + 1 + 3) & ~3));
+  uint16_t *kn_raw = reinterpret_cast<uint16_t *>(q_lds + KSTEPS * kWave);
+  uint16_t *vn_raw = kn_raw + D;
+  CT *kn_lds = KV8 ? reinterpret_cast<CT *>(vn_raw + D) : reinterpret_cast<CT *>(kn_raw);
+  CT *vn_lds = KV8 ? kn_lds + D : reinterpret_cast<CT *>(vn_raw);
 
   const int kvh = blockIdx.x % num_kv_heads;
   const int j = blockIdx.x / num_kv_heads;
@@ -202,22 +212,21 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
 
   // Tile prefix over all sequences (the same in every wavefront).  Range-0
   // wavefronts also write the zero rows of sequences with nothing to attend.
-  // With a fused append the last position is the new token, which the
-  // merge pass adds: this pass covers the L - 1 tokens before it and leaves
-  // every output row to the merge pass.
+  // With a fused append the last position L - 1 is the new token: the
+  // wavefront holding that tile takes its K and V from k_new / v_new
+  // instead of the cache and stores them into the cache slot.
   int carry = 0;
   for (int c = 0; c < num_seqs; c += kWave) {
     const int s = c + lane;
     int len = s < num_seqs ? context_lens[s] : 0;
     len = min(max(len, 0), max_len);
-    if (append) len = max(len - 1, 0);
     const int incl = wave_incl_scan((len + kTile - 1) / kTile) + carry;
     if (s < num_seqs) {
       cu[s + 1] = incl;
       lens[s] = len;
     }
     carry = __shfl(incl, kWave - 1);
-    if (j == 0 && !append) {
+    if (j == 0) {
       uint64_t zero = __ballot(s < num_seqs && len == 0);
       while (zero) {
         const int zs = c + __builtin_ctzll(zero);
@@ -267,15 +276,22 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
     b0 = tbl[it >> 1];
     boff = (it & 1) * kTile;
   }
+  // Fused append: the sequence's last tile holds the new token at row
+  // nvalid - 1; nblk is its block (-1 if the id is outside the pool: the
+  // token then enters the attention but is not stored).
+  const bool is_new = APPEND && it == ntiles_sq - 1;
+  const int nraw = (BS == 8 && nvalid > 8) ? b1 : b0;
+  const int nblk = (is_new && nraw >= 0 && nraw < num_blocks) ? nraw : -1;
   b0 = (b0 >= 0 && b0 < num_blocks) ? b0 : 0;  // ids outside the pool: stay inside it
   b1 = (b1 >= 0 && b1 < num_blocks) ? b1 : 0;
   const int seg_end = (it == ntiles_sq - 1 || tau == t1 - 1) ? 1 : 0;
-  const int whole = (!append && first >= t0 && first + ntiles_sq <= t1) ? 1 : 0;
+  const int whole = (first >= t0 && first + ntiles_sq <= t1) ? 1 : 0;
   const uint64_t ends = __ballot(seg_end && lane < cnt);  // bit i: a segment ends at tile i
   // The flags of tile t0 + lane in one word, so that one readlane per tile
-  // fetches them: bits 0-4 valid tokens, 5 segment end, 6 whole sequence.
-  constexpr int kEnd = 1 << 5, kWhole = 1 << 6;
-  const int meta = nvalid | (seg_end ? kEnd : 0) | (whole ? kWhole : 0);
+  // fetches them: bits 0-4 valid tokens, 5 segment end, 6 whole sequence,
+  // 7 the sequence's new token (fused append).
+  constexpr int kEnd = 1 << 5, kWhole = 1 << 6, kNew = 1 << 7;
+  const int meta = nvalid | (seg_end ? kEnd : 0) | (whole ? kWhole : 0) | (is_new ? kNew : 0);
 
   // Query fragment of the current segment and, one segment ahead, of the
   // next.  Lane (row, grp) holds 8 dims of head row per k-step: dims
@@ -302,12 +318,38 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // next segment's, prefetched one segment ahead, is held in registers.
   // (Two register sets swapped at segment ends make the compiler copy a
   // fresh load, which waits for it and drains the ring.)
+  // With APPEND the new token's K and V rows go the same way, PER elements
+  // per lane.
+  uint32_t knx[PER], vnx[PER];
+  auto load_new = [&](int idx) {
+    if constexpr (APPEND) {
+      const int s = __builtin_amdgcn_readlane(sq, idx);
+      const int64_t src = ((int64_t)s * num_kv_heads + kvh) * D + lane * PER;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        knx[i] = k_new[src + i];
+        vnx[i] = v_new[src + i];
+      }
+    }
+  };
+  auto publish_new = [&]() {
+    if constexpr (APPEND) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        kn_raw[lane * PER + i] = (uint16_t)knx[i];
+        vn_raw[lane * PER + i] = (uint16_t)vnx[i];
+      }
+    }
+  };
   u32x4 qnext[KSTEPS];
   load_q(qnext, 0);
+  load_new(0);
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) q_lds[ks * kWave + lane] = qnext[ks];
+  publish_new();
   __builtin_amdgcn_sched_barrier(0);
   load_q(qnext, next_first(__builtin_ctzll(ends)));
+  load_new(next_first(__builtin_ctzll(ends)));
   const int64_t blk_stride = (int64_t)num_kv_heads * BS * D;  // elements per block
   const CT *kbase = static_cast<const CT *>(k_cache) + (int64_t)kvh * BS * D;
   const CT *vbase = static_cast<const CT *>(v_cache) + (int64_t)kvh * D * BS;
@@ -372,6 +414,58 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   auto step = [&](Frag<D, KV8> &f, int idx) {
     const int mt = __builtin_amdgcn_readlane(meta, idx);
     const int n = mt & 31;
+    if (APPEND && (mt & kNew)) {
+      // The new token (row r of the tile) comes from k_new / v_new, not
+      // from its cache slot, which this wavefront now fills.  Lanes of A-row
+      // r hold the token's K pieces; lanes of quarter r / 4 hold element
+      // r % 4 of each V^T fragment.  E4M3 caches: the wave first quantises
+      // the rows, PER elements per lane (the lane's own LDS writes).
+      const int r = n - 1;
+      const int e = r & 3;
+      if constexpr (KV8) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int d = lane * PER + i;
+          kn_lds[d] = (uint8_t)e4m3_code(elem_to_float<DT>(kn_raw[d]) * k_inv);
+          vn_lds[d] = (uint8_t)e4m3_code(elem_to_float<DT>(vn_raw[d]) * v_inv);
+        }
+        __syncthreads();  // the codes of every lane before the reads below
+      }
+      if (row == r) {
+#pragma unroll
+        for (int h = 0; h < (KV8 ? D / 64 : KSTEPS); ++h)
+          f.k[h] = *(const u32x4 *)(kn_lds + (KV8 ? 64 * h + 16 * grp : 32 * h + 8 * grp));
+      }
+      if (grp == (r >> 2)) {
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) {
+          const uint32_t x = vn_lds[dt * 16 + row];
+          if constexpr (KV8) {
+            f.v[dt] = (f.v[dt] & ~(0xffu << (8 * e))) | (x << (8 * e));
+          } else if (e >> 1) {
+            f.v[dt].y = (e & 1) ? ((f.v[dt].y & 0xffffu) | (x << 16)) : ((f.v[dt].y & 0xffff0000u) | x);
+          } else {
+            f.v[dt].x = (e & 1) ? ((f.v[dt].x & 0xffffu) | (x << 16)) : ((f.v[dt].x & 0xffff0000u) | x);
+          }
+        }
+      }
+      const int nb = __builtin_amdgcn_readlane(nblk, idx);
+      if (nb >= 0) {
+        const int off = BS == 8 ? (r & 7) : (BS == 16 ? r : __builtin_amdgcn_readlane(boff, idx) + r);
+        const int64_t bh = (int64_t)nb * num_kv_heads + kvh;
+        CT *kd = static_cast<CT *>(k_cache) + (bh * BS + off) * D;
+        CT *vd = static_cast<CT *>(v_cache) + bh * D * BS + off;
+        if (row == r) {
+#pragma unroll
+          for (int h = 0; h < (KV8 ? D / 64 : KSTEPS); ++h)
+            *(u32x4 *)(kd + (KV8 ? 64 * h + 16 * grp : 32 * h + 8 * grp)) = f.k[h];
+        }
+        if (grp == (r >> 2)) {
+#pragma unroll
+          for (int dt = 0; dt < DTILES; ++dt) vd[(dt * 16 + row) * BS] = vn_lds[dt * 16 + row];
+        }
+      }
+    }
     u32x4 qf[KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = q_lds[ks * kWave + lane];
@@ -475,9 +569,12 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
       // which starts after the next segment end following tile idx.
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) q_lds[ks * kWave + lane] = qnext[ks];
+      publish_new();
       __builtin_amdgcn_sched_barrier(0);
       const uint64_t later = idx + 1 < kWave ? ends & (~0ull << (idx + 1)) : 0ull;
-      load_q(qnext, later ? next_first(__builtin_ctzll(later)) : cnt - 1);
+      const int nf = later ? next_first(__builtin_ctzll(later)) : cnt - 1;
+      load_q(qnext, nf);
+      load_new(nf);
     }
   };
 
@@ -558,146 +655,6 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
   }
 }
 
-// The merge of a decode step with the append fused in: the sequence's new
-// token (position L-1, which the split pass left out) joins as one more
-// partial with m = its score, l = 1, o = its V row, and the wave of each
-// group's first query head stores that token's K and V into the caches at
-// position L-1 of the block table, as the append step would (KV8: as E4M3
-// codes of x * k_inv / v_inv, whose values then enter the attention).
-// Every output row is written here, zeros for L = 0.
-template <int DT, int D, bool KV8>
-__global__ __launch_bounds__(kWave) void decode_merge_append_kernel(
-    uint16_t *__restrict__ out, const float *__restrict__ ws_o,
-    const float *__restrict__ ws_ml, const int32_t *__restrict__ ws_cu, int num_seqs,
-    int num_heads, int waves, int slots, const uint16_t *__restrict__ q,
-    const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
-    void *__restrict__ k_cache, void *__restrict__ v_cache,
-    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    float scale_log2, float v_scale, float k_inv, float v_inv, int num_kv_heads, int group,
-    int block_size, int max_blocks, int64_t num_blocks) {
-  using E = Elem<DT>;
-  constexpr int PER = D / kWave;  // dims per lane
-  const int head = blockIdx.x;
-  const int seq = blockIdx.y;
-  const int lane = threadIdx.x;
-  uint16_t *op = out + ((int64_t)seq * num_heads + head) * D + lane * PER;
-  const int n_tiles = ws_cu[num_seqs];
-  const int c0 = ws_cu[seq], c1 = ws_cu[seq + 1];
-  const int len = min(max(context_lens[seq], 0), max_blocks * block_size);
-  const int kvh = head / group;
-  // Every load that does not depend on another is issued here, before any
-  // branch, so the kernel waits on one round trip instead of a chain: the
-  // q / k_new / v_new rows, the new token's table entry and the first
-  // partial.  All stay in bounds for any lengths (the table index is
-  // clamped to the sequence's row; the partial index to the head's slots).
-  const int64_t src = ((int64_t)seq * num_kv_heads + kvh) * D + lane * PER;
-  uint32_t qc[PER], kc[PER], vc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    qc[i] = q[((int64_t)seq * num_heads + head) * D + lane * PER + i];
-    kc[i] = k_new[src + i];
-    vc[i] = v_new[src + i];
-  }
-  const int pos = max(len, 1) - 1;  // the new token's position
-  const int64_t blk = block_tables[(int64_t)seq * max_blocks + pos / block_size];
-  const int nt = max(n_tiles, 1);
-  const int wv = max(min(waves, n_tiles), 1);  // as in the split pass: all ranges non-empty
-  const int jf = wave_of(c0, nt, wv);
-  const int64_t base = (int64_t)head * slots + jf + seq;
-  const f32x2 *ml = (const f32x2 *)(ws_ml + base * 2);
-  const float *o = ws_o + base * D + lane * PER;
-  const f32x2 ml0 = ml[0];
-  float o0[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) o0[i] = o[i];
-
-  if (len == 0) {  // nothing to attend and nothing to append
-    if constexpr (PER == 2) *(uint32_t *)op = 0u;
-    else op[0] = 0;
-    return;
-  }
-  // The new token opens the running combination: M the max so far (log2
-  // units), den = sum c_p, num = sum c_p o_p, with c_p = l_p * 2^(m_p - M);
-  // the new token enters with m = its score, l = 1, o = V.
-  float big, den = 1.f;
-  float num[PER];
-  {
-    float qe[PER], ke[PER], ve[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      qe[i] = elem_to_float<DT>(qc[i]);
-      if constexpr (KV8) {
-        kc[i] = e4m3_code(elem_to_float<DT>(kc[i]) * k_inv);
-        vc[i] = e4m3_code(elem_to_float<DT>(vc[i]) * v_inv);
-        ke[i] = e4m3_value(kc[i]);
-        ve[i] = e4m3_value(vc[i]) * v_scale;
-      } else {
-        ke[i] = elem_to_float<DT>(kc[i]);
-        ve[i] = elem_to_float<DT>(vc[i]);
-      }
-    }
-    float dot = 0.f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) dot = fmaf(qe[i], ke[i], dot);
-#pragma unroll
-    for (int m = kWave / 2; m > 0; m >>= 1) dot += __shfl_xor(dot, m);
-    big = dot * scale_log2;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) num[i] = ve[i];
-    if (head % group == 0 && blk >= 0 && blk < num_blocks) {  // one writer per KV head
-      const int64_t bh = blk * num_kv_heads + kvh;
-      const int off = pos % block_size;
-      const int d0 = lane * PER;
-      if constexpr (KV8) {
-        uint8_t *kd = (uint8_t *)k_cache + (bh * block_size + off) * D + d0;
-        uint8_t *vd = (uint8_t *)v_cache + (bh * D + d0) * block_size + off;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          kd[i] = (uint8_t)kc[i];
-          vd[i * block_size] = (uint8_t)vc[i];
-        }
-      } else {
-        uint16_t *kd = (uint16_t *)k_cache + (bh * block_size + off) * D + d0;
-        uint16_t *vd = (uint16_t *)v_cache + (bh * D + d0) * block_size + off;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          kd[i] = (uint16_t)kc[i];
-          vd[i * block_size] = (uint16_t)vc[i];
-        }
-      }
-    }
-  }
-  if (c1 > c0) {  // the partials of positions 0 .. L-2 (none when the new token is all)
-    const int np = wave_of(c1 - 1, nt, wv) - jf + 1;
-    // One pass with a running maximum, so each partial's (m, l) and o are
-    // used together: c_p = l_p * 2^(m_p - M) rescaled as M grows.
-    auto combine = [&](f32x2 v, const float (&opv)[PER]) {
-      const float m_new = fmaxf(big, v.x);
-      const float a = __builtin_amdgcn_exp2f(big - m_new);
-      const float c = v.y * __builtin_amdgcn_exp2f(v.x - m_new);
-      den = den * a + c;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) num[i] = num[i] * a + c * opv[i];
-      big = m_new;
-    };
-    combine(ml0, o0);
-#pragma unroll 4
-    for (int p = 1; p < np; ++p) {
-      const f32x2 v = ml[p];
-      float opv[PER];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) opv[i] = o[(int64_t)p * D + i];
-      combine(v, opv);
-    }
-  }
-  const float inv = 1.0f / den;
-  if constexpr (PER == 2) {
-    *(uint32_t *)op = E::pack(num[0] * inv, num[1] * inv);
-  } else {
-    op[0] = (uint16_t)(E::pack(num[0] * inv, 0.f) & 0xffffu);
-  }
-}
-
 template <int DT, int D, int BS>
 int launch_typed(const DecodeArgs &a) {
   // log2(e) folds the exponential's base into the score scale; an E4M3
@@ -708,39 +665,33 @@ int launch_typed(const DecodeArgs &a) {
   hipError_t e = hipSuccess;
   if (a.stages & 1) {
     dim3 grid((unsigned)a.num_kv_heads * (unsigned)a.waves);
+    // LDS: tile prefix and lengths, query fragments, and for the fused
+    // append the new rows (16-bit, plus E4M3 codes).
     const size_t lds = (size_t)((2 * a.num_seqs + 1 + 3) & ~3) * sizeof(int) +
-                       (size_t)(D / 32) * kWave * 16;
-    if (a.kv_fp8)
-      decode_split_kernel<DT, D, BS, true><<<grid, kWave, lds, st>>>(
-          (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, (const uint16_t *)a.q, a.k_cache,
-          a.v_cache, a.block_tables, a.context_lens, scale_log2, a.v_scale, a.num_seqs,
-          a.num_kv_heads, a.num_heads, group, a.max_blocks_per_seq, a.num_blocks, a.waves,
-          a.slots, a.append);
-    else
-      decode_split_kernel<DT, D, BS, false><<<grid, kWave, lds, st>>>(
-          (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, (const uint16_t *)a.q, a.k_cache,
-          a.v_cache, a.block_tables, a.context_lens, scale_log2, 1.0f, a.num_seqs,
-          a.num_kv_heads, a.num_heads, group, a.max_blocks_per_seq, a.num_blocks, a.waves,
-          a.slots, a.append);
+                       (size_t)(D / 32) * kWave * 16 + (a.append ? 6 * D : 0);
+#define PA_SPLIT(KV8, APPEND, OUT_SCALE)                                                      \
+  decode_split_kernel<DT, D, BS, KV8, APPEND><<<grid, kWave, lds, st>>>(                      \
+      (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, (const uint16_t *)a.q, (void *)a.k_cache,  \
+      (void *)a.v_cache, a.block_tables, a.context_lens, (const uint16_t *)a.k_new,           \
+      (const uint16_t *)a.v_new, scale_log2, OUT_SCALE, a.k_inv, a.v_inv, a.num_seqs,         \
+      a.num_kv_heads, a.num_heads, group, a.max_blocks_per_seq, a.num_blocks, a.waves,        \
+      a.slots)
+    if (a.kv_fp8) {
+      if (a.append) PA_SPLIT(true, true, a.v_scale);
+      else PA_SPLIT(true, false, a.v_scale);
+    } else {
+      if (a.append) PA_SPLIT(false, true, 1.0f);
+      else PA_SPLIT(false, false, 1.0f);
+    }
+#undef PA_SPLIT
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
   if (a.stages & 2) {
     dim3 g2((unsigned)a.num_heads, (unsigned)a.num_seqs);
-#define PA_MERGE(KV8)                                                                         \
-  decode_merge_append_kernel<DT, D, KV8><<<g2, kWave, 0, st>>>(                               \
-      (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, a.num_seqs, a.num_heads, a.waves, a.slots, \
-      (const uint16_t *)a.q, (const uint16_t *)a.k_new, (const uint16_t *)a.v_new,          \
-      (void *)a.k_cache, (void *)a.v_cache, a.block_tables, a.context_lens, scale_log2,       \
-      a.v_scale, a.k_inv, a.v_inv, a.num_kv_heads, group, a.block_size,                       \
-      a.max_blocks_per_seq, a.num_blocks)
-    if (!a.append)
-      decode_merge_kernel<DT, D><<<g2, kWave, 0, st>>>(
-          (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, a.num_seqs, a.num_heads, a.waves,
-          a.slots);
-    else if (a.kv_fp8) PA_MERGE(true);
-    else PA_MERGE(false);
-#undef PA_MERGE
+    decode_merge_kernel<DT, D><<<g2, kWave, 0, st>>>((uint16_t *)a.out, a.ws_o, a.ws_ml,
+                                                     a.ws_cu, a.num_seqs, a.num_heads,
+                                                     a.waves, a.slots);
     e = hipGetLastError();
   }
   return (int)e;

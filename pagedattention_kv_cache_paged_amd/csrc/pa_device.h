@@ -25,17 +25,6 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
   return sign | code;
 }
 
-// Value of an E4M3 code (exact in fp32): subnormals m * 2^-9, normals
-// (1 + m/8) * 2^(e-7); 0x7f / 0xff are NaN.
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  float a;
-  if ((c & 0x7fu) == 0x7fu) a = __uint_as_float(0x7fc00000u);
-  else if (e == 0) a = (float)m * 0.001953125f;
-  else a = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (c & 0x80u) ? -a : a;
-}
-
 // 16-bit element (binary16 when DT == 0, bfloat16 when DT == 1) as fp32.
 template <int DT>
 __device__ __forceinline__ float elem_to_float(uint32_t bits16) {

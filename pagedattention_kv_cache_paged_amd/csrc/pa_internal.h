@@ -43,8 +43,8 @@ struct DecodeArgs {
   int32_t stages;      // bit 0: split pass, bit 1: merge pass
   // Fused append: the new token of each sequence (k_new, v_new [num_seqs,
   // num_kv_heads, head_dim], the q dtype) is context position L-1.  The
-  // split pass then attends over positions 0 .. L-2 only, and the merge
-  // pass adds the new token and stores it into its cache slot.
+  // split pass's wavefront holding that position takes the token's K and V
+  // from these rows instead of the cache and stores them into its slot.
   int32_t append;
   const void *k_new;
   const void *v_new;

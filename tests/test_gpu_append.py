@@ -189,28 +189,48 @@ def test_append_edges(bs, pt):
             assert np.array_equal(got[s, h], vn[s, h // w.group]), (s, h)
 
 
-def test_append_matches_separate_calls():
-    """The fused step and paged_kv_write + paged_attention_decode leave
-    bit-identical caches and outputs within the tolerance of each other."""
+@pytest.mark.parametrize("fp8", [False, True], ids=["native", "e4m3"])
+@pytest.mark.parametrize("pt", [0, 16])
+def test_append_matches_separate_calls(fp8, pt):
+    """The fused step does the arithmetic of paged_kv_write (or _fp8) followed
+    by paged_attention_decode (or _fp8): both leave bit-identical caches and
+    bit-identical outputs, whether a sequence is held by one wavefront or
+    split across many (partition of one tile)."""
     w = W.llama8b()
-    got, kc, vc = run_append(w)
+    say(f"append vs separate fp8={fp8} pt={pt}")
+    got, kc, vc = run_append(w, fp8=fp8, pt=pt)
     ksh, vsh = w.cache_shapes()
-    nan = int(np.array([W.NAN_BITS[w.dtype]], np.uint16).view(np.int16)[0])
-    kc2 = torch.full(ksh, nan, dtype=torch.int16, device=DEV).view(TD[w.dtype])
-    vc2 = torch.full(vsh, nan, dtype=torch.int16, device=DEV).view(TD[w.dtype])
+    if fp8:
+        kc2 = torch.full(ksh, W.FP8_NAN, dtype=torch.uint8, device=DEV)
+        vc2 = torch.full(vsh, W.FP8_NAN, dtype=torch.uint8, device=DEV)
+    else:
+        nan = int(np.array([W.NAN_BITS[w.dtype]], np.uint16).view(np.int16)[0])
+        kc2 = torch.full(ksh, nan, dtype=torch.int16, device=DEV).view(TD[w.dtype])
+        vc2 = torch.full(vsh, nan, dtype=torch.int16, device=DEV).view(TD[w.dtype])
     for which in ("hist", "new"):
         k, v, s = w.write_batch(which)
-        B.paged_kv_write(dev_bits(k, w.dtype), dev_bits(v, w.dtype), torch.from_numpy(s).to(DEV),
-                         kc2, vc2)
+        args = (dev_bits(k, w.dtype), dev_bits(v, w.dtype), torch.from_numpy(s).to(DEV),
+                kc2, vc2)
+        if fp8:
+            B.paged_kv_write_fp8(*args, KS, VS)
+        else:
+            B.paged_kv_write(*args)
     q = dev_bits(w.q, w.dtype)
     out2 = torch.empty_like(q)
-    B.paged_attention_decode(out2, q, kc2, vc2, torch.from_numpy(w.block_tables).to(DEV),
-                             torch.from_numpy(w.context_lens).to(DEV), w.scale, w.block_size,
-                             w.num_kv_heads)
+    bt = torch.from_numpy(w.block_tables).to(DEV)
+    cl = torch.from_numpy(w.context_lens).to(DEV)
+    if fp8:
+        B.paged_attention_decode_fp8(out2, q, kc2, vc2, bt, cl, w.scale, KS, VS, w.block_size,
+                                     w.num_kv_heads, partition_tokens=pt)
+    else:
+        B.paged_attention_decode(out2, q, kc2, vc2, bt, cl, w.scale, w.block_size,
+                                 w.num_kv_heads, partition_tokens=pt)
     torch.cuda.synchronize()
-    assert np.array_equal(kc, host_bits(kc2)) and np.array_equal(vc, host_bits(vc2))
-    a, b = f64(got, w.dtype), f64(host_bits(out2), w.dtype)
-    assert np.all(np.abs(a - b) <= 2 * (ATOL + RTOL * np.abs(b)))
+    if fp8:
+        assert np.array_equal(kc, kc2.cpu().numpy()) and np.array_equal(vc, vc2.cpu().numpy())
+    else:
+        assert np.array_equal(kc, host_bits(kc2)) and np.array_equal(vc, host_bits(vc2))
+    assert np.array_equal(got, host_bits(out2)), "fused and separate outputs differ"
 
 
 # ---- E4M3 caches ------------------------------------------------------------
