@@ -360,10 +360,14 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // what a clamped lane reads is masked away by step().  K and V are read
   // once per launch, so they bypass the caches' normal replacement.
   auto load = [&](Frag<D, KV8> &f, int idx) {
-    const int n = __builtin_amdgcn_readlane(meta, idx) & 31;
+    const int mt = __builtin_amdgcn_readlane(meta, idx);
+    const int n = mt & 31;
     const int ka = __builtin_amdgcn_readlane(b0, idx);
     const int ktok = min(row, n - 1);
-    const int vtok = min(grp * 4, (n - 1) & ~3);
+    // V of the new token's tile is read at every position (the step writes
+    // that tile's V back whole); elsewhere lanes past the valid tokens
+    // repeat the last valid group.
+    const int vtok = (APPEND && (mt & kNew)) ? grp * 4 : min(grp * 4, (n - 1) & ~3);
     const CT *kp, *vp;
     if constexpr (BS == 8) {  // the tile's two blocks: per-lane choice
       const int kz = __builtin_amdgcn_readlane(b1, idx);
@@ -449,20 +453,32 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
           }
         }
       }
+      // Store the token: its K row, and the tile's whole V^T as loaded with
+      // the token in place.  In the dim-major V cache one token touches a
+      // few bytes of every line of the (block, head) region; writing the
+      // tile's lines whole (the other positions with the bytes they hold)
+      // avoids a partial-line write per dimension.  At block size 8 only
+      // the new token's block is written.
       const int nb = __builtin_amdgcn_readlane(nblk, idx);
       if (nb >= 0) {
-        const int off = BS == 8 ? (r & 7) : (BS == 16 ? r : __builtin_amdgcn_readlane(boff, idx) + r);
+        const int bo = BS == 32 ? __builtin_amdgcn_readlane(boff, idx) : 0;
+        const int off = BS == 8 ? (r & 7) : bo + r;
         const int64_t bh = (int64_t)nb * num_kv_heads + kvh;
         CT *kd = static_cast<CT *>(k_cache) + (bh * BS + off) * D;
-        CT *vd = static_cast<CT *>(v_cache) + bh * D * BS + off;
+        CT *vd = static_cast<CT *>(v_cache) + bh * D * BS;
         if (row == r) {
 #pragma unroll
           for (int h = 0; h < (KV8 ? D / 64 : KSTEPS); ++h)
             *(u32x4 *)(kd + (KV8 ? 64 * h + 16 * grp : 32 * h + 8 * grp)) = f.k[h];
         }
-        if (grp == (r >> 2)) {
+        if (BS != 8 || (grp >> 1) == (r >> 3)) {
+          const int t = BS == 8 ? (grp * 4) & 7 : bo + grp * 4;
 #pragma unroll
-          for (int dt = 0; dt < DTILES; ++dt) vd[(dt * 16 + row) * BS] = vn_lds[dt * 16 + row];
+          for (int dt = 0; dt < DTILES; ++dt) {
+            CT *vp = vd + (dt * 16 + row) * BS + t;
+            if constexpr (KV8) *(uint32_t *)vp = f.v[dt];
+            else *(u32x2 *)vp = f.v[dt];
+          }
         }
       }
     }
