@@ -519,7 +519,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures the single-GPU path only: this build has no multi-GPU "
+        print("bench.py measures the single-GPU path only: the library has no multi-GPU "
               "code (the decode shards by sequence or KV head with no exchange); run with "
               "--gpus 1", file=sys.stderr)
         sys.exit(2)

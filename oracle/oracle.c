@@ -175,8 +175,8 @@ static uint16_t v_elem(const uint16_t *v_cache, int64_t block, int kv_head,
 
 /* ---- KV append ---------------------------------------------------------- */
 
-/* Append step of [P3] 2.1: a token's K and V go to "physical block address
- * plus offset inside the block".  The caller has already chosen the slot
+/* Append step of [P3] 2.1: a token's K and V are written at its physical
+ * block's address plus its offset within that block.  The caller has already chosen the slot
  * (block allocated when the sequence's fill count is a multiple of the block
  * size); here every token with a non-negative slot is copied bit for bit into
  * block slot/block_size at offset slot%block_size, for every KV head.
