@@ -229,7 +229,7 @@ def bench_copy_blocks(args, torch, B, W, dev, lib):
     cow_pairs = np.stack([np.full(nforks, shared), ids[1:1 + nforks]], axis=1).astype(np.int64)
     big_pairs = np.stack([ids[:4096], ids[4096:8192]], axis=1).astype(np.int64)
     kc = torch.randint(-30000, 30000, (nb, hkv, bs, d), dtype=torch.int16, device=dev)
-    vc = torch.randint(-30000, 30000, (nb, hkv, d, bs), dtype=torch.int16, device=dev)
+    vc = torch.randint(-30000, 30000, (nb, hkv, bs // 4, d, 4), dtype=torch.int16, device=dev)
     sp = torch.cuda.current_stream().cuda_stream
     stream = torch.cuda.current_stream()
 
@@ -309,9 +309,9 @@ def bench_swap_blocks(args, torch, B, dev, lib):
     out_pairs = torch.from_numpy(np.stack([ids[:n], np.arange(n)], 1).astype(np.int64)).to(dev)
     in_pairs = torch.from_numpy(np.stack([np.arange(n), ids[n:2 * n]], 1).astype(np.int64)).to(dev)
     kc = torch.randint(-30000, 30000, (nd, hkv, bs, d), dtype=torch.int16, device=dev)
-    vc = torch.randint(-30000, 30000, (nd, hkv, d, bs), dtype=torch.int16, device=dev)
+    vc = torch.randint(-30000, 30000, (nd, hkv, bs // 4, d, 4), dtype=torch.int16, device=dev)
     hk = torch.empty((n, hkv, bs, d), dtype=torch.int16).pin_memory()
-    hv = torch.empty((n, hkv, d, bs), dtype=torch.int16).pin_memory()
+    hv = torch.empty((n, hkv, bs // 4, d, 4), dtype=torch.int16).pin_memory()
     sp = torch.cuda.current_stream().cuda_stream
     stream = torch.cuda.current_stream()
 

@@ -29,7 +29,11 @@
  *   q, out          [num_seqs][num_heads][head_dim]
  *   k, v (new)      [num_tokens][num_kv_heads][head_dim]
  *   k_cache         [num_blocks][num_kv_heads][block_size][head_dim]  token-major
- *   v_cache         [num_blocks][num_kv_heads][head_dim][block_size]  dim-major
+ *   v_cache         [num_blocks][num_kv_heads][block_size/4][head_dim][4]
+ *                   positions in groups of four; within a group the four
+ *                   positions of one dimension are adjacent (8 bytes, the
+ *                   P.V matrix-core operand of one lane), and one position's
+ *                   head_dim values lie in one run of 4 * head_dim elements
  *   block_tables    int32 [num_seqs][max_blocks_per_seq]
  *   context_lens    int32 [num_seqs]   (tokens to attend over, the new one included)
  *   slot_mapping    int64 [num_tokens] slot = block * block_size + offset; < 0 = skip

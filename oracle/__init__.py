@@ -14,7 +14,8 @@ Storage convention (identical to the library's documented one, implemented
 independently in ``oracle.c``):
 
 * K cache ``uint16 [num_blocks, num_kv_heads, block_size, head_dim]``
-* V cache ``uint16 [num_blocks, num_kv_heads, head_dim, block_size]``
+* V cache ``uint16 [num_blocks, num_kv_heads, block_size // 4, head_dim, 4]``: positions in
+  groups of four, the four positions of one dimension adjacent.
 * q ``uint16 [num_seqs, num_heads, head_dim]``; k, v ``uint16 [T, num_kv_heads, head_dim]``
 * ``dtype`` 0 = IEEE binary16, 1 = bfloat16 (raw bit patterns).
 * FP8 caches: uint8 OCP E4M3 codes in the same layouts, standing for
@@ -160,7 +161,7 @@ def kv_write(k, v, slot_mapping, k_cache, v_cache, block_size: int) -> None:
     T, hkv, d = k.shape
     nb = k_cache.shape[0]
     assert k_cache.shape == (nb, hkv, block_size, d)
-    assert v_cache.shape == (nb, hkv, d, block_size)
+    assert v_cache.shape == (nb, hkv, block_size // 4, d, 4)
     rc = _load().oracle_kv_write(_ptr(k), _ptr(v), _ptr(slot), _ptr(k_cache),
                                  _ptr(v_cache), T, hkv, d, block_size, nb)
     _check(rc, "oracle_kv_write")
@@ -174,7 +175,8 @@ def _decode_args(q, k_cache, v_cache, block_tables, context_lens, scale,
     kc, vc = _u16(k_cache), _u16(v_cache)
     B, hq, d = q.shape
     nb, hkv = kc.shape[0], kc.shape[1]
-    assert kc.shape == (nb, hkv, block_size, d) and vc.shape == (nb, hkv, d, block_size)
+    assert kc.shape == (nb, hkv, block_size, d)
+    assert vc.shape == (nb, hkv, block_size // 4, d, 4)
     assert bt.shape[0] == B and cl.shape == (B,)
     keep = (q, bt, cl, kc, vc)
     args = [_ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(cl), float(scale),
@@ -243,7 +245,7 @@ def kv_write_fp8(k, v, slot_mapping, k_cache, v_cache, block_size: int, dtype,
     T, hkv, d = k.shape
     nb = k_cache.shape[0]
     assert k_cache.shape == (nb, hkv, block_size, d)
-    assert v_cache.shape == (nb, hkv, d, block_size)
+    assert v_cache.shape == (nb, hkv, block_size // 4, d, 4)
     rc = _load().oracle_kv_write_fp8(_ptr(k), _ptr(v), _ptr(slot), _ptr(k_cache),
                                      _ptr(v_cache), T, hkv, d, block_size, nb,
                                      dtype_code(dtype), float(k_scale), float(v_scale))
@@ -260,7 +262,8 @@ def _decode_fp8_args(q, k_cache, v_cache, block_tables, context_lens, scale, blo
     assert kc.dtype == np.uint8 and vc.dtype == np.uint8
     B, hq, d = q.shape
     nb, hkv = kc.shape[0], kc.shape[1]
-    assert kc.shape == (nb, hkv, block_size, d) and vc.shape == (nb, hkv, d, block_size)
+    assert kc.shape == (nb, hkv, block_size, d)
+    assert vc.shape == (nb, hkv, block_size // 4, d, 4)
     keep = (q, bt, cl, kc, vc)
     args = [_ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(cl), float(scale), block_size, hkv,
             B, hq, d, bt.shape[1], nb, dtype_code(q_dtype), float(k_scale), float(v_scale)]
@@ -301,7 +304,7 @@ def copy_blocks(pairs, k_cache, v_cache, block_size: int) -> None:
     assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
     assert k_cache.dtype == v_cache.dtype and k_cache.dtype.itemsize in (1, 2)
     nb, hkv, bs, d = k_cache.shape
-    assert bs == block_size and v_cache.shape == (nb, hkv, d, bs)
+    assert bs == block_size and v_cache.shape == (nb, hkv, bs // 4, d, 4)
     rc = _load().oracle_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0],
                                     hkv, d, bs, nb, k_cache.dtype.itemsize)
     _check(rc, "oracle_copy_blocks")
@@ -317,7 +320,7 @@ def swap_blocks(pairs, dst_k, dst_v, src_k, src_v, block_size: int) -> None:
     nd, hkv, bs, d = dst_k.shape
     ns = src_k.shape[0]
     assert bs == block_size and src_k.shape[1:] == dst_k.shape[1:]
-    assert dst_v.shape == (nd, hkv, d, bs) and src_v.shape == (ns, hkv, d, bs)
+    assert dst_v.shape == (nd, hkv, bs // 4, d, 4) and src_v.shape == (ns, hkv, bs // 4, d, 4)
     rc = _load().oracle_swap_blocks(_ptr(dst_k), _ptr(dst_v), nd, _ptr(src_k), _ptr(src_v), ns,
                                     _ptr(pairs), pairs.shape[0], hkv, d, bs,
                                     dst_k.dtype.itemsize)

@@ -28,7 +28,9 @@
  * Storage (shared by the oracle and the library only as a documented
  * convention; each side has its own code for it):
  *   K cache  [num_blocks][num_kv_heads][block_size][head_dim]   token-major
- *   V cache  [num_blocks][num_kv_heads][head_dim][block_size]   dim-major
+ *   V cache  [num_blocks][num_kv_heads][block_size/4][head_dim][4]
+ *            positions in groups of four; inside a group the four positions
+ *            of one dimension are adjacent (block_size a multiple of 4)
  *   q        [num_seqs][num_heads][head_dim]
  *   k, v     [num_tokens][num_kv_heads][head_dim]   (new tokens to append)
  *   slot     int64 [num_tokens]; slot = physical_block * block_size + offset,
@@ -166,11 +168,19 @@ static const uint16_t *k_row(const uint16_t *k_cache, int64_t block, int kv_head
   return k_cache + row * head_dim;
 }
 
+/* Index of V element (block, kv_head, position offset, dimension dim): the
+ * (block, head) slice holds block_size * head_dim elements, as block_size/4
+ * groups of [head_dim][4]. */
+static int64_t v_index(int64_t block, int kv_head, int offset, int dim, int num_kv_heads,
+                       int block_size, int head_dim) {
+  int64_t slice = (block * num_kv_heads + kv_head) * (int64_t)block_size * head_dim;
+  return slice + ((int64_t)(offset / 4) * head_dim + dim) * 4 + offset % 4;
+}
+
 static uint16_t v_elem(const uint16_t *v_cache, int64_t block, int kv_head,
                        int offset, int dim, int num_kv_heads, int block_size,
                        int head_dim) {
-  int64_t base = (block * num_kv_heads + kv_head) * (int64_t)head_dim + dim;
-  return v_cache[base * block_size + offset];
+  return v_cache[v_index(block, kv_head, offset, dim, num_kv_heads, block_size, head_dim)];
 }
 
 /* ---- KV append ---------------------------------------------------------- */
@@ -187,6 +197,7 @@ int oracle_kv_write(const uint16_t *k, const uint16_t *v,
                     uint16_t *v_cache, int64_t num_tokens, int num_kv_heads,
                     int head_dim, int block_size, int64_t num_blocks) {
   if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      block_size % 4 != 0 ||
       num_blocks <= 0)
     return ORACLE_EARG;
   int64_t num_slots = num_blocks * block_size;
@@ -215,8 +226,7 @@ int oracle_kv_write(const uint16_t *k, const uint16_t *v,
           (uint16_t *)k_row(k_cache, block, j, offset, num_kv_heads, block_size, head_dim);
       for (int d = 0; d < head_dim; ++d) {
         dst_k[d] = src_k[d];
-        int64_t vbase = (block * num_kv_heads + j) * (int64_t)head_dim + d;
-        v_cache[vbase * block_size + offset] = src_v[d];
+        v_cache[v_index(block, j, offset, d, num_kv_heads, block_size, head_dim)] = src_v[d];
       }
     }
   }
@@ -245,7 +255,7 @@ static int decode_row_any(double *out_row, const uint16_t *q, const void *k_cach
                           int cache_dtype, double k_scale, double v_scale, int s, int h) {
   if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || s < 0 ||
       s >= num_seqs || h < 0 || h >= num_heads || block_size <= 0 ||
-      head_dim <= 0 || (q_dtype != ORACLE_F16 && q_dtype != ORACLE_BF16) ||
+      block_size % 4 != 0 || head_dim <= 0 || (q_dtype != ORACLE_F16 && q_dtype != ORACLE_BF16) ||
       (cache_dtype != ORACLE_F16 && cache_dtype != ORACLE_BF16 &&
        cache_dtype != ORACLE_FP8))
     return ORACLE_EARG;
@@ -294,9 +304,7 @@ static int decode_row_any(double *out_row, const uint16_t *q, const void *k_cach
     int64_t block = table[t / block_size];
     int offset = (int)(t % block_size);
     for (int d = 0; d < head_dim; ++d) {
-      /* V element (token t, dim d): [block][kv_head][d][offset] */
-      int64_t vi = ((block * num_kv_heads + kv_head) * (int64_t)head_dim + d) *
-                       block_size + offset;
+      int64_t vi = v_index(block, kv_head, offset, d, num_kv_heads, block_size, head_dim);
       out_row[d] += x[t] * cache_value(v_cache, vi, cache_dtype, v_scale);
     }
   }
@@ -371,6 +379,7 @@ int oracle_decode_row_partitioned(double *out_row, const uint16_t *q,
                                   int dtype, int s, int h, int part_tokens) {
   if (part_tokens <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
       s < 0 || s >= num_seqs || h < 0 || h >= num_heads || block_size <= 0 ||
+      block_size % 4 != 0 ||
       head_dim <= 0 || (dtype != ORACLE_F16 && dtype != ORACLE_BF16))
     return ORACLE_EARG;
   int group = num_heads / num_kv_heads;
@@ -460,6 +469,7 @@ int oracle_kv_write_fp8(const uint16_t *k, const uint16_t *v,
                         int block_size, int64_t num_blocks, int dtype, float k_scale,
                         float v_scale) {
   if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      block_size % 4 != 0 ||
       num_blocks <= 0 || (dtype != ORACLE_F16 && dtype != ORACLE_BF16) ||
       !(k_scale > 0.0f) || !(v_scale > 0.0f) || isinf(k_scale) || isinf(v_scale))
     return ORACLE_EARG;
@@ -490,7 +500,7 @@ int oracle_kv_write_fp8(const uint16_t *k, const uint16_t *v,
         float vx = (float)decode(v[src], dtype) * v_inv;
         k_cache[((block * num_kv_heads + j) * (int64_t)block_size + offset) * head_dim + d] =
             oracle_f64_to_e4m3((double)kx);
-        v_cache[((block * num_kv_heads + j) * (int64_t)head_dim + d) * block_size + offset] =
+        v_cache[v_index(block, j, offset, d, num_kv_heads, block_size, head_dim)] =
             oracle_f64_to_e4m3((double)vx);
       }
     }
@@ -553,6 +563,7 @@ int oracle_copy_blocks(void *k_cache, void *v_cache, const int64_t *pairs, int64
                        int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
                        int elem_bytes) {
   if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      block_size % 4 != 0 ||
       num_blocks <= 0 || (elem_bytes != 1 && elem_bytes != 2))
     return ORACLE_EARG;
   unsigned char *role = calloc((size_t)num_blocks, 1); /* bit 0: source, bit 1: destination */
@@ -587,8 +598,8 @@ int oracle_copy_blocks(void *k_cache, void *v_cache, const int64_t *pairs, int64
         for (int d = 0; d < head_dim; ++d) {
           int64_t ks = (((src * num_kv_heads + j) * (int64_t)block_size + o) * head_dim + d);
           int64_t kd = (((dst * num_kv_heads + j) * (int64_t)block_size + o) * head_dim + d);
-          int64_t vs = (((src * num_kv_heads + j) * (int64_t)head_dim + d) * block_size + o);
-          int64_t vd = (((dst * num_kv_heads + j) * (int64_t)head_dim + d) * block_size + o);
+          int64_t vs = v_index(src, j, o, d, num_kv_heads, block_size, head_dim);
+          int64_t vd = v_index(dst, j, o, d, num_kv_heads, block_size, head_dim);
           memcpy(kc + kd * elem_bytes, kc + ks * elem_bytes, (size_t)elem_bytes);
           memcpy(vc + vd * elem_bytes, vc + vs * elem_bytes, (size_t)elem_bytes);
         }
@@ -612,6 +623,7 @@ int oracle_swap_blocks(void *dst_k, void *dst_v, int64_t dst_num_blocks, const v
                        int64_t num_pairs, int num_kv_heads, int head_dim, int block_size,
                        int elem_bytes) {
   if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      block_size % 4 != 0 ||
       dst_num_blocks <= 0 || src_num_blocks <= 0 || (elem_bytes != 1 && elem_bytes != 2))
     return ORACLE_EARG;
   unsigned char *taken = calloc((size_t)dst_num_blocks, 1);
@@ -640,8 +652,8 @@ int oracle_swap_blocks(void *dst_k, void *dst_v, int64_t dst_num_blocks, const v
         for (int d = 0; d < head_dim; ++d) {
           int64_t ks = (((src * num_kv_heads + j) * (int64_t)block_size + o) * head_dim + d);
           int64_t kd = (((dst * num_kv_heads + j) * (int64_t)block_size + o) * head_dim + d);
-          int64_t vs = (((src * num_kv_heads + j) * (int64_t)head_dim + d) * block_size + o);
-          int64_t vd = (((dst * num_kv_heads + j) * (int64_t)head_dim + d) * block_size + o);
+          int64_t vs = v_index(src, j, o, d, num_kv_heads, block_size, head_dim);
+          int64_t vd = v_index(dst, j, o, d, num_kv_heads, block_size, head_dim);
           memcpy(dk + kd * elem_bytes, sk + ks * elem_bytes, (size_t)elem_bytes);
           memcpy(dv + vd * elem_bytes, sv + vs * elem_bytes, (size_t)elem_bytes);
         }
@@ -674,7 +686,8 @@ static int prefill_any(double *out, const uint16_t *q, const void *k_cache,
                        int head_dim, int max_blocks_per_seq, int64_t num_blocks, int dtype,
                        int cache_dtype, double k_scale, double v_scale) {
   if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || num_seqs < 0 ||
-      block_size <= 0 || head_dim <= 0 || (dtype != ORACLE_F16 && dtype != ORACLE_BF16) ||
+      block_size <= 0 || block_size % 4 != 0 || head_dim <= 0 ||
+      (dtype != ORACLE_F16 && dtype != ORACLE_BF16) ||
       (cache_dtype != dtype && cache_dtype != ORACLE_FP8))
     return ORACLE_EARG;
   int group = num_heads / num_kv_heads;
@@ -717,8 +730,7 @@ static int prefill_any(double *out, const uint16_t *q, const void *k_cache,
           int64_t block = table[t / block_size];
           int offset = (int)(t % block_size);
           for (int d = 0; d < head_dim; ++d) {
-            int64_t vi = ((block * num_kv_heads + kv_head) * (int64_t)head_dim + d) *
-                             block_size + offset;
+            int64_t vi = v_index(block, kv_head, offset, d, num_kv_heads, block_size, head_dim);
             orow[d] += x[t] * cache_value(v_cache, vi, cache_dtype, v_scale);
           }
         }

@@ -118,6 +118,13 @@ def load() -> ctypes.CDLL:
     return lib
 
 
+def v_shape(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int) -> tuple:
+    """Shape of a V cache: each (block, KV head) slice holds block_size / 4
+    groups of [head_dim][4] (the four positions of a group adjacent per
+    dimension)."""
+    return (num_blocks, num_kv_heads, block_size // 4, head_dim, 4)
+
+
 def _check(fn: str, code: int):
     if code != PA_OK:
         text = load().pa_strerror(code).decode()
@@ -178,7 +185,7 @@ def workspace(dev, nbytes: int) -> Optional[torch.Tensor]:
 def paged_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                    k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
     """Scatter k, v [T, Hkv, D] into k_cache [N, Hkv, bs, D] and
-    v_cache [N, Hkv, D, bs] at slot_mapping (int64 [T])."""
+    v_cache [N, Hkv, bs/4, D, 4] at slot_mapping (int64 [T])."""
     dev = _dev(k, v, slot_mapping, k_cache, v_cache)
     if k.dim() != 3 or v.shape != k.shape:
         raise ValueError("k and v must be [num_tokens, num_kv_heads, head_dim]")
@@ -186,8 +193,8 @@ def paged_kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
     if k_cache.dim() != 4 or k_cache.shape[1] != hkv or k_cache.shape[3] != d:
         raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
     nb, _, bs, _ = k_cache.shape
-    if tuple(v_cache.shape) != (nb, hkv, d, bs):
-        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size]")
+    if tuple(v_cache.shape) != v_shape(nb, hkv, bs, d):
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, block_size / 4, head_dim, 4]")
     if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (T,):
         raise ValueError("slot_mapping must be int64 [num_tokens]")
     dt = _dtype(k)
@@ -215,8 +222,8 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
     if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (num_kv_heads, block_size, d):
         raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
     nb = k_cache.shape[0]
-    if tuple(v_cache.shape) != (nb, num_kv_heads, d, block_size):
-        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size]")
+    if tuple(v_cache.shape) != v_shape(nb, num_kv_heads, block_size, d):
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, block_size / 4, head_dim, 4]")
     if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be int32 [num_seqs, max_blocks_per_seq]")
     if context_lens.dtype != torch.int32 or tuple(context_lens.shape) != (B,):
@@ -270,7 +277,7 @@ def paged_kv_write_fp8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Ten
                        k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float,
                        v_scale: float) -> None:
     """Quantise k, v [T, Hkv, D] (fp16 / bf16) into E4M3 caches: uint8
-    k_cache [N, Hkv, bs, D] and v_cache [N, Hkv, D, bs], at slot_mapping."""
+    k_cache [N, Hkv, bs, D] and v_cache [N, Hkv, bs/4, D, 4], at slot_mapping."""
     dev = _dev(k, v, slot_mapping, k_cache, v_cache)
     if k.dim() != 3 or v.shape != k.shape:
         raise ValueError("k and v must be [num_tokens, num_kv_heads, head_dim]")
@@ -280,8 +287,8 @@ def paged_kv_write_fp8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Ten
     if k_cache.dim() != 4 or k_cache.shape[1] != hkv or k_cache.shape[3] != d:
         raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
     nb, _, bs, _ = k_cache.shape
-    if tuple(v_cache.shape) != (nb, hkv, d, bs):
-        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size]")
+    if tuple(v_cache.shape) != v_shape(nb, hkv, bs, d):
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, block_size / 4, head_dim, 4]")
     if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (T,):
         raise ValueError("slot_mapping must be int64 [num_tokens]")
     dt = _dtype(k)
@@ -310,8 +317,8 @@ def paged_attention_decode_fp8(out: torch.Tensor, q: torch.Tensor, k_cache: torc
     if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (num_kv_heads, block_size, d):
         raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
     nb = k_cache.shape[0]
-    if tuple(v_cache.shape) != (nb, num_kv_heads, d, block_size):
-        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size]")
+    if tuple(v_cache.shape) != v_shape(nb, num_kv_heads, block_size, d):
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, block_size / 4, head_dim, 4]")
     if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be int32 [num_seqs, max_blocks_per_seq]")
     if context_lens.dtype != torch.int32 or tuple(context_lens.shape) != (B,):
@@ -357,8 +364,8 @@ def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: tor
     if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (num_kv_heads, block_size, d):
         raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
     nb = k_cache.shape[0]
-    if tuple(v_cache.shape) != (nb, num_kv_heads, d, block_size):
-        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size]")
+    if tuple(v_cache.shape) != v_shape(nb, num_kv_heads, block_size, d):
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, block_size / 4, head_dim, 4]")
     if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be int32 [num_seqs, max_blocks_per_seq]")
     if context_lens.dtype != torch.int32 or tuple(context_lens.shape) != (B,):
@@ -453,8 +460,8 @@ def paged_copy_blocks(pairs: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     if k_cache.dim() != 4:
         raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
     nb, hkv, bs, d = k_cache.shape
-    if tuple(v_cache.shape) != (nb, hkv, d, bs) or v_cache.dtype != k_cache.dtype:
-        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size], "
+    if tuple(v_cache.shape) != v_shape(nb, hkv, bs, d) or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, block_size / 4, head_dim, 4], "
                          "k_cache's dtype")
     rc = load().paged_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), pairs.data_ptr(),
                                   pairs.shape[0], hkv, d, bs, nb, k_cache.element_size(),
@@ -488,8 +495,9 @@ def paged_swap_blocks(pairs: torch.Tensor, dst_k: torch.Tensor, dst_v: torch.Ten
         raise ValueError("pairs must be int64 [num_pairs, 2]")
     nd, hkv, bs, d = dst_k.shape
     ns = src_k.shape[0]
-    if (tuple(src_k.shape[1:]) != (hkv, bs, d) or tuple(dst_v.shape) != (nd, hkv, d, bs) or
-            tuple(src_v.shape) != (ns, hkv, d, bs)):
+    if (tuple(src_k.shape[1:]) != (hkv, bs, d) or
+            tuple(dst_v.shape) != v_shape(nd, hkv, bs, d) or
+            tuple(src_v.shape) != v_shape(ns, hkv, bs, d)):
         raise ValueError("pools must share the cache layouts and sizes per block")
     if len({t.dtype for t in (dst_k, dst_v, src_k, src_v)}) != 1:
         raise ValueError("pools must share one element type")
@@ -518,8 +526,8 @@ def _prefill_shapes(out, q, k_cache, v_cache, block_tables, context_lens, query_
     if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (num_kv_heads, block_size, d):
         raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
     nb = k_cache.shape[0]
-    if tuple(v_cache.shape) != (nb, num_kv_heads, d, block_size):
-        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size]")
+    if tuple(v_cache.shape) != v_shape(nb, num_kv_heads, block_size, d):
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, block_size / 4, head_dim, 4]")
     if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be int32 [num_seqs, max_blocks_per_seq]")
     if context_lens.dtype != torch.int32 or context_lens.dim() != 1:

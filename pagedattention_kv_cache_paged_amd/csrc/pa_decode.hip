@@ -25,8 +25,9 @@
 //        -> D/32 MFMA 16x16x32; A = K rows as stored (token-major cache),
 //           each lane loading 16 contiguous bytes of one token's row.
 //   O^T[D x 16 head]     += V^T[D x 16 tok] * P^T[16 tok x 16 head]
-//        -> D/16 MFMA 16x16x16; A = V^T read straight from the dim-major
-//           V cache (8 contiguous bytes = 4 tokens of one dim per lane),
+//        -> D/16 MFMA 16x16x16; A = V^T read straight from the V cache,
+//           whose (block, head) slice is block_size/4 groups of [D][4]
+//           (8 contiguous bytes = 4 tokens of one dim per lane),
 //           B = P exactly as the QK MFMA left it in registers (lane l holds
 //           head l%16, tokens 4*(l/16)+0..3), so no shuffle is needed.
 //           For bfloat16, P goes in as a hi and a lo bfloat16 part (two
@@ -364,22 +365,19 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
     const int n = mt & 31;
     const int ka = __builtin_amdgcn_readlane(b0, idx);
     const int ktok = min(row, n - 1);
-    // V of the new token's tile is read at every position (the step writes
-    // that tile's V back whole); elsewhere lanes past the valid tokens
-    // repeat the last valid group.
-    const int vtok = (APPEND && (mt & kNew)) ? grp * 4 : min(grp * 4, (n - 1) & ~3);
+    const int vtok = min(grp * 4, (n - 1) & ~3);  // this lane's 4-token group
     const CT *kp, *vp;
     if constexpr (BS == 8) {  // the tile's two blocks: per-lane choice
       const int kz = __builtin_amdgcn_readlane(b1, idx);
       kp = kbase + (int64_t)(ktok < 8 ? ka : kz) * blk_stride + (ktok & 7) * D + grp * (KV8 ? 16 : 8);
-      vp = vbase + (int64_t)(vtok < 8 ? ka : kz) * blk_stride + row * BS + (vtok & 7);
+      vp = vbase + (int64_t)(vtok < 8 ? ka : kz) * blk_stride + (((vtok & 7) >> 2) * D + row) * 4;
     } else {
       // block base in scalar registers, 32-bit lane offsets
       const int o = BS == 16 ? 0 : __builtin_amdgcn_readlane(boff, idx);
       const CT *kblk = kbase + (int64_t)ka * blk_stride + o * D;
-      const CT *vblk = vbase + (int64_t)ka * blk_stride + o;
+      const CT *vblk = vbase + (int64_t)ka * blk_stride;
       kp = kblk + (uint32_t)(ktok * D + grp * (KV8 ? 16 : 8));
-      vp = vblk + (uint32_t)(row * BS + vtok);
+      vp = vblk + (uint32_t)((((o + vtok) >> 2) * D + row) * 4);
     }
     if constexpr (KV8) {
 #pragma unroll
@@ -387,14 +385,14 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
         f.k[h] = __builtin_nontemporal_load((const u32x4 *)(kp + h * 64));
 #pragma unroll
       for (int dt = 0; dt < DTILES; ++dt)
-        f.v[dt] = __builtin_nontemporal_load((const uint32_t *)(vp + dt * 16 * BS));
+        f.v[dt] = __builtin_nontemporal_load((const uint32_t *)(vp + dt * 64));
     } else {
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks)
         f.k[ks] = __builtin_nontemporal_load((const u32x4 *)(kp + ks * 32));
 #pragma unroll
       for (int dt = 0; dt < DTILES; ++dt)
-        f.v[dt] = __builtin_nontemporal_load((const u32x2 *)(vp + dt * 16 * BS));
+        f.v[dt] = __builtin_nontemporal_load((const u32x2 *)(vp + dt * 64));
     }
   };
 
@@ -453,12 +451,10 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
           }
         }
       }
-      // Store the token: its K row, and the tile's whole V^T as loaded with
-      // the token in place.  In the dim-major V cache one token touches a
-      // few bytes of every line of the (block, head) region; writing the
-      // tile's lines whole (the other positions with the bytes they hold)
-      // avoids a partial-line write per dimension.  At block size 8 only
-      // the new token's block is written.
+      // Store the token: its K row, and its V as part of its whole 4-token
+      // group (the lanes of quarter r / 4 hold that group's [D][4] run, the
+      // other three positions with the bytes they held), so the V store
+      // writes whole cache lines rather than a few bytes of each.
       const int nb = __builtin_amdgcn_readlane(nblk, idx);
       if (nb >= 0) {
         const int bo = BS == 32 ? __builtin_amdgcn_readlane(boff, idx) : 0;
@@ -471,11 +467,11 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
           for (int h = 0; h < (KV8 ? D / 64 : KSTEPS); ++h)
             *(u32x4 *)(kd + (KV8 ? 64 * h + 16 * grp : 32 * h + 8 * grp)) = f.k[h];
         }
-        if (BS != 8 || (grp >> 1) == (r >> 3)) {
-          const int t = BS == 8 ? (grp * 4) & 7 : bo + grp * 4;
+        if (grp == (r >> 2)) {
+          const int g4 = ((BS == 8 ? (grp * 4) & 7 : bo + grp * 4) >> 2);  // group in the block
 #pragma unroll
           for (int dt = 0; dt < DTILES; ++dt) {
-            CT *vp = vd + (dt * 16 + row) * BS + t;
+            CT *vp = vd + (g4 * D + dt * 16 + row) * 4;
             if constexpr (KV8) *(uint32_t *)vp = f.v[dt];
             else *(u32x2 *)vp = f.v[dt];
           }

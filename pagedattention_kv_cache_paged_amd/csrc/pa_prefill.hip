@@ -141,8 +141,9 @@ __device__ __forceinline__ float rows_sum(float x) {
 // LDS tile layouts (16-bit elements), rows padded so that the 16 rows one
 // MFMA operand reads spread over the banks:
 //   K tile [64 keys][D + 8]  (token-major, as in the cache)
-//   V tile [D][64 + 4]       (dim-major, as in the cache; a 34-dword row, the
-//                             fastest measured of a few 8-byte-aligned ones)
+//   V tile [D][64 + 4]       (dim-major: the cache's groups of four keys
+//                             laid end to end per dimension; a 34-dword row,
+//                             the fastest measured of a few 8-byte-aligned ones)
 template <int D>
 struct Tile {
   static constexpr int kRow = D + 8;        // K row, in elements
@@ -230,7 +231,8 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
 
   // Tile loads: a tile is 8*D pieces of 8 elements (16 bytes, or 8 with E4M3
   // codes) of K (piece p: key p / (D/8), dims 8*(p % (D/8)) ..) and 8*D of V
-  // (piece p: keys 8*(p / D) .. +7 of dim p % D).  Wave w's load j moves pieces w*64 + j*threads .. +63 of each:
+  // (piece p: keys 8*(p / D) .. +7 of dim p % D, two runs of 4 adjacent
+  // elements, since the V cache keeps positions in groups of [D][4]).  Wave w's load j moves pieces w*64 + j*threads .. +63 of each:
   // 64 / (D/8) whole K rows, or 64 dims of one key octet, so every piece of
   // one load lies in one cache block (blocks hold at least 8 tokens).  The
   // block base is then a scalar and each lane adds a fixed offset.
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
   constexpr int KPL = kWave / KPR;  // keys per K load (4 at D = 128, 8 at D = 64)
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const uint32_t koff = (uint32_t)((lane / KPR) * D + (lane % KPR) * 8) * EB;  // bytes
-  const uint32_t voff = (uint32_t)(lane * bs) * EB;
+  const uint32_t voff = (uint32_t)(lane * 4) * EB;
   using Piece = std::conditional_t<KV8, u32x2, u32x4>;
   // A ring of kStages register stages: a tile's loads are issued
   // kStages - 1 tiles before they go into LDS, so the wait for them is
@@ -264,9 +266,13 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
       const int pw = min(wv * kWave + j * kThreads, PIECES - kWave);
       const int key0 = min(tile * kKT + (pw / D) * 8, wg_hi & ~7);  // the load's key octet
       const int blk = __builtin_amdgcn_readfirstlane(tbl_lds[key0 >> log2_bs]);
-      const char *src =
-          vbase + blk * blk_bytes + (int64_t)(((pw % D) * bs + (key0 & (bs - 1))) * EB);
-      st_v[stage][j] = __builtin_nontemporal_load((const Piece *)(src + voff));
+      const char *src = vbase + blk * blk_bytes +
+                        (int64_t)((((key0 & (bs - 1)) >> 2) * D + pw % D) * 4 * EB) + voff;
+      using Half = std::conditional_t<KV8, uint32_t, u32x2>;  // 4 keys of one dim
+      const Half lo = __builtin_nontemporal_load((const Half *)src);
+      const Half hi = __builtin_nontemporal_load((const Half *)(src + D * 4 * EB));
+      if constexpr (KV8) st_v[stage][j] = Piece{lo, hi};
+      else st_v[stage][j] = Piece{lo.x, lo.y, hi.x, hi.y};
     }
   };
   // Into LDS; V of keys past the workgroup's last position is zeroed there

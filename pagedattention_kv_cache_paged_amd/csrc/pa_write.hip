@@ -7,9 +7,11 @@
 // The FP8 variant quantises while it scatters (see kv_write_fp8_kernel).
 //
 // One workgroup per token.  A K row (head_dim contiguous elements) lands
-// contiguously in the token-major K cache, moved as 16-byte vectors; a V
-// row is spread across the dim-major V cache with a stride of block_size
-// elements, so it is read as 16-byte vectors and stored as 16-bit elements.
+// contiguously in the token-major K cache, moved as 16-byte vectors.  The V
+// cache holds each (block, head) slice as block_size/4 groups of [head_dim][4]
+// (four positions of one dimension adjacent), so a V row lands with a stride
+// of 4 elements inside its position group: read as 16-byte vectors, stored
+// as single elements.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -51,15 +53,15 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
     const u32x4 vx = c == c0 ? vx0 : *(const u32x4 *)(v + src);
     const int64_t bh = blk * num_kv_heads + h;
     *(u32x4 *)(k_cache + (bh * BS + off) * D + d0) = kx;
-    uint16_t *vd = v_cache + (bh * D + d0) * BS + off;
-    vd[0 * BS] = (uint16_t)(vx.x & 0xffffu);
-    vd[1 * BS] = (uint16_t)(vx.x >> 16);
-    vd[2 * BS] = (uint16_t)(vx.y & 0xffffu);
-    vd[3 * BS] = (uint16_t)(vx.y >> 16);
-    vd[4 * BS] = (uint16_t)(vx.z & 0xffffu);
-    vd[5 * BS] = (uint16_t)(vx.z >> 16);
-    vd[6 * BS] = (uint16_t)(vx.w & 0xffffu);
-    vd[7 * BS] = (uint16_t)(vx.w >> 16);
+    uint16_t *vd = v_cache + bh * BS * D + ((off >> 2) * D + d0) * 4 + (off & 3);
+    vd[0 * 4] = (uint16_t)(vx.x & 0xffffu);
+    vd[1 * 4] = (uint16_t)(vx.x >> 16);
+    vd[2 * 4] = (uint16_t)(vx.y & 0xffffu);
+    vd[3 * 4] = (uint16_t)(vx.y >> 16);
+    vd[4 * 4] = (uint16_t)(vx.z & 0xffffu);
+    vd[5 * 4] = (uint16_t)(vx.z >> 16);
+    vd[6 * 4] = (uint16_t)(vx.w & 0xffffu);
+    vd[7 * 4] = (uint16_t)(vx.w >> 16);
   }
 }
 
@@ -105,9 +107,9 @@ __global__ __launch_bounds__(256) void kv_write_fp8_kernel(
     kw.x = kc[0] | (kc[1] << 8) | (kc[2] << 16) | (kc[3] << 24);
     kw.y = kc[4] | (kc[5] << 8) | (kc[6] << 16) | (kc[7] << 24);
     *(u32x2 *)(k_cache + (bh * BS + off) * D + d0) = kw;  // 8-byte aligned: d0 % 8 == 0
-    uint8_t *vd = v_cache + (bh * D + d0) * BS + off;
+    uint8_t *vd = v_cache + bh * BS * D + ((off >> 2) * D + d0) * 4 + (off & 3);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) vd[i * BS] = (uint8_t)vc[i];
+    for (int i = 0; i < 8; ++i) vd[i * 4] = (uint8_t)vc[i];
   }
 }
 

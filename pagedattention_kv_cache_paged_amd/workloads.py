@@ -209,7 +209,7 @@ class Workload:
 
     def cache_shapes(self):
         nb, h, bs, d = self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim
-        return (nb, h, bs, d), (nb, h, d, bs)
+        return (nb, h, bs, d), (nb, h, bs // 4, d, 4)
 
     def nan_caches(self):
         """Host K and V caches filled with the dtype's NaN."""

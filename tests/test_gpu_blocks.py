@@ -90,7 +90,7 @@ def test_cow_flow_on_device(bs):
     pool = B.BlockPool(nb, order)
     nan = int(np.array([W.NAN_BITS[W.BF16]], np.uint16).view(np.int16)[0])
     kc = torch.full((nb, hkv, bs, d), nan, dtype=torch.int16, device=DEV).view(torch.bfloat16)
-    vc = torch.full((nb, hkv, d, bs), nan, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    vc = torch.full((nb, hkv, bs // 4, d, 4), nan, dtype=torch.int16, device=DEV).view(torch.bfloat16)
 
     def put(kk, vv, slot):
         B.paged_kv_write(torch.from_numpy(kk.view(np.int16)).to(DEV).view(torch.bfloat16),

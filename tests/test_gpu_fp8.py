@@ -126,12 +126,12 @@ def test_write_fp8_crafted_values(dtype, ks, vs):
     slots = np.random.default_rng(9).permutation(nb * bs)[:T].astype(np.int64)
     slots[3] = -1                          # padding
     kc = torch.full((nb, 2, bs, D), W.FP8_NAN, dtype=torch.uint8, device=DEV)
-    vc = torch.full((nb, 2, D, bs), W.FP8_NAN, dtype=torch.uint8, device=DEV)
+    vc = torch.full((nb, 2, bs // 4, D, 4), W.FP8_NAN, dtype=torch.uint8, device=DEV)
     B.paged_kv_write_fp8(dev_bits(bits, dtype), dev_bits(vbits, dtype),
                          torch.from_numpy(slots).to(DEV), kc, vc, ks, vs)
     torch.cuda.synchronize()
     okc = np.full((nb, 2, bs, D), W.FP8_NAN, np.uint8)
-    ovc = np.full((nb, 2, D, bs), W.FP8_NAN, np.uint8)
+    ovc = np.full((nb, 2, bs // 4, D, 4), W.FP8_NAN, np.uint8)
     oracle.kv_write_fp8(bits, vbits, slots, okc, ovc, bs, dtype, ks, vs)
     assert np.array_equal(kc.cpu().numpy(), okc)
     assert np.array_equal(vc.cpu().numpy(), ovc)

@@ -29,7 +29,7 @@ def rand_caches(g, nb, hkv, bs, d, itemsize):
     dt = np.uint16 if itemsize == 2 else np.uint8
     hi = 1 << (8 * itemsize)
     k = g.integers(0, hi, size=(nb, hkv, bs, d), dtype=np.int64).astype(dt)
-    v = g.integers(0, hi, size=(nb, hkv, d, bs), dtype=np.int64).astype(dt)
+    v = g.integers(0, hi, size=(nb, hkv, bs // 4, d, 4), dtype=np.int64).astype(dt)
     return k, v
 
 
@@ -86,7 +86,7 @@ def fork_with_cow(prompt_len, suffix_lens, bs, hkv, d, seed):
     order = g.permutation(nb)
     alloc = W.BlockAllocator(order)
     kc, vc = (np.full((nb, hkv, bs, d), W.NAN_BITS[W.BF16], np.uint16),
-              np.full((nb, hkv, d, bs), W.NAN_BITS[W.BF16], np.uint16))
+              np.full((nb, hkv, bs // 4, d, 4), W.NAN_BITS[W.BF16], np.uint16))
     pk = W.normal_bits(g, (prompt_len, hkv, d), W.BF16)
     pv = W.normal_bits(g, (prompt_len, hkv, d), W.BF16)
     root = []
@@ -132,7 +132,7 @@ def private_layout(logical, bs, hkv, d):
     per = [int(np.ceil(len(k) / bs)) for k, _ in logical]
     nb = sum(per)
     kc = np.full((nb, hkv, bs, d), W.NAN_BITS[W.BF16], np.uint16)
-    vc = np.full((nb, hkv, d, bs), W.NAN_BITS[W.BF16], np.uint16)
+    vc = np.full((nb, hkv, bs // 4, d, 4), W.NAN_BITS[W.BF16], np.uint16)
     bt = np.zeros((B, max(per)), np.int32)
     base = 0
     for s, (k, v) in enumerate(logical):
@@ -210,7 +210,7 @@ def test_preempt_and_resume_decodes_the_same():
     used = int(np.ceil(w.context_lens[seq] / 16))
     blocks = w.block_tables[seq, :used].copy()
     hk = np.zeros((used, 2, 16, 64), np.uint16)
-    hv = np.zeros((used, 2, 64, 16), np.uint16)
+    hv = np.zeros((used, 2, 4, 64, 4), np.uint16)
     oracle.swap_blocks(np.stack([blocks, np.arange(used)], 1), hk, hv, kc, vc, 16)
     kc[blocks] = 0x7FC0                      # the freed blocks now hold something else
     vc[blocks] = 0x7FC0

@@ -108,7 +108,7 @@ def test_append_codes_and_places(bs, dtype, ks, vs):
         b, o = divmod(int(slot), bs)
         written[slot] = True
         assert np.array_equal(kc[b, :, o, :], kq[i])
-        assert np.array_equal(vc[b, :, :, o], vq[i])
+        assert np.array_equal(vc[b, :, o // 4, :, o % 4], vq[i])
     # every other slot is untouched
     k_slots = kc.transpose(0, 2, 1, 3).reshape(-1, kc.shape[1] * kc.shape[3])
     assert np.all(k_slots[~written] == W.FP8_NAN)
@@ -142,7 +142,7 @@ def dense_fp8(w, kc, vc, ks, vs):
         for h in range(w.num_heads):
             j = h // G
             K = np.stack([kval[blocks[t], j, t % bs, :] for t in range(L)])
-            V = np.stack([vval[blocks[t], j, :, t % bs] for t in range(L)])
+            V = np.stack([vval[blocks[t], j, (t % bs) // 4, :, t % 4] for t in range(L)])
             x = K @ qf[s, h] * w.scale
             p = np.exp(x - x.max())
             out[s, h] = p @ V / p.sum()

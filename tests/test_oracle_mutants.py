@@ -36,15 +36,16 @@ MUTANTS = [
      "for (int64_t t = 0; t < len; ++t) {\n    int64_t block = table[t / block_size];\n    int offset",
      "for (int64_t t = 1; t < len; ++t) {\n    int64_t block = table[t / block_size];\n    int offset"),
     ("v_read_token_major",
-     "int64_t vi = ((block * num_kv_heads + kv_head) * (int64_t)head_dim + d) *\n"
-     "                       block_size + offset;",
+     "int64_t vi = v_index(block, kv_head, offset, d, num_kv_heads, block_size, head_dim);",
      "int64_t vi = ((block * num_kv_heads + kv_head) * (int64_t)block_size + offset) *\n"
      "                       head_dim + d;"),
+    # a consistent but different V layout (writes and reads move together)
     ("v_both_token_major",
-     "int64_t vi = ((block * num_kv_heads + kv_head) * (int64_t)head_dim + d) *\n"
-     "                       block_size + offset;",
-     "int64_t vi = ((block * num_kv_heads + kv_head) * (int64_t)block_size + offset) *\n"
-     "                       head_dim + d;"),
+     "return slice + ((int64_t)(offset / 4) * head_dim + dim) * 4 + offset % 4;",
+     "return slice + (int64_t)offset * head_dim + dim;"),
+    ("v_both_dim_major",
+     "return slice + ((int64_t)(offset / 4) * head_dim + dim) * 4 + offset % 4;",
+     "return slice + (int64_t)dim * block_size + offset;"),
     ("k_offset_shift", "(int)(t % block_size)) * head_dim;",
      "(int)((t + 1) % block_size)) * head_dim;"),
     # E4M3 coding and the FP8 append
@@ -69,7 +70,7 @@ MUTANTS = [
     ("copy_first_head_only", "for (int j = 0; j < num_kv_heads; ++j)\n      for (int o = 0; o < block_size; ++o)",
      "for (int j = 0; j < 1; ++j)\n      for (int o = 0; o < block_size; ++o)"),
     ("copy_v_token_major",
-     "int64_t vd = (((dst * num_kv_heads + j) * (int64_t)head_dim + d) * block_size + o);",
+     "int64_t vd = v_index(dst, j, o, d, num_kv_heads, block_size, head_dim);",
      "int64_t vd = (((dst * num_kv_heads + j) * (int64_t)block_size + o) * head_dim + d);"),
     ("copy_reversed", "memcpy(kc + kd * elem_bytes, kc + ks * elem_bytes, (size_t)elem_bytes);",
      "memcpy(kc + ks * elem_bytes, kc + kd * elem_bytes, (size_t)elem_bytes);"),
@@ -92,12 +93,8 @@ MUTANTS = [
      "dot += decode(qrow[d], dtype) * cache_value(k_cache, krow + d, cache_dtype, k_scale);",
      "dot += decode(qrow[d], dtype) * cache_value(k_cache, krow + d, cache_dtype, 1.0);"),
 ]
-# the consistent V-layout mutant also moves the write to token-major order
-EXTRA = {
-    "v_both_token_major": ("v_cache[vbase * block_size + offset] = src_v[d];",
-                           "v_cache[((block * num_kv_heads + j) * (int64_t)block_size + offset)"
-                           " * head_dim + d] = src_v[d];"),
-}
+# planted edits that need a second, matching one elsewhere
+EXTRA = {}
 
 
 def _build_variant(tmp, name, old, new):

@@ -129,9 +129,9 @@ def test_write_round_trip(bs):
         for t in range(int(w.context_lens[s])):
             b, o = w.block_tables[s, t // bs], t % bs
             np.testing.assert_array_equal(kc[b, :, o, :], K[t])
-            np.testing.assert_array_equal(vc[b, :, :, o], V[t])
+            np.testing.assert_array_equal(vc[b, :, o // 4, :, o % 4], V[t])
             touched_k[b, :, o, :] = True
-            touched_v[b, :, :, o] = True
+            touched_v[b, :, o // 4, :, o % 4] = True
     assert np.all(kc[~touched_k] == nan) and np.all(vc[~touched_v] == nan)
 
 
@@ -242,7 +242,7 @@ def test_shared_prefix_equals_private_copies():
     nb = need + 1
     alloc = W.BlockAllocator(np.random.default_rng(5).permutation(nb))
     kc, vc = (np.full(s, W.NAN_BITS[w.dtype], np.uint16) for s in
-              ((nb, 2, bs, 64), (nb, 2, 64, bs)))
+              ((nb, 2, bs, 64), (nb, 2, bs // 4, 64, 4)))
     tables = np.full((w.num_seqs, w.max_blocks_per_seq), alloc.free[0], np.int32)
     for s in range(w.num_seqs):
         t = W.BlockTable(alloc, bs)

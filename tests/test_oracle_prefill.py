@@ -143,7 +143,7 @@ def test_causality_ignores_later_positions():
         for t in range(p + 1, L):
             b, o = w.block_tables[0, t // 16], t % 16
             k2[b, :, o, :] = W.NAN_BITS[W.BF16]
-            v2[b, :, :, o] = W.NAN_BITS[W.BF16]
+            v2[b, :, o // 4, :, o % 4] = W.NAN_BITS[W.BF16]
         got = oracle.prefill(q[p:p + 1], k2, v2, w.block_tables, np.array([p + 1], np.int32),
                              np.array([0, 1], np.int32), w.scale, 16, w.dtype)
         assert np.array_equal(got[0], full[p])

@@ -58,7 +58,7 @@ def sdpa_fp8(w, kc, vc, q, qs, chunks, ks, vs):
         L = int(w.context_lens[s])
         blocks = [w.block_tables[s][t // bs] for t in range(L)]
         K = np.stack([kval[blocks[t], :, t % bs, :] for t in range(L)], 1)   # [Hkv, L, D]
-        V = np.stack([vval[blocks[t], :, :, t % bs] for t in range(L)], 1)
+        V = np.stack([vval[blocks[t], :, (t % bs) // 4, :, t % 4] for t in range(L)], 1)
         k = torch.from_numpy(K).repeat_interleave(G, 0)
         v = torch.from_numpy(V).repeat_interleave(G, 0)
         qq = torch.from_numpy(f64(q[qs[s]:qs[s] + n], w.dtype)).permute(1, 0, 2)
