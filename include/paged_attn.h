@@ -233,11 +233,10 @@ int paged_attention_decode_fp8(void *out, const void *q, const void *k_cache,
  * values.  k_new, v_new: 4-byte aligned.  The workspace is that of
  * paged_attention_decode for the same sizes.  The caller owns all buffers;
  * out, the new token's cache slots and the workspace are written.  In the V
- * cache the new token's 16-position tile of its block (the whole block at
- * block size 8 or 16, half of it at 32) is written back whole for each KV
- * head, its other positions with the bytes they held, so the caller must
- * not modify that block during the call (it owns it alone anyway: a shared
- * block is copied before a write into it).
+ * cache the new token's group of four positions is written whole for each KV
+ * head, its other three positions with the bytes they held, so the caller
+ * must not modify that block during the call (it owns it alone anyway: a
+ * shared block is copied before a write into it).
  */
 int paged_attention_decode_append(void *out, const void *q, const void *k_new,
                                   const void *v_new, void *k_cache, void *v_cache,
