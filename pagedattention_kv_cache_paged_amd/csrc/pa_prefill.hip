@@ -349,20 +349,24 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
           const uint16_t *vl = kl + T::kElems;
           // raw scores q.k: kRB 16-key row blocks x HW heads; the scale (> 0,
           // in log2 units) joins in the exponent's FMA and on the tile max
+          // k-step outer: the four row blocks' fragments of one k-step are
+          // read together, then feed kRB * HW independent accumulations, so
+          // no MFMA waits on the one before it or on a read just issued.
           f32x4 sc[kRB][HW];
     #pragma unroll
-          for (int rb = 0; rb < kRB; ++rb) {
-            u32x4 ka[KSTEPS];
+          for (int rb = 0; rb < kRB; ++rb)
     #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks)
-              ka[ks] = *(const u32x4 *)(kl + (rb * 16 + col) * T::kRow + ks * 32 + grp * 8);
+            for (int c = 0; c < HW; ++c) sc[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     #pragma unroll
-            for (int c = 0; c < HW; ++c) {
-              f32x4 s = {0.f, 0.f, 0.f, 0.f};
+          for (int ks = 0; ks < KSTEPS; ++ks) {
+            u32x4 ka[kRB];
     #pragma unroll
-              for (int ks = 0; ks < KSTEPS; ++ks) s = E::mfma(ka[ks], qf[c][ks], s);
-              sc[rb][c] = s;
-            }
+            for (int rb = 0; rb < kRB; ++rb)
+              ka[rb] = *(const u32x4 *)(kl + (rb * 16 + col) * T::kRow + ks * 32 + grp * 8);
+    #pragma unroll
+            for (int rb = 0; rb < kRB; ++rb)
+    #pragma unroll
+              for (int c = 0; c < HW; ++c) sc[rb][c] = E::mfma(ka[rb], qf[c][ks], sc[rb][c]);
           }
           if (t0 + kKT - 1 > wave_lo) {  // causal edge: keys past a row's position
     #pragma unroll
