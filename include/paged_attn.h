@@ -66,7 +66,8 @@ enum {
   PA_ERR_ALIGN = -7      /* a pointer is not aligned as required */
 };
 
-/* Version of this ABI; bumped on any incompatible change. */
+/* Version of this ABI; bumped on any incompatible change (7: the V cache
+ * layout became [num_blocks][num_kv_heads][block_size/4][head_dim][4]). */
 int pa_abi_version(void);
 
 /* Text for a return code (static storage). */

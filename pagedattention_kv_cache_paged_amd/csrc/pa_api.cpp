@@ -74,7 +74,7 @@ bool decode_sizes_ok(int32_t num_seqs, int32_t num_kv_heads, int32_t num_heads,
 
 extern "C" {
 
-int pa_abi_version(void) { return 6; }
+int pa_abi_version(void) { return 7; }
 
 const char *pa_strerror(int code) {
   switch (code) {

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
             "paged_validate_prefill", "paged_attention_prefill_fp8"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 6
+    assert lib.pa_abi_version() == 7
 
 
 def test_single_hip_runtime():
