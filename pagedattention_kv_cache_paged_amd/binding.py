@@ -16,6 +16,7 @@ import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpaged_attn.so")
+ABI_VERSION = 7  # the argument lists and layouts below are those of this version
 
 PA_F16, PA_BF16 = 0, 1
 PA_OK = 0
@@ -56,6 +57,9 @@ def load() -> ctypes.CDLL:
                             ctypes.c_float, ctypes.c_size_t)
     lib.pa_abi_version.restype = ctypes.c_int
     lib.pa_abi_version.argtypes = []
+    if lib.pa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {lib.pa_abi_version()}, this binding "
+                           f"expects {ABI_VERSION}: rebuild the library")
     lib.pa_strerror.restype = ctypes.c_char_p
     lib.pa_strerror.argtypes = [ctypes.c_int]
     lib.paged_kv_write.restype = ctypes.c_int
