@@ -357,6 +357,10 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
           for (int rb = 0; rb < kRB; ++rb)
     #pragma unroll
             for (int c = 0; c < HW; ++c) sc[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+          // Raised wave priority over the QK MFMAs: when both waves of a
+          // SIMD can issue, the one with matrix work goes first and the
+          // other fills the vector ALU.
+          __builtin_amdgcn_s_setprio(1);
     #pragma unroll
           for (int ks = 0; ks < KSTEPS; ++ks) {
             u32x4 ka[kRB];
@@ -368,6 +372,7 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
     #pragma unroll
               for (int c = 0; c < HW; ++c) sc[rb][c] = E::mfma(ka[rb], qf[c][ks], sc[rb][c]);
           }
+          __builtin_amdgcn_s_setprio(0);
           if (t0 + kKT - 1 > wave_lo) {  // causal edge: keys past a row's position
     #pragma unroll
             for (int rb = 0; rb < kRB; ++rb)
