@@ -158,6 +158,9 @@ def test_split_and_workspace():
         32 * 192 * 128 * 4 + 32 * 192 * 2 * 4 + 512)
     assert B.workspace_bytes(64, 32, 8, 128, 128, 16, 2048) == 0
     assert B.workspace_bytes(0, 32, 8, 128, 128, 16) == 0
+    # the batch limit: 8192 sequences (lengths and tile prefix in LDS)
+    assert B.workspace_bytes(8192, 4, 2, 64, 3, 16) > 0
+    assert B.workspace_bytes(8193, 4, 2, 64, 3, 16) == 0
 
 
 def test_validate_metadata():

@@ -233,6 +233,20 @@ def test_append_matches_separate_calls(fp8, pt):
     assert np.array_equal(got, host_bits(out2)), "fused and separate outputs differ"
 
 
+def test_append_max_batch():
+    """The fused step at the largest batch (8192 sequences), short ragged
+    contexts: caches bit-exact, outputs against the oracle."""
+    g = np.random.default_rng(6)
+    w = W.build("maxa", g.integers(1, 41, size=8192), num_heads=4, num_kv_heads=2,
+                head_dim=64, block_size=16, dtype=W.F16, seed=124)
+    say("append max batch")
+    got, kc, vc = run_append(w)
+    rk, rv = oracle_state(w)
+    assert np.array_equal(kc, rk) and np.array_equal(vc, rv)
+    ref = oracle.decode(w.q, rk, rv, w.block_tables, w.context_lens, w.scale, 16, w.dtype)
+    check_close(got, ref, w.dtype, "append max batch")
+
+
 # ---- E4M3 caches ------------------------------------------------------------
 
 @pytest.mark.parametrize("name,make,full", [NAMED[0], NAMED[2], NAMED[4], NAMED[5]],

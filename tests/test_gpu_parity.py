@@ -195,6 +195,21 @@ def test_max_partition_and_group():
         check_close(got, ref, w.dtype, f"max bs{bs}")
 
 
+def test_max_batch():
+    """The largest batch the library takes (8192 sequences: their lengths
+    and tile prefix fill 64 KB of LDS in every wavefront of the split
+    pass), short ragged contexts, default split and one tile per wavefront."""
+    g = np.random.default_rng(5)
+    w = W.build("maxb", g.integers(1, 41, size=8192), num_heads=4, num_kv_heads=2,
+                head_dim=64, block_size=16, dtype=W.F16, seed=123)
+    c = Case(w)
+    kc, vc = oracle_caches(w)
+    ref = oracle.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, 16, w.dtype)
+    for pt in (0, 16):
+        say(f"max batch pt={pt}")
+        check_close(c.decode(partition_tokens=pt), ref, w.dtype, f"max batch pt{pt}")
+
+
 # ---- invariants -----------------------------------------------------------------------------
 
 def test_partition_size_invariance():
