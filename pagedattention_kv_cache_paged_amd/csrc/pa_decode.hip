@@ -611,21 +611,30 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   }
 }
 
+// Query heads per merge workgroup (one wavefront each), at most: when each
+// sequence has few partials, workgroups of four wavefronts dispatch faster
+// than four single-wavefront ones, which shortens this latency-bound launch
+// by about 1 us at 2048 (sequence, head) rows (eight or sixteen are slower
+// again); with many partials per sequence the four heavier wavefronts of a
+// workgroup compete on one CU, and the launcher uses one.
+constexpr int kMergeHeads = 4;
+
 // Log-sum-exp merge of the partial results of one (sequence, query head):
 //   M = max_p m_p,  c_p = l_p * 2^(m_p - M),  out = sum_p c_p o_p / sum_p c_p.
 // The partials of sequence s come from wavefronts wave_of(cu[s]) ..
 // wave_of(cu[s+1] - 1), in consecutive slots starting at that first
 // wavefront + s.
 template <int DT, int D>
-__global__ __launch_bounds__(kWave) void decode_merge_kernel(
+__global__ __launch_bounds__(kMergeHeads * kWave) void decode_merge_kernel(
     uint16_t *__restrict__ out, const float *__restrict__ ws_o,
     const float *__restrict__ ws_ml, const int32_t *__restrict__ ws_cu, int num_seqs,
     int num_heads, int waves, int slots) {
   using E = Elem<DT>;
   constexpr int PER = D / kWave;  // dims per lane
-  const int head = blockIdx.x;
+  const int head = blockIdx.x * (int)(blockDim.x / kWave) + (int)(threadIdx.x / kWave);
   const int seq = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x % kWave;
+  if (head >= num_heads) return;
   const int n_tiles = ws_cu[num_seqs];
   const int c0 = ws_cu[seq], c1 = ws_cu[seq + 1];
   if (c1 <= c0) return;  // nothing to attend: the split pass wrote zeros
@@ -700,8 +709,10 @@ int launch_typed(const DecodeArgs &a) {
     if (e != hipSuccess) return (int)e;
   }
   if (a.stages & 2) {
-    dim3 g2((unsigned)a.num_heads, (unsigned)a.num_seqs);
-    decode_merge_kernel<DT, D><<<g2, kWave, 0, st>>>((uint16_t *)a.out, a.ws_o, a.ws_ml,
+    // about waves / num_seqs partials per sequence
+    const int mh = a.waves <= 4 * a.num_seqs ? kMergeHeads : 1;
+    dim3 g2((unsigned)((a.num_heads + mh - 1) / mh), (unsigned)a.num_seqs);
+    decode_merge_kernel<DT, D><<<g2, mh * kWave, 0, st>>>((uint16_t *)a.out, a.ws_o, a.ws_ml,
                                                      a.ws_cu, a.num_seqs, a.num_heads,
                                                      a.waves, a.slots);
     e = hipGetLastError();
