@@ -193,6 +193,7 @@ def cpu_baseline(w, seconds: float, fp8: bool = False):
         t_total += time.perf_counter() - t0
         done_tokens += int(w.context_lens[n])
         n += 1
+    # one GPU's share of the host: at most 16 threads, whatever the host has
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
     t0 = time.perf_counter()
     with ThreadPoolExecutor(max_workers=threads) as ex:
@@ -205,6 +206,7 @@ def cpu_baseline(w, seconds: float, fp8: bool = False):
             "kind": "oracle",
             "sample": f"{sample}, one sequence per task on {threads} threads, {t_pool:.2f} s",
             "seq_tokens_per_s": round(done_tokens / t_pool, 1), "cpu": cpu_model(),
+            "host_cpus": os.cpu_count(), "cpus_usable": len(os.sched_getaffinity(0)),
             "single_thread": {"value": round(kvb / t_total / 1e9, 6), "unit": "GB/s",
                               "cores": 1, "seq_tokens_per_s": round(done_tokens / t_total, 1),
                               "sample": f"{sample}, single thread, {t_total:.1f} s"}}
@@ -611,14 +613,14 @@ def main():
                 ws.data_ptr(), ws.numel(), stages, sp)
         assert rc == 0, rc
 
-    def fused(i):
+    def fused(i, stages=3):
         kc, vc = caches[i % copies]
-        rc = lib.paged_attention_decode_append(
+        rc = lib.paged_attention_decode_append_stages(
             out.data_ptr(), q.data_ptr(), nk.data_ptr(), nv.data_ptr(), kc.data_ptr(),
             vc.data_ptr(), bt.data_ptr(), cl.data_ptr(), w.scale, FP8_K_SCALE, FP8_V_SCALE,
             w.block_size, w.num_kv_heads, w.num_seqs, w.num_heads, w.head_dim,
             w.max_blocks_per_seq, w.num_blocks, dtc, 1 if fp8 else 0, pt, ws.data_ptr(),
-            ws.numel(), sp)
+            ws.numel(), stages, sp)
         assert rc == 0, rc
 
     def separate(i):
@@ -656,16 +658,24 @@ def main():
     torch.cuda.synchronize()
     ms_other = o0.elapsed_time(o1) / K
 
-    # Roofline of the split pass: K back-to-back split launches on the launch
-    # stream, bracketed by two events (average launch duration, no event
-    # overhead between launches).
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record(stream)
-    for i in range(K):
-        decode(i, 1)
-    s1.record(stream)
-    torch.cuda.synchronize()
-    t_split = s0.elapsed_time(s1) / K * 1e3   # us
+    def back_to_back(fn):
+        """Average duration of K back-to-back calls of fn(i) on the launch
+        stream, bracketed by two events (no event overhead between them)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(K):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K * 1e3   # us
+
+    # Roofline of the dominant kernel: the split pass of the step timed above
+    # (the fused step's variant, which also stores the new tokens), alone.
+    t_split = back_to_back(lambda i: fused(i, 1))
+    # The plain decode's split pass, and the decode alone (split + merge, no
+    # append: attention over the block tables).
+    t_split_plain = back_to_back(lambda i: decode(i, 1))
+    t_decode = back_to_back(lambda i: decode(i, 3))
 
     # Per-launch breakdown (informative): the same K steps again with events
     # between the launches, which adds the events' own overhead.
@@ -695,6 +705,11 @@ def main():
     kv_bytes = w.unique_tokens * kv_bytes_per_token(w, fp8)
     gbs = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (t_split * 1e-6) / 1e9
+    dec_gbs = kv_bytes / (t_decode * 1e-6) / 1e9
+    # cache slots the sequences hold (whole blocks) against tokens stored
+    slots_held = sum(-(-int(L) // w.block_size) * w.block_size for L in w.context_lens)
+    if w.shared_tokens:
+        slots_held -= (w.num_seqs - 1) * w.shared_tokens
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -727,13 +742,20 @@ def main():
         "seq_tokens_per_s": round(w.logical_tokens / (ms_step * 1e-3), 1),
         "new_tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "split_us_back_to_back": round(t_split, 3),
+        "split_plain_us_back_to_back": round(t_split_plain, 3),
+        "t_decode": {"us": round(t_decode, 3), "GB/s": round(dec_gbs, 2),
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "seq_tokens_per_s": round(w.logical_tokens / (t_decode * 1e-6), 1),
+                     "what": "split pass + merge pass back to back, no append (the append "
+                             "is timed separately in kernel_us_event_bracketed.kv_write)"},
+        "cache_tokens_per_slot": round(w.unique_tokens / slots_held, 4),
         "kernel_us_event_bracketed": {
             "kv_write": round(t_write, 3), "decode_split": round(t_part, 3),
             "decode_merge": round(t_merge, 3),
             "decode_split_p10_p50_p90": [round(x, 3) for x in p_part]},
         "host_wall_ms_per_step": round(t_wall * 1e3 / K, 5),
         "roofline": {
-            "kernel": "decode_split_kernel",
+            "kernel": "decode_split_kernel (fused-append variant)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

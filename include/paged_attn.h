@@ -67,7 +67,8 @@ enum {
 };
 
 /* Version of this ABI; bumped on any incompatible change (7: the V cache
- * layout became [num_blocks][num_kv_heads][block_size/4][head_dim][4]). */
+ * layout became [num_blocks][num_kv_heads][block_size/4][head_dim][4];
+ * 8: paged_attention_decode_append_stages). */
 int pa_abi_version(void);
 
 /* Text for a return code (static storage). */
@@ -248,6 +249,28 @@ int paged_attention_decode_append(void *out, const void *q, const void *k_new,
                                   int32_t max_blocks_per_seq, int64_t num_blocks,
                                   int32_t dtype, int32_t kv_fp8, int32_t partition_tokens,
                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * paged_attention_decode_append split into its two launches, as
+ * paged_attention_decode_stages splits paged_attention_decode: stages 1 =
+ * the split pass with the new tokens' stores (sequences held by one
+ * wavefront get their final row), 2 = the merge pass (the same launch as
+ * paged_attention_decode_stages' stage 2; the split pass with the same
+ * arguments must have run before it on the same stream), 3 = both, which is
+ * paged_attention_decode_append.  Other values give PA_ERR_SHAPE.  Running
+ * stage 1 again with the same arguments stores the same bytes again.
+ */
+int paged_attention_decode_append_stages(void *out, const void *q, const void *k_new,
+                                         const void *v_new, void *k_cache, void *v_cache,
+                                         const int32_t *block_tables,
+                                         const int32_t *context_lens, float scale,
+                                         float k_scale, float v_scale, int32_t block_size,
+                                         int32_t num_kv_heads, int32_t num_seqs,
+                                         int32_t num_heads, int32_t head_dim,
+                                         int32_t max_blocks_per_seq, int64_t num_blocks,
+                                         int32_t dtype, int32_t kv_fp8,
+                                         int32_t partition_tokens, void *workspace,
+                                         size_t workspace_bytes, int32_t stages, void *stream);
 
 /*
  * Paged (chunked) prefill attention ("vLLM core architecture overview"

@@ -195,15 +195,54 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
     return out
 
 
+def all_rows(num_seqs: int, num_heads: int) -> np.ndarray:
+    """Every (seq, head) pair, sequence-major: int32 [num_seqs * num_heads, 2]."""
+    s, h = np.meshgrid(np.arange(num_seqs), np.arange(num_heads), indexing="ij")
+    return np.ascontiguousarray(np.stack([s.ravel(), h.ravel()], 1), dtype=np.int32)
+
+
+def host_threads() -> int:
+    """Threads for a pooled oracle run: the CPUs this process may use, at
+    most 16 (one GPU's share of a GPU host's cores)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _pooled(fn, rows, d, threads):
+    """fn(out_chunk, rows_chunk) over chunks of rows on a pool of host
+    threads; the C oracle runs outside Python's lock, so the chunks run
+    concurrently.  Each row is computed exactly as in a single call."""
+    out = np.zeros((rows.shape[0], d), dtype=np.float64)
+    if threads <= 1 or rows.shape[0] <= 1:
+        fn(out, rows)
+        return out
+    from concurrent.futures import ThreadPoolExecutor
+    n = min(rows.shape[0], threads * 8)
+    bounds = np.linspace(0, rows.shape[0], n + 1).astype(np.int64)
+
+    def run(i):
+        a, b = int(bounds[i]), int(bounds[i + 1])
+        if b > a:
+            chunk_out = np.zeros((b - a, d), dtype=np.float64)
+            fn(chunk_out, np.ascontiguousarray(rows[a:b]))
+            out[a:b] = chunk_out
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(run, range(n)))
+    return out
+
+
 def decode_rows(rows, q, k_cache, v_cache, block_tables, context_lens, scale,
-                block_size, dtype) -> np.ndarray:
-    """Selected (seq, head) rows; returns float64 [len(rows), D]."""
+                block_size, dtype, threads: int = 1) -> np.ndarray:
+    """Selected (seq, head) rows; returns float64 [len(rows), D].  With
+    threads > 1 the rows are shared out over that many host threads."""
     rows = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
     keep, args, (_, _, d) = _decode_args(q, k_cache, v_cache, block_tables,
                                          context_lens, scale, block_size, dtype)
-    out = np.zeros((rows.shape[0], d), dtype=np.float64)
-    _check(_load().oracle_decode_rows(_ptr(out), _ptr(rows), rows.shape[0], *args),
-           "oracle_decode_rows")
+    lib = _load()
+
+    def fn(out, rr):
+        _check(lib.oracle_decode_rows(_ptr(out), _ptr(rr), rr.shape[0], *args),
+               "oracle_decode_rows")
+    out = _pooled(fn, rows, d, threads)
     del keep
     return out
 
@@ -237,7 +276,7 @@ def f64_to_e4m3(y: float) -> int:
 def kv_write_fp8(k, v, slot_mapping, k_cache, v_cache, block_size: int, dtype,
                  k_scale: float, v_scale: float) -> None:
     """In-place quantising scatter of 16-bit k/v [T, Hkv, D] into uint8 E4M3
-    caches ([N, Hkv, bs, D] and [N, Hkv, D, bs]) at slot_mapping."""
+    caches ([N, Hkv, bs, D] and [N, Hkv, bs // 4, D, 4]) at slot_mapping."""
     k, v = _u16(k), _u16(v)
     slot = np.ascontiguousarray(slot_mapping, dtype=np.int64)
     assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
@@ -283,14 +322,18 @@ def decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale, block_siz
 
 
 def decode_fp8_rows(rows, q, k_cache, v_cache, block_tables, context_lens, scale,
-                    block_size, q_dtype, k_scale, v_scale) -> np.ndarray:
-    """Selected (seq, head) rows of decode_fp8; returns float64 [len(rows), D]."""
+                    block_size, q_dtype, k_scale, v_scale, threads: int = 1) -> np.ndarray:
+    """Selected (seq, head) rows of decode_fp8; returns float64 [len(rows), D].
+    With threads > 1 the rows are shared out over that many host threads."""
     rows = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
     keep, args, (_, _, d) = _decode_fp8_args(q, k_cache, v_cache, block_tables, context_lens,
                                              scale, block_size, q_dtype, k_scale, v_scale)
-    out = np.zeros((rows.shape[0], d), dtype=np.float64)
-    _check(_load().oracle_decode_fp8_rows(_ptr(out), _ptr(rows), rows.shape[0], *args),
-           "oracle_decode_fp8_rows")
+    lib = _load()
+
+    def fn(out, rr):
+        _check(lib.oracle_decode_fp8_rows(_ptr(out), _ptr(rr), rr.shape[0], *args),
+               "oracle_decode_fp8_rows")
+    out = _pooled(fn, rows, d, threads)
     del keep
     return out
 

@@ -5,8 +5,11 @@ The compute lives in libpaged_attn.so (C ABI in include/paged_attn.h);
 that the input generator (``workloads``) can be used without torch.
 """
 _BINDING = ("paged_kv_write", "paged_attention_decode", "paged_kv_write_fp8",
-            "paged_attention_decode_fp8", "split_waves",
-            "workspace_bytes", "validate_metadata", "PagedAttentionError", "load")
+            "paged_attention_decode_fp8", "paged_attention_decode_append",
+            "paged_attention_prefill", "paged_attention_prefill_fp8", "paged_copy_blocks",
+            "paged_swap_blocks", "BlockPool", "split_waves", "workspace_bytes",
+            "validate_metadata", "validate_prefill", "validate_copy_pairs",
+            "validate_swap_pairs", "v_shape", "PagedAttentionError", "load")
 
 __all__ = list(_BINDING)
 

@@ -16,7 +16,7 @@ import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpaged_attn.so")
-ABI_VERSION = 7  # the argument lists and layouts below are those of this version
+ABI_VERSION = 8  # the argument lists and layouts below are those of this version
 
 PA_F16, PA_BF16 = 0, 1
 PA_OK = 0
@@ -80,10 +80,12 @@ def load() -> ctypes.CDLL:
     lib.paged_attention_decode_fp8.restype = ctypes.c_int
     lib.paged_attention_decode_fp8.argtypes = [p, p, p, p, p, p, f32, f32, f32, i32, i32, i32,
                                                i32, i32, i32, i64, i32, i32, p, sz, i32, p]
+    app = [p, p, p, p, p, p, p, p, f32, f32, f32, i32, i32, i32, i32, i32, i32, i64, i32, i32,
+           i32, p, sz]
     lib.paged_attention_decode_append.restype = ctypes.c_int
-    lib.paged_attention_decode_append.argtypes = [p, p, p, p, p, p, p, p, f32, f32, f32, i32,
-                                                  i32, i32, i32, i32, i32, i64, i32, i32, i32,
-                                                  p, sz, p]
+    lib.paged_attention_decode_append.argtypes = app + [p]
+    lib.paged_attention_decode_append_stages.restype = ctypes.c_int
+    lib.paged_attention_decode_append_stages.argtypes = app + [i32, p]
     lib.paged_attention_prefill.restype = ctypes.c_int
     lib.paged_attention_prefill.argtypes = [p, p, p, p, p, p, p, f32, i32, i32, i32, i32, i32,
                                             i32, i64, i32, i32, p]
@@ -175,13 +177,20 @@ _workspaces = {}
 
 
 def workspace(dev, nbytes: int) -> Optional[torch.Tensor]:
-    """A cached uint8 device buffer of at least nbytes (grown on demand)."""
+    """A cached uint8 device buffer of at least nbytes (grown on demand), one
+    per (device, stream): the decode writes its partial results there and
+    reads them back in a second launch on the same stream, so calls on
+    different streams must not share a buffer.  The buffer is allocated while
+    that stream is current, so torch's allocator orders its reuse after the
+    stream's queued work when a larger one replaces it."""
     if nbytes == 0:
         return None
-    key = (dev.type, dev.index)
+    stream = torch.cuda.current_stream(dev)
+    key = (dev.type, dev.index, stream.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(stream):
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
@@ -353,12 +362,13 @@ def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: tor
                                   context_lens: torch.Tensor, scale: float, block_size: int,
                                   num_kv_heads: int, k_scale: Optional[float] = None,
                                   v_scale: Optional[float] = None, partition_tokens: int = 0,
-                                  workspace_tensor: Optional[torch.Tensor] = None
-                                  ) -> torch.Tensor:
+                                  workspace_tensor: Optional[torch.Tensor] = None,
+                                  stages: int = 3) -> torch.Tensor:
     """Store each sequence's new token (k_new, v_new [B, Hkv, D]) at context
     position L-1 of its block table, then decode over all L tokens.  uint8
     caches hold E4M3 codes and need k_scale, v_scale; 16-bit caches share
-    q's dtype.  Returns out."""
+    q's dtype.  stages: 1 split pass (with the stores), 2 merge, 3 both.
+    Returns out."""
     dev = _dev(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens)
     if q.dim() != 3 or out.shape != q.shape:
         raise ValueError("q and out must be [num_seqs, num_heads, head_dim]")
@@ -388,11 +398,11 @@ def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: tor
     ws = workspace_tensor if workspace_tensor is not None else workspace(dev, need)
     ws_ptr = ws.data_ptr() if ws is not None else None
     ws_len = ws.numel() * ws.element_size() if ws is not None else 0
-    rc = load().paged_attention_decode_append(
+    rc = load().paged_attention_decode_append_stages(
         out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
         v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
         float(k_scale or 1.0), float(v_scale or 1.0), block_size, num_kv_heads, B, hq, d, mb,
-        nb, dt, 1 if fp8 else 0, partition_tokens, ws_ptr, ws_len, _stream(dev))
+        nb, dt, 1 if fp8 else 0, partition_tokens, ws_ptr, ws_len, stages, _stream(dev))
     _check("paged_attention_decode_append", rc)
     return out
 

@@ -67,14 +67,16 @@ bool decode_sizes_ok(int32_t num_seqs, int32_t num_kv_heads, int32_t num_heads,
          num_kv_heads <= kMaxGrid && num_heads > 0 && num_heads <= kMaxGrid &&
          num_heads % num_kv_heads == 0 && num_heads / num_kv_heads <= pa::kMaxGroup &&
          supported_dim(head_dim) && supported_bs(block_size) && max_blocks_per_seq > 0 &&
-         (int64_t)max_blocks_per_seq * block_size <= INT32_MAX / 2;
+         (int64_t)max_blocks_per_seq * block_size <= INT32_MAX / 2 &&
+         // the split pass keeps its tile prefix over all sequences in int32
+         tiles_cap(num_seqs, max_blocks_per_seq, block_size) <= INT32_MAX;
 }
 
 }  // namespace
 
 extern "C" {
 
-int pa_abi_version(void) { return 7; }
+int pa_abi_version(void) { return 8; }
 
 const char *pa_strerror(int code) {
   switch (code) {
@@ -94,7 +96,8 @@ int32_t paged_attention_split_waves(int32_t num_seqs, int32_t num_kv_heads,
                                     int32_t max_blocks_per_seq, int32_t block_size,
                                     int32_t partition_tokens) {
   if (num_seqs <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
-      !supported_bs(block_size) || !valid_partition(partition_tokens))
+      !supported_bs(block_size) || !valid_partition(partition_tokens) ||
+      tiles_cap(num_seqs, max_blocks_per_seq, block_size) > INT32_MAX)
     return 0;
   const int64_t w = split_waves(num_seqs, num_kv_heads, max_blocks_per_seq, block_size,
                                 partition_tokens);
@@ -191,6 +194,24 @@ static int decode_common(void *out, const void *q, const void *k_cache, const vo
   return pa::launch_decode(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
 }
 
+int paged_attention_decode_append_stages(void *out, const void *q, const void *k_new,
+                                         const void *v_new, void *k_cache, void *v_cache,
+                                         const int32_t *block_tables,
+                                         const int32_t *context_lens, float scale,
+                                         float k_scale, float v_scale, int32_t block_size,
+                                         int32_t num_kv_heads, int32_t num_seqs,
+                                         int32_t num_heads, int32_t head_dim,
+                                         int32_t max_blocks_per_seq, int64_t num_blocks,
+                                         int32_t dtype, int32_t kv_fp8,
+                                         int32_t partition_tokens, void *workspace,
+                                         size_t workspace_bytes, int32_t stages, void *stream) {
+  if (kv_fp8 != 0 && kv_fp8 != 1) return PA_ERR_DTYPE;
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                       num_kv_heads, num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                       num_blocks, dtype, partition_tokens, workspace, workspace_bytes, stages,
+                       kv_fp8, k_scale, v_scale, stream, 1, k_new, v_new);
+}
+
 int paged_attention_decode_append(void *out, const void *q, const void *k_new,
                                   const void *v_new, void *k_cache, void *v_cache,
                                   const int32_t *block_tables, const int32_t *context_lens,
@@ -200,11 +221,12 @@ int paged_attention_decode_append(void *out, const void *q, const void *k_new,
                                   int64_t num_blocks, int32_t dtype, int32_t kv_fp8,
                                   int32_t partition_tokens, void *workspace,
                                   size_t workspace_bytes, void *stream) {
-  if (kv_fp8 != 0 && kv_fp8 != 1) return PA_ERR_DTYPE;
-  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
-                       num_kv_heads, num_seqs, num_heads, head_dim, max_blocks_per_seq,
-                       num_blocks, dtype, partition_tokens, workspace, workspace_bytes, 3,
-                       kv_fp8, k_scale, v_scale, stream, 1, k_new, v_new);
+  return paged_attention_decode_append_stages(out, q, k_new, v_new, k_cache, v_cache,
+                                              block_tables, context_lens, scale, k_scale,
+                                              v_scale, block_size, num_kv_heads, num_seqs,
+                                              num_heads, head_dim, max_blocks_per_seq,
+                                              num_blocks, dtype, kv_fp8, partition_tokens,
+                                              workspace, workspace_bytes, 3, stream);
 }
 
 int paged_attention_decode_stages(void *out, const void *q, const void *k_cache,

@@ -31,11 +31,12 @@ def test_library_exports_every_declared_symbol():
             "paged_attention_decode_stages", "paged_attention_workspace_bytes",
             "paged_attention_split_waves", "paged_validate_metadata", "pa_strerror",
             "pa_abi_version", "paged_kv_write_fp8", "paged_attention_decode_fp8",
-            "paged_attention_decode_append", "paged_attention_prefill",
+            "paged_attention_decode_append", "paged_attention_decode_append_stages",
+            "paged_attention_prefill",
             "paged_validate_prefill", "paged_attention_prefill_fp8"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 7
+    assert lib.pa_abi_version() == 8
 
 
 def test_single_hip_runtime():
@@ -71,6 +72,8 @@ def _decode(**kw):
     (dict(B=-1), -3),
     (dict(B=70000), -3),
     (dict(B=8193), -3),              # tile prefix of more sequences than LDS holds
+    (dict(B=8192, mb=300000), -3),   # 2.46e9 tiles per KV head: past the int32 tile prefix
+    (dict(B=4, mb=600000000), -3),   # a table wider than int32 positions
     (dict(mb=0), -3),
     (dict(nb=0), -3),
     (dict(scale=float("nan")), -3),
@@ -161,6 +164,12 @@ def test_split_and_workspace():
     # the batch limit: 8192 sequences (lengths and tile prefix in LDS)
     assert B.workspace_bytes(8192, 4, 2, 64, 3, 16) > 0
     assert B.workspace_bytes(8193, 4, 2, 64, 3, 16) == 0
+    # the split pass's tile prefix is int32: at most 2^31 - 1 tiles per KV head
+    # (8192 sequences x 262143 tiles fits; x 262145 does not)
+    assert B.split_waves(8192, 8, 262143, 16) > 0
+    assert B.workspace_bytes(8192, 32, 8, 128, 262143, 16) > 0
+    assert B.split_waves(8192, 8, 262145, 16) == 0
+    assert B.workspace_bytes(8192, 32, 8, 128, 262145, 16) == 0
 
 
 def test_validate_metadata():

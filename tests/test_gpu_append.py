@@ -6,7 +6,7 @@ oracle_kv_write of the history and of each sequence's new token (its slot is
 position L-1 of its block table), bit for bit over both whole buffers, and
 the output is oracle_decode over those caches, within
 |gpu - oracle| <= 2e-3 + 1e-2 * |oracle|.  Covered: the named workloads
-(sampled rows at full size, in the default launch configuration), ragged
+(every output row, in the default launch configuration), ragged
 shapes over head_dim, block size and GQA group, empty sequences and
 one-token sequences (the new token alone), partition sizes down to one tile,
 and the E4M3 caches (codes bit-exact, attention as for
@@ -55,13 +55,6 @@ def check_close(got_bits, ref, dtype, what=""):
     bad = ~(err <= ATOL + RTOL * np.abs(ref))
     say(f"  {what} max_abs={err.max():.3e} n={ref.size}")
     assert not bad.any(), f"{what}: {bad.sum()} out of tolerance, worst {err[bad].max():.3e}"
-
-
-def rows_sample(w, n, seed):
-    g = np.random.default_rng(seed)
-    seqs = np.arange(w.num_seqs) if w.num_seqs <= n else np.sort(
-        g.choice(w.num_seqs, n, replace=False))
-    return np.array([(s, int(g.integers(w.num_heads))) for s in seqs], dtype=np.int32)
 
 
 def new_rows(w, live=None):
@@ -119,13 +112,13 @@ def oracle_state(w, fp8=False, live=None):
     return kc, vc
 
 
-NAMED = [("tiny", W.tiny, True), ("short_bs8", lambda: W.short(8), True),
-         ("short_bs16", lambda: W.short(16), True), ("short_bs32", lambda: W.short(32), True),
-         ("llama8b", W.llama8b, False), ("prefix", W.prefix, False), ("long", W.long, False)]
+NAMED = [("tiny", W.tiny), ("short_bs8", lambda: W.short(8)),
+         ("short_bs16", lambda: W.short(16)), ("short_bs32", lambda: W.short(32)),
+         ("llama8b", W.llama8b), ("prefix", W.prefix), ("long", W.long)]
 
 
-@pytest.mark.parametrize("name,make,full", NAMED, ids=[n for n, _, _ in NAMED])
-def test_append_named(name, make, full):
+@pytest.mark.parametrize("name,make", NAMED, ids=[n for n, _ in NAMED])
+def test_append_named(name, make):
     w = make()
     say(f"append {name} B={w.num_seqs} Hq={w.num_heads} Hkv={w.num_kv_heads} "
         f"D={w.head_dim} bs={w.block_size}")
@@ -133,15 +126,11 @@ def test_append_named(name, make, full):
     rk, rv = oracle_state(w)
     assert np.array_equal(kc, rk) and np.array_equal(vc, rv), "caches differ from the oracle"
     assert np.all(np.isfinite(f64(got, w.dtype)))
-    if full:
-        ref = oracle.decode(w.q, rk, rv, w.block_tables, w.context_lens, w.scale,
-                            w.block_size, w.dtype)
-        check_close(got, ref, w.dtype, name)
-    else:
-        rows = rows_sample(w, 64 if name != "long" else 16, seed=11)
-        ref = oracle.decode_rows(rows, w.q, rk, rv, w.block_tables, w.context_lens, w.scale,
-                                 w.block_size, w.dtype)
-        check_close(got[rows[:, 0], rows[:, 1]], ref, w.dtype, name)
+    # every output row, the oracle's rows shared out over host threads
+    rows = oracle.all_rows(w.num_seqs, w.num_heads)
+    ref = oracle.decode_rows(rows, w.q, rk, rv, w.block_tables, w.context_lens, w.scale,
+                             w.block_size, w.dtype, threads=oracle.host_threads())
+    check_close(got, ref.reshape(got.shape), w.dtype, name)
 
 
 @pytest.mark.parametrize("i,G,D,bs,dt", [(0, 1, 64, 8, W.F16), (1, 4, 128, 16, W.BF16),
@@ -249,23 +238,19 @@ def test_append_max_batch():
 
 # ---- E4M3 caches ------------------------------------------------------------
 
-@pytest.mark.parametrize("name,make,full", [NAMED[0], NAMED[2], NAMED[4], NAMED[5]],
-                         ids=["tiny", "short_bs16", "llama8b", "prefix"])
-def test_append_fp8_named(name, make, full):
+@pytest.mark.parametrize("name,make", NAMED, ids=[n for n, _ in NAMED])
+def test_append_fp8_named(name, make):
+    """The fused step over E4M3 caches on every named workload: codes
+    bit-exact over both caches, every output row against the oracle."""
     w = make()
     say(f"append fp8 {name}")
     got, kc, vc = run_append(w, fp8=True)
     rk, rv = oracle_state(w, fp8=True)
     assert np.array_equal(kc, rk) and np.array_equal(vc, rv), "E4M3 caches differ"
-    if full:
-        ref = oracle.decode_fp8(w.q, rk, rv, w.block_tables, w.context_lens, w.scale,
-                                w.block_size, w.dtype, KS, VS)
-        check_close(got, ref, w.dtype, f"fp8 {name}")
-    else:
-        rows = rows_sample(w, 64, seed=12)
-        ref = oracle.decode_fp8_rows(rows, w.q, rk, rv, w.block_tables, w.context_lens,
-                                     w.scale, w.block_size, w.dtype, KS, VS)
-        check_close(got[rows[:, 0], rows[:, 1]], ref, w.dtype, f"fp8 {name}")
+    rows = oracle.all_rows(w.num_seqs, w.num_heads)
+    ref = oracle.decode_fp8_rows(rows, w.q, rk, rv, w.block_tables, w.context_lens, w.scale,
+                                 w.block_size, w.dtype, KS, VS, threads=oracle.host_threads())
+    check_close(got, ref.reshape(got.shape), w.dtype, f"fp8 {name}")
 
 
 @pytest.mark.parametrize("bs", [8, 32])

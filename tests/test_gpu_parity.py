@@ -4,9 +4,9 @@
   sentinels in every slot not written must survive).
 * paged_attention_decode: |gpu - oracle| <= 2e-3 + 1e-2 * |oracle| element
   by element (fp16 / bf16 inputs, fp32 accumulation, output rounded to the
-  input type), on the five named workloads (full outputs where the oracle is
-  fast, sampled rows at full size otherwise, in the launch configuration the
-  benchmark uses), on random ragged shapes over every supported head_dim,
+  input type), on the five named workloads (every output row, in the launch
+  configuration the benchmark uses; the oracle's rows are shared out over
+  host threads), on random ragged shapes over every supported head_dim,
   block size and GQA group, and on the method's invariants.
 """
 import math
@@ -119,23 +119,20 @@ def test_write_bit_exact(name, make):
     assert np.array_equal(host_bits(c.vc), vc)
 
 
-def _rows_sample(w, n, seed):
-    g = np.random.default_rng(seed)
-    seqs = np.arange(w.num_seqs) if w.num_seqs <= n else np.sort(
-        g.choice(w.num_seqs, n, replace=False))
-    return np.array([(s, int(g.integers(w.num_heads))) for s in seqs], dtype=np.int32)
+def oracle_all(w, kc, vc, context_lens=None):
+    """Every (seq, head) row of the oracle, the rows shared out over host
+    threads; float64 [B, Hq, D]."""
+    rows = oracle.all_rows(w.num_seqs, w.num_heads)
+    ref = oracle.decode_rows(rows, w.q, kc, vc, w.block_tables,
+                             w.context_lens if context_lens is None else context_lens,
+                             w.scale, w.block_size, w.dtype, threads=oracle.host_threads())
+    return ref.reshape(w.num_seqs, w.num_heads, w.head_dim)
 
 
-@pytest.mark.parametrize("name,make,full", [
-    ("tiny", W.tiny, True),
-    ("short_bs8", lambda: W.short(8), True),
-    ("short_bs16", lambda: W.short(16), True),
-    ("short_bs32", lambda: W.short(32), True),
-    ("llama8b", W.llama8b, False),
-    ("prefix", W.prefix, False),
-    ("long", W.long, False),
-], ids=["tiny", "short_bs8", "short_bs16", "short_bs32", "llama8b", "prefix", "long"])
-def test_decode_named(name, make, full):
+@pytest.mark.parametrize("name,make", NAMED, ids=[n for n, _ in NAMED])
+def test_decode_named(name, make):
+    """Every output row of each named workload, in the benchmark's launch
+    configuration (default split)."""
     w = make()
     say(f"decode {name} B={w.num_seqs} Hq={w.num_heads} Hkv={w.num_kv_heads} "
         f"D={w.head_dim} bs={w.block_size} "
@@ -143,15 +140,8 @@ def test_decode_named(name, make, full):
     got = Case(w).decode()
     kc, vc = oracle_caches(w)
     assert np.all(np.isfinite(f64(got, w.dtype)))
-    if full:
-        ref = oracle.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
-                            w.block_size, w.dtype)
-        check_close(got, ref, w.dtype, name)
-    else:
-        rows = _rows_sample(w, 64 if name != "long" else 16, seed=7)
-        ref = oracle.decode_rows(rows, w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
-                                 w.block_size, w.dtype)
-        check_close(got[rows[:, 0], rows[:, 1]], ref, w.dtype, name)
+    ref = oracle_all(w, kc, vc)
+    check_close(got, ref, w.dtype, name)
 
 
 # ---- random ragged shapes ------------------------------------------------------------

@@ -365,6 +365,22 @@ def test_rows_equal_full():
         assert np.array_equal(got[i], full[s, h])
 
 
+@pytest.mark.parametrize("threads", [2, 3, 8])
+def test_pooled_rows_equal_full(threads):
+    """Rows shared out over host threads (how the GPU tests check every row
+    of the large workloads) equal the single full call, bit for bit."""
+    w = W.build("pool", [1, 17, 33, 100, 250, 5, 64], num_heads=8, num_kv_heads=2,
+                head_dim=64, block_size=16, dtype=W.BF16, seed=17)
+    kc, vc = fill(w)
+    full = run(w, kc, vc)
+    rows = oracle.all_rows(w.num_seqs, w.num_heads)
+    assert rows.shape == (w.num_seqs * w.num_heads, 2)
+    assert np.array_equal(rows[w.num_heads + 3], [1, 3])
+    got = oracle.decode_rows(rows, w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                             w.block_size, w.dtype, threads=threads)
+    assert np.array_equal(got.reshape(full.shape), full)
+
+
 # ---- metadata errors --------------------------------------------------------------------
 
 def test_bad_block_id_refused():
