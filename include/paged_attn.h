@@ -63,7 +63,8 @@ enum {
   PA_ERR_WORKSPACE = -4, /* workspace missing or smaller than required */
   PA_ERR_LAUNCH = -5,    /* the HIP runtime refused a launch */
   PA_ERR_METADATA = -6,  /* (validator) bad block table, length or slot */
-  PA_ERR_ALIGN = -7      /* a pointer is not aligned as required */
+  PA_ERR_ALIGN = -7,     /* a pointer is not aligned as required */
+  PA_ERR_SCRATCH = -8    /* (no-allocation call) needs more than the fixed scratch */
 };
 
 /* Version of this ABI; bumped on any incompatible change (7: the V cache
@@ -271,6 +272,34 @@ int paged_attention_decode_append_stages(void *out, const void *q, const void *k
                                          int32_t dtype, int32_t kv_fp8,
                                          int32_t partition_tokens, void *workspace,
                                          size_t workspace_bytes, int32_t stages, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the step
+ * of paged_attention_decode_append with no workspace argument.  Its partial
+ * results and tile prefix go to a fixed 16 MiB array inside the library
+ * (PA_SCRATCH_BYTES), one per GPU, held until the process ends; the call
+ * allocates nothing.  Every other argument, result and error is that of
+ * paged_attention_decode_append.  Sizes whose workspace
+ * (paged_attention_workspace_bytes) exceeds PA_SCRATCH_BYTES are refused
+ * with PA_ERR_SCRATCH before anything is enqueued; the five workloads this
+ * library is measured on need at most about 9 MiB (8 x 32768 tokens, 64
+ * query heads).  Every call on one GPU shares that GPU's array and leaves
+ * its contents behind (nothing in it needs clearing between calls): calls
+ * that overlap on one GPU -- on other streams, or from other threads before
+ * the first has finished on the device -- race and give unspecified results.
+ */
+#define PA_SCRATCH_BYTES ((size_t)16 << 20)
+int paged_attention_decode_append_noalloc(void *out, const void *q, const void *k_new,
+                                          const void *v_new, void *k_cache, void *v_cache,
+                                          const int32_t *block_tables,
+                                          const int32_t *context_lens, float scale,
+                                          float k_scale, float v_scale, int32_t block_size,
+                                          int32_t num_kv_heads, int32_t num_seqs,
+                                          int32_t num_heads, int32_t head_dim,
+                                          int32_t max_blocks_per_seq, int64_t num_blocks,
+                                          int32_t dtype, int32_t kv_fp8,
+                                          int32_t partition_tokens, void *stream);
 
 /*
  * Paged (chunked) prefill attention ("vLLM core architecture overview"

@@ -20,7 +20,8 @@ ABI_VERSION = 8  # the argument lists and layouts below are those of this versio
 
 PA_F16, PA_BF16 = 0, 1
 PA_OK = 0
-_ERR_SHAPE = {-2, -3, -7}
+_ERR_SHAPE = {-2, -3, -7, -8}
+SCRATCH_BYTES = 16 << 20  # PA_SCRATCH_BYTES: the no-allocation step's fixed workspace
 
 _DTYPES = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
@@ -86,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.paged_attention_decode_append.argtypes = app + [p]
     lib.paged_attention_decode_append_stages.restype = ctypes.c_int
     lib.paged_attention_decode_append_stages.argtypes = app + [i32, p]
+    lib.paged_attention_decode_append_noalloc.restype = ctypes.c_int
+    lib.paged_attention_decode_append_noalloc.argtypes = app[:-2] + [p]
     lib.paged_attention_prefill.restype = ctypes.c_int
     lib.paged_attention_prefill.argtypes = [p, p, p, p, p, p, p, f32, i32, i32, i32, i32, i32,
                                             i32, i64, i32, i32, p]
@@ -356,19 +359,9 @@ def paged_attention_decode_fp8(out: torch.Tensor, q: torch.Tensor, k_cache: torc
 
 # ---- decode step with the append fused in ---------------------------------
 
-def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
-                                  v_new: torch.Tensor, k_cache: torch.Tensor,
-                                  v_cache: torch.Tensor, block_tables: torch.Tensor,
-                                  context_lens: torch.Tensor, scale: float, block_size: int,
-                                  num_kv_heads: int, k_scale: Optional[float] = None,
-                                  v_scale: Optional[float] = None, partition_tokens: int = 0,
-                                  workspace_tensor: Optional[torch.Tensor] = None,
-                                  stages: int = 3) -> torch.Tensor:
-    """Store each sequence's new token (k_new, v_new [B, Hkv, D]) at context
-    position L-1 of its block table, then decode over all L tokens.  uint8
-    caches hold E4M3 codes and need k_scale, v_scale; 16-bit caches share
-    q's dtype.  stages: 1 split pass (with the stores), 2 merge, 3 both.
-    Returns out."""
+def _append_shapes(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                   block_size, num_kv_heads, k_scale, v_scale):
+    """Checks of the fused step's tensors; returns (dev, B, hq, d, mb, nb, dt, fp8)."""
     dev = _dev(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens)
     if q.dim() != 3 or out.shape != q.shape:
         raise ValueError("q and out must be [num_seqs, num_heads, head_dim]")
@@ -393,7 +386,25 @@ def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: tor
             raise ValueError("E4M3 caches: both uint8, with k_scale and v_scale")
     elif k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise ValueError("16-bit caches must share q's dtype")
-    mb = block_tables.shape[1]
+    return dev, B, hq, d, block_tables.shape[1], nb, dt, fp8
+
+
+def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                                  v_new: torch.Tensor, k_cache: torch.Tensor,
+                                  v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, scale: float, block_size: int,
+                                  num_kv_heads: int, k_scale: Optional[float] = None,
+                                  v_scale: Optional[float] = None, partition_tokens: int = 0,
+                                  workspace_tensor: Optional[torch.Tensor] = None,
+                                  stages: int = 3) -> torch.Tensor:
+    """Store each sequence's new token (k_new, v_new [B, Hkv, D]) at context
+    position L-1 of its block table, then decode over all L tokens.  uint8
+    caches hold E4M3 codes and need k_scale, v_scale; 16-bit caches share
+    q's dtype.  stages: 1 split pass (with the stores), 2 merge, 3 both.
+    Returns out."""
+    dev, B, hq, d, mb, nb, dt, fp8 = _append_shapes(out, q, k_new, v_new, k_cache, v_cache,
+                                                    block_tables, context_lens, block_size,
+                                                    num_kv_heads, k_scale, v_scale)
     need = workspace_bytes(B, hq, num_kv_heads, d, mb, block_size, partition_tokens)
     ws = workspace_tensor if workspace_tensor is not None else workspace(dev, need)
     ws_ptr = ws.data_ptr() if ws is not None else None
@@ -404,6 +415,30 @@ def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: tor
         float(k_scale or 1.0), float(v_scale or 1.0), block_size, num_kv_heads, B, hq, d, mb,
         nb, dt, 1 if fp8 else 0, partition_tokens, ws_ptr, ws_len, stages, _stream(dev))
     _check("paged_attention_decode_append", rc)
+    return out
+
+
+def paged_attention_decode_append_noalloc(out: torch.Tensor, q: torch.Tensor,
+                                          k_new: torch.Tensor, v_new: torch.Tensor,
+                                          k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                          block_tables: torch.Tensor,
+                                          context_lens: torch.Tensor, scale: float,
+                                          block_size: int, num_kv_heads: int,
+                                          k_scale: Optional[float] = None,
+                                          v_scale: Optional[float] = None,
+                                          partition_tokens: int = 0) -> torch.Tensor:
+    """paged_attention_decode_append with the library's fixed per-GPU
+    scratch array as its workspace: allocates nothing.  Calls that overlap on
+    one GPU race.  Sizes needing more than SCRATCH_BYTES raise ValueError."""
+    dev, B, hq, d, mb, nb, dt, fp8 = _append_shapes(out, q, k_new, v_new, k_cache, v_cache,
+                                                    block_tables, context_lens, block_size,
+                                                    num_kv_heads, k_scale, v_scale)
+    rc = load().paged_attention_decode_append_noalloc(
+        out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
+        float(k_scale or 1.0), float(v_scale or 1.0), block_size, num_kv_heads, B, hq, d, mb,
+        nb, dt, 1 if fp8 else 0, partition_tokens, _stream(dev))
+    _check("paged_attention_decode_append_noalloc", rc)
     return out
 
 

@@ -88,6 +88,8 @@ const char *pa_strerror(int code) {
     case PA_ERR_LAUNCH: return "kernel launch failed";
     case PA_ERR_METADATA: return "invalid block table, context length or slot";
     case PA_ERR_ALIGN: return "pointer not aligned as required";
+    case PA_ERR_SCRATCH:
+      return "the call needs more scratch than the library's fixed 16 MiB device array holds";
   }
   return "unknown error";
 }
@@ -161,7 +163,8 @@ static int decode_common(void *out, const void *q, const void *k_cache, const vo
                          int64_t num_blocks, int32_t dtype, int32_t partition_tokens,
                          void *workspace, size_t workspace_bytes, int32_t stages, int fp8,
                          float k_scale, float v_scale, void *stream, int append = 0,
-                         const void *k_new = nullptr, const void *v_new = nullptr) {
+                         const void *k_new = nullptr, const void *v_new = nullptr,
+                         bool use_scratch = false) {
   if (dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_DTYPE;
   if (stages < 1 || stages > 3) return PA_ERR_SHAPE;
   if (fp8 && !(valid_scale(k_scale) && valid_scale(v_scale))) return PA_ERR_SHAPE;
@@ -181,6 +184,11 @@ static int decode_common(void *out, const void *q, const void *k_cache, const vo
       (append && (!aligned(k_new, 4) || !aligned(v_new, 4))))
     return PA_ERR_ALIGN;
   const WsLayout l = ws_layout(num_seqs, num_heads, head_dim, waves);
+  if (use_scratch) {  // the library's fixed per-GPU array, after every other check
+    if ((size_t)l.total > pa::kScratchBytes) return PA_ERR_SCRATCH;
+    if (pa::scratch_buffer(&workspace) != 0) return PA_ERR_LAUNCH;
+    workspace_bytes = pa::kScratchBytes;
+  }
   if (!workspace || workspace_bytes < (size_t)l.total) return PA_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return PA_ERR_ALIGN;
   char *ws = static_cast<char *>(workspace);
@@ -227,6 +235,23 @@ int paged_attention_decode_append(void *out, const void *q, const void *k_new,
                                               num_heads, head_dim, max_blocks_per_seq,
                                               num_blocks, dtype, kv_fp8, partition_tokens,
                                               workspace, workspace_bytes, 3, stream);
+}
+
+int paged_attention_decode_append_noalloc(void *out, const void *q, const void *k_new,
+                                          const void *v_new, void *k_cache, void *v_cache,
+                                          const int32_t *block_tables,
+                                          const int32_t *context_lens, float scale,
+                                          float k_scale, float v_scale, int32_t block_size,
+                                          int32_t num_kv_heads, int32_t num_seqs,
+                                          int32_t num_heads, int32_t head_dim,
+                                          int32_t max_blocks_per_seq, int64_t num_blocks,
+                                          int32_t dtype, int32_t kv_fp8,
+                                          int32_t partition_tokens, void *stream) {
+  if (kv_fp8 != 0 && kv_fp8 != 1) return PA_ERR_DTYPE;
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                       num_kv_heads, num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                       num_blocks, dtype, partition_tokens, nullptr, 0, 3, kv_fp8, k_scale,
+                       v_scale, stream, 1, k_new, v_new, true);
 }
 
 int paged_attention_decode_stages(void *out, const void *q, const void *k_cache,

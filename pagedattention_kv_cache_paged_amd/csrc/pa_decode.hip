@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -743,6 +744,37 @@ int launch_dim(const DecodeArgs &a) {
 
 int launch_decode(const DecodeArgs &a) {
   return a.dtype == kBF16 ? launch_dim<kBF16>(a) : launch_dim<kF16>(a);
+}
+
+// Workspace of the no-allocation decode step.  Each GPU the library runs on
+// holds its own copy of this array at its own address.  In host code its name
+// is only a host-side stand-in, so kernels and copies take the device address
+// that hipGetSymbolAddress returns for the current device, looked up once
+// per device and cached.  Every call on one GPU shares the array: calls that
+// overlap on one GPU (other streams, other threads) race.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];
+}  // namespace
+
+int scratch_buffer(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return 0;
 }
 
 }  // namespace pa

@@ -15,6 +15,9 @@ constexpr int kMaxTilesPerWave = 64; // one tile per lane of the wave's tile map
 constexpr int kTargetWaves = 1024;   // default split: one wave per SIMD of 256 CUs
 constexpr int kMaxSeqs = 8192;       // tile prefix and lengths live in LDS
 constexpr int kPrefillMaxBlocks = 4096;  // prefill keeps a sequence's block ids in LDS
+// Device scratch of the no-allocation decode step: a fixed array in the
+// library's code object, one per GPU, held until the process ends.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
 
 struct DecodeArgs {
   void *out;
@@ -110,6 +113,9 @@ struct PrefillArgs {
 
 // Return 0 on success, a nonzero HIP error code otherwise.
 int launch_decode(const DecodeArgs &a);
+// Device address of the current GPU's kScratchBytes scratch array (looked
+// up once per device, then cached).
+int scratch_buffer(void **ptr);
 int launch_kv_write(const WriteArgs &a);
 int launch_copy_blocks(const CopyArgs &a);
 int launch_prefill(const PrefillArgs &a);

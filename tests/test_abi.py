@@ -32,6 +32,7 @@ def test_library_exports_every_declared_symbol():
             "paged_attention_split_waves", "paged_validate_metadata", "pa_strerror",
             "pa_abi_version", "paged_kv_write_fp8", "paged_attention_decode_fp8",
             "paged_attention_decode_append", "paged_attention_decode_append_stages",
+            "paged_attention_decode_append_noalloc",
             "paged_attention_prefill",
             "paged_validate_prefill", "paged_attention_prefill_fp8"} <= set(names)
     for n in names:
@@ -46,8 +47,8 @@ def test_single_hip_runtime():
 
 def test_strerror():
     lib = B.load()
-    for code in range(-7, 1):
-        assert lib.pa_strerror(code)
+    for code in range(-8, 1):
+        assert lib.pa_strerror(code) and lib.pa_strerror(code) != b"unknown error"
     assert lib.pa_strerror(-99) == b"unknown error"
 
 
@@ -231,6 +232,46 @@ def test_append_rejects_before_launch(kw, code):
 
 def test_append_zero_sequences_is_noop():
     assert _append(B=0, out=None, q=None, kn=None, vn=None) == 0
+
+
+def _noalloc(**kw):
+    a = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, scale=0.125,
+             ks=1.0, vs=1.0, bs=16, hkv=8, B=4, hq=32, d=128, mb=128, nb=1000, dtype=1, fp8=0,
+             pt=0, stream=None)
+    a.update(kw)
+    return B.load().paged_attention_decode_append_noalloc(
+        a["out"], a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["bt"], a["cl"], a["scale"],
+        a["ks"], a["vs"], a["bs"], a["hkv"], a["B"], a["hq"], a["d"], a["mb"], a["nb"],
+        a["dtype"], a["fp8"], a["pt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    # 512 x 32 heads: 1536 partial slots of 128 fp32 per head, 25 MB > 16 MiB
+    (dict(B=512), -8),
+    # 128-token split of 8 full 32k-token sequences, 64 heads: 2056 slots, 67 MB
+    (dict(B=8, hq=64, mb=2048, pt=128), -8),
+    (dict(d=96), -3), (dict(bs=12), -3), (dict(pt=24), -3), (dict(dtype=3), -2),
+])
+def test_noalloc_rejects_before_launch(kw, code):
+    """Sizes past the fixed scratch array are refused with PA_ERR_SCRATCH
+    before the library touches the GPU; other bad sizes as for the step with
+    a workspace."""
+    assert _noalloc(**kw) == code
+
+
+def test_noalloc_zero_sequences_is_noop():
+    assert _noalloc(B=0, out=None, q=None, kn=None, vn=None) == 0
+
+
+def test_noalloc_scratch_covers_named_workloads():
+    """The fixed 16 MiB holds the workspace of every named workload."""
+    for w in (W.tiny(), W.short(8), W.short(16), W.short(32)):
+        assert 0 < B.workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                     w.max_blocks_per_seq, w.block_size) <= B.SCRATCH_BYTES
+    for args in ((64, 32, 8, 128, 128, 16),     # llama8b
+                 (128, 32, 8, 128, 96, 16),     # prefix
+                 (8, 64, 8, 128, 2048, 16)):    # long
+        assert 0 < B.workspace_bytes(*args) <= B.SCRATCH_BYTES
 
 
 def test_append_binding_checks_shapes():
