@@ -498,6 +498,9 @@ def main():
                          "paged_kv_write + paged_attention_decode (three launches)")
     ap.add_argument("--kv-dtype", default="native", choices=("native", "fp8"),
                     help="KV cache element type: the workload's 16-bit type, or E4M3 codes")
+    ap.add_argument("--no-shared-path", action="store_true",
+                    help="prefix workload: decode without telling the library about the "
+                         "shared prefix (every sequence streams it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (byte-counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -572,9 +575,11 @@ def main():
     bt = torch.from_numpy(w.block_tables).to(dev)
     cl = torch.from_numpy(w.context_lens).to(dev)
     pt = args.partition
+    # shared prefix: the leading table entries every sequence holds by reference
+    sb = 0 if args.no_shared_path else w.shared_tokens // w.block_size
     waves = B.split_waves(w.num_seqs, w.num_kv_heads, w.max_blocks_per_seq, w.block_size, pt)
-    ws_need = B.workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
-                                w.max_blocks_per_seq, w.block_size, pt)
+    ws_need = B.workspace_bytes_shared(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                       w.max_blocks_per_seq, w.block_size, sb, pt)
     ws = torch.empty(max(ws_need, 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
@@ -599,7 +604,14 @@ def main():
 
     def decode(i, stages):
         kc, vc = caches[i % copies]
-        if fp8:
+        if sb:
+            rc = lib.paged_attention_decode_shared(
+                out.data_ptr(), q.data_ptr(), None, None, kc.data_ptr(), vc.data_ptr(),
+                bt.data_ptr(), cl.data_ptr(), w.scale, FP8_K_SCALE, FP8_V_SCALE, w.block_size,
+                w.num_kv_heads, w.num_seqs, w.num_heads, w.head_dim, w.max_blocks_per_seq,
+                w.num_blocks, dtc, 1 if fp8 else 0, sb, pt, ws.data_ptr(), ws.numel(), stages,
+                sp)
+        elif fp8:
             rc = lib.paged_attention_decode_fp8(
                 out.data_ptr(), q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bt.data_ptr(),
                 cl.data_ptr(), w.scale, FP8_K_SCALE, FP8_V_SCALE, w.block_size,
@@ -615,6 +627,15 @@ def main():
 
     def fused(i, stages=3):
         kc, vc = caches[i % copies]
+        if sb:
+            rc = lib.paged_attention_decode_shared(
+                out.data_ptr(), q.data_ptr(), nk.data_ptr(), nv.data_ptr(), kc.data_ptr(),
+                vc.data_ptr(), bt.data_ptr(), cl.data_ptr(), w.scale, FP8_K_SCALE, FP8_V_SCALE,
+                w.block_size, w.num_kv_heads, w.num_seqs, w.num_heads, w.head_dim,
+                w.max_blocks_per_seq, w.num_blocks, dtc, 1 if fp8 else 0, sb, pt,
+                ws.data_ptr(), ws.numel(), stages, sp)
+            assert rc == 0, rc
+            return
         rc = lib.paged_attention_decode_append_stages(
             out.data_ptr(), q.data_ptr(), nk.data_ptr(), nv.data_ptr(), kc.data_ptr(),
             vc.data_ptr(), bt.data_ptr(), cl.data_ptr(), w.scale, FP8_K_SCALE, FP8_V_SCALE,
@@ -735,6 +756,7 @@ def main():
             "waves_per_kv_head": waves,
             "pool_copies": copies, "pool_mb_per_copy": round(pool_bytes / 2**20, 1),
             "placement": args.placement if args.workload == "llama8b" else "random",
+            "shared_blocks": sb,
         },
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "step": args.step,

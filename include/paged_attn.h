@@ -69,7 +69,7 @@ enum {
 
 /* Version of this ABI; bumped on any incompatible change (7: the V cache
  * layout became [num_blocks][num_kv_heads][block_size/4][head_dim][4];
- * 8: paged_attention_decode_append_stages). */
+ * 8: paged_attention_decode_append_stages; 9: the shared-prefix decode). */
 int pa_abi_version(void);
 
 /* Text for a return code (static storage). */
@@ -272,6 +272,57 @@ int paged_attention_decode_append_stages(void *out, const void *q, const void *k
                                          int32_t dtype, int32_t kv_fp8,
                                          int32_t partition_tokens, void *workspace,
                                          size_t workspace_bytes, int32_t stages, void *stream);
+
+/*
+ * Decode with a prefix shared by the whole batch ("vLLM framework analysis:
+ * how PagedAttention speeds up LLM inference 20x" (intelliparadigm.com), 2.3:
+ * requests with a common system prompt hold its blocks by reference;
+ * "vLLM core architecture overview" (5688vip.com), 4.1: prefix blocks
+ * shared across requests).  The caller states that every sequence's first
+ * shared_blocks table entries are the same physical blocks and that every
+ * context_lens[s] >= shared_blocks * block_size (paged_validate_shared_prefix
+ * checks both on host copies; a violation gives unspecified values, the
+ * kernels staying inside every buffer).  The result is the attention of
+ * paged_attention_decode (k_new == v_new == NULL) or of
+ * paged_attention_decode_append (both non-NULL; then every context length
+ * must exceed the prefix, so that each new token lands in a private block),
+ * up to floating-point rounding; only the work is arranged differently: the
+ * prefix's K/V tiles are streamed once per group of sequences (as many as
+ * fill 32 matrix-core columns with their query heads) instead of once per
+ * sequence, and merged with each sequence's own tiles by log-sum-exp.  Only
+ * whole 16-token tiles of the prefix are shared (at block size 8 an odd
+ * shared_blocks leaves its last block with the private tokens);
+ * shared_blocks = 0 is the call without a prefix.  0 <= shared_blocks <=
+ * max_blocks_per_seq, else PA_ERR_SHAPE.  kv_fp8, scales, partition_tokens
+ * and stages as for paged_attention_decode_append_stages.  The workspace
+ * must hold paged_attention_workspace_bytes_shared bytes (the partials of
+ * the prefix come on top of those of paged_attention_workspace_bytes).
+ */
+size_t paged_attention_workspace_bytes_shared(int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t max_blocks_per_seq, int32_t block_size,
+                                              int32_t shared_blocks, int32_t partition_tokens);
+int paged_attention_decode_shared(void *out, const void *q, const void *k_new,
+                                  const void *v_new, void *k_cache, void *v_cache,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  float scale, float k_scale, float v_scale, int32_t block_size,
+                                  int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                                  int32_t head_dim, int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, int32_t dtype, int32_t kv_fp8,
+                                  int32_t shared_blocks, int32_t partition_tokens,
+                                  void *workspace, size_t workspace_bytes, int32_t stages,
+                                  void *stream);
+
+/*
+ * Host-side check of the shared-prefix contract (host pointers): every
+ * sequence's first shared_blocks table entries equal sequence 0's, every
+ * context length is at least shared_blocks * block_size, and with append != 0
+ * (the fused step) greater than it.  Returns PA_OK, PA_ERR_METADATA on a
+ * violation, PA_ERR_NULL / PA_ERR_SHAPE for bad arguments.
+ */
+int paged_validate_shared_prefix(const int32_t *block_tables, const int32_t *context_lens,
+                                 int32_t num_seqs, int32_t max_blocks_per_seq,
+                                 int32_t block_size, int32_t shared_blocks, int32_t append);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph

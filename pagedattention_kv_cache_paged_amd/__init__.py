@@ -6,6 +6,8 @@ that the input generator (``workloads``) can be used without torch.
 """
 _BINDING = ("paged_kv_write", "paged_attention_decode", "paged_kv_write_fp8",
             "paged_attention_decode_fp8", "paged_attention_decode_append",
+            "paged_attention_decode_append_noalloc", "paged_attention_decode_shared",
+            "workspace_bytes_shared", "validate_shared_prefix",
             "paged_attention_prefill", "paged_attention_prefill_fp8", "paged_copy_blocks",
             "paged_swap_blocks", "BlockPool", "split_waves", "workspace_bytes",
             "validate_metadata", "validate_prefill", "validate_copy_pairs",

@@ -16,7 +16,7 @@ import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpaged_attn.so")
-ABI_VERSION = 8  # the argument lists and layouts below are those of this version
+ABI_VERSION = 9  # the argument lists and layouts below are those of this version
 
 PA_F16, PA_BF16 = 0, 1
 PA_OK = 0
@@ -89,6 +89,13 @@ def load() -> ctypes.CDLL:
     lib.paged_attention_decode_append_stages.argtypes = app + [i32, p]
     lib.paged_attention_decode_append_noalloc.restype = ctypes.c_int
     lib.paged_attention_decode_append_noalloc.argtypes = app[:-2] + [p]
+    lib.paged_attention_decode_shared.restype = ctypes.c_int
+    lib.paged_attention_decode_shared.argtypes = app[:-3] + [i32, i32, p, sz, i32, p]
+    lib.paged_attention_workspace_bytes_shared.restype = sz
+    lib.paged_attention_workspace_bytes_shared.argtypes = [i32, i32, i32, i32, i32, i32, i32,
+                                                           i32]
+    lib.paged_validate_shared_prefix.restype = ctypes.c_int
+    lib.paged_validate_shared_prefix.argtypes = [p, p, i32, i32, i32, i32, i32]
     lib.paged_attention_prefill.restype = ctypes.c_int
     lib.paged_attention_prefill.argtypes = [p, p, p, p, p, p, p, f32, i32, i32, i32, i32, i32,
                                             i32, i64, i32, i32, p]
@@ -149,6 +156,9 @@ def _dtype(t: torch.Tensor) -> int:
 
 
 def _dev(*ts):
+    for t in ts:
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"expected torch tensors on the GPU, got {type(t).__name__}")
     dev = ts[0].device
     for t in ts:
         if t.device.type != "cuda" or t.device != dev:
@@ -440,6 +450,65 @@ def paged_attention_decode_append_noalloc(out: torch.Tensor, q: torch.Tensor,
         nb, dt, 1 if fp8 else 0, partition_tokens, _stream(dev))
     _check("paged_attention_decode_append_noalloc", rc)
     return out
+
+
+# ---- decode with a prefix shared by the whole batch ---------------------------
+
+def workspace_bytes_shared(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                           block_size, shared_blocks, partition_tokens: int = 0) -> int:
+    return int(load().paged_attention_workspace_bytes_shared(
+        num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+        shared_blocks, partition_tokens))
+
+
+def paged_attention_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                                  v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, scale: float, block_size: int,
+                                  num_kv_heads: int, shared_blocks: int,
+                                  k_new: Optional[torch.Tensor] = None,
+                                  v_new: Optional[torch.Tensor] = None,
+                                  k_scale: Optional[float] = None,
+                                  v_scale: Optional[float] = None, partition_tokens: int = 0,
+                                  stages: int = 3,
+                                  workspace_tensor: Optional[torch.Tensor] = None
+                                  ) -> torch.Tensor:
+    """Decode (k_new, v_new None) or the fused step (both given) when every
+    sequence's first shared_blocks table entries are the same blocks and
+    every context covers them: the prefix is streamed once per group of
+    sequences.  uint8 caches hold E4M3 codes (k_scale, v_scale).  Returns out."""
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    append = k_new is not None
+    kn = k_new if append else q.new_empty((q.shape[0], num_kv_heads, q.shape[2]))
+    vn = v_new if append else kn
+    dev, B, hq, d, mb, nb, dt, fp8 = _append_shapes(out, q, kn, vn, k_cache, v_cache,
+                                                    block_tables, context_lens, block_size,
+                                                    num_kv_heads, k_scale, v_scale)
+    need = workspace_bytes_shared(B, hq, num_kv_heads, d, mb, block_size, shared_blocks,
+                                  partition_tokens)
+    ws = workspace_tensor if workspace_tensor is not None else workspace(dev, need)
+    ws_ptr = ws.data_ptr() if ws is not None else None
+    ws_len = ws.numel() * ws.element_size() if ws is not None else 0
+    rc = load().paged_attention_decode_shared(
+        out.data_ptr(), q.data_ptr(), kn.data_ptr() if append else None,
+        vn.data_ptr() if append else None, k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), float(k_scale or 1.0),
+        float(v_scale or 1.0), block_size, num_kv_heads, B, hq, d, mb, nb, dt, 1 if fp8 else 0,
+        int(shared_blocks), partition_tokens, ws_ptr, ws_len, stages, _stream(dev))
+    _check("paged_attention_decode_shared", rc)
+    return out
+
+
+def validate_shared_prefix(block_tables, context_lens, block_size: int, shared_blocks: int,
+                           append: bool = False) -> int:
+    """Host check of the shared-prefix contract (numpy or CPU tensors);
+    returns the library's code (0 = valid)."""
+    import numpy as np
+    bt = np.ascontiguousarray(np.asarray(block_tables), dtype=np.int32)
+    cl = np.ascontiguousarray(np.asarray(context_lens), dtype=np.int32)
+    return int(load().paged_validate_shared_prefix(bt.ctypes.data, cl.ctypes.data, cl.size,
+                                                   bt.shape[1], block_size, shared_blocks,
+                                                   1 if append else 0))
 
 
 # ---- block pool and copy-on-write (include/paged_blocks.h) ------------------

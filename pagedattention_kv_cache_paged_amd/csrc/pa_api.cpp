@@ -26,9 +26,11 @@ bool valid_partition(int32_t pt) {
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-// Upper bound on the 16-token tiles of one KV head over all sequences.
-int64_t tiles_cap(int64_t seqs, int64_t max_blocks, int64_t bs) {
-  return seqs * ((max_blocks * bs + pa::kTile - 1) / pa::kTile);
+// Upper bound on the 16-token tiles of one KV head over all sequences; with
+// `skip` shared tiles, over the tiles past them.
+int64_t tiles_cap(int64_t seqs, int64_t max_blocks, int64_t bs, int64_t skip = 0) {
+  const int64_t per = (max_blocks * bs + pa::kTile - 1) / pa::kTile - skip;
+  return seqs * (per > 0 ? per : 0);
 }
 
 // Wavefronts per KV head.  Enough that no wavefront gets more than
@@ -36,8 +38,8 @@ int64_t tiles_cap(int64_t seqs, int64_t max_blocks, int64_t bs) {
 // kTargetWaves in total, otherwise enough that a wavefront holds at most
 // partition_tokens tokens.  Never more than there can be tiles.
 int64_t split_waves(int64_t seqs, int64_t kv_heads, int64_t max_blocks, int64_t bs,
-                    int64_t pt) {
-  const int64_t cap = tiles_cap(seqs, max_blocks, bs);
+                    int64_t pt, int64_t skip = 0) {
+  const int64_t cap = tiles_cap(seqs, max_blocks, bs, skip);
   if (cap <= 0) return 1;
   const int64_t w_min = (cap + pa::kMaxTilesPerWave - 1) / pa::kMaxTilesPerWave;
   int64_t w = pt ? (cap * pa::kTile + pt - 1) / pt
@@ -48,17 +50,43 @@ int64_t split_waves(int64_t seqs, int64_t kv_heads, int64_t max_blocks, int64_t 
 
 // Workspace layout: partial outputs fp32 [H][slots][D], then (m, l) fp32
 // [H][slots][2], then the tile prefix int32 [seqs + 1]; slots = waves + seqs.
+// With a shared prefix of `chunks` chunks, then its partials fp32
+// [H][seqs][chunks][D] and their (m, l) [H][seqs][chunks][2].
 struct WsLayout {
-  int64_t o, ml, cu, total;
+  int64_t o, ml, cu, sh_o, sh_ml, total;
 };
-WsLayout ws_layout(int64_t seqs, int64_t heads, int64_t dim, int64_t waves) {
+WsLayout ws_layout(int64_t seqs, int64_t heads, int64_t dim, int64_t waves,
+                   int64_t chunks = 0) {
   const int64_t slots = waves + seqs;
   WsLayout l;
   l.o = 0;
   l.ml = round_up(heads * slots * dim * 4, pa::kWorkspaceAlign);
   l.cu = l.ml + round_up(heads * slots * 2 * 4, pa::kWorkspaceAlign);
-  l.total = l.cu + round_up((seqs + 1) * 4, pa::kWorkspaceAlign);
+  l.sh_o = l.cu + round_up((seqs + 1) * 4, pa::kWorkspaceAlign);
+  l.sh_ml = l.sh_o + round_up(heads * seqs * chunks * dim * 4, pa::kWorkspaceAlign);
+  l.total = l.sh_ml + (chunks ? round_up(heads * seqs * chunks * 2 * 4, pa::kWorkspaceAlign) : 0);
   return l;
+}
+
+// The shared-prefix plan: `shared_blocks` leading table entries, whole
+// 16-token tiles of them (a trailing half tile at block size 8 stays with
+// the private tiles).  tiles == 0: no shared path.
+pa::SharedPrefix shared_plan(int64_t seqs, int64_t heads, int64_t kv_heads,
+                             int64_t shared_blocks, int64_t bs) {
+  pa::SharedPrefix sh;
+  sh.tiles = (int32_t)(shared_blocks * bs / pa::kTile);
+  if (sh.tiles == 0 || seqs == 0) {
+    sh.tiles = 0;
+    return sh;
+  }
+  const int64_t g = heads / kv_heads;
+  sh.chunk_tiles = pa::kSharedChunkTiles;
+  sh.chunks = (sh.tiles + sh.chunk_tiles - 1) / sh.chunk_tiles;
+  sh.seqs_per_group = (int32_t)(16 / g);
+  const int64_t per_set = (int64_t)pa::kSharedGroups * sh.seqs_per_group;
+  sh.colsets = (int32_t)((seqs + per_set - 1) / per_set);
+  sh.waves = sh.chunks * sh.colsets;
+  return sh;
 }
 
 bool decode_sizes_ok(int32_t num_seqs, int32_t num_kv_heads, int32_t num_heads,
@@ -76,7 +104,7 @@ bool decode_sizes_ok(int32_t num_seqs, int32_t num_kv_heads, int32_t num_heads,
 
 extern "C" {
 
-int pa_abi_version(void) { return 8; }
+int pa_abi_version(void) { return 9; }
 
 const char *pa_strerror(int code) {
   switch (code) {
@@ -104,6 +132,24 @@ int32_t paged_attention_split_waves(int32_t num_seqs, int32_t num_kv_heads,
   const int64_t w = split_waves(num_seqs, num_kv_heads, max_blocks_per_seq, block_size,
                                 partition_tokens);
   return w * num_kv_heads > INT32_MAX ? 0 : (int32_t)w;
+}
+
+size_t paged_attention_workspace_bytes_shared(int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t max_blocks_per_seq, int32_t block_size,
+                                              int32_t shared_blocks,
+                                              int32_t partition_tokens) {
+  if (num_seqs <= 0 ||
+      !decode_sizes_ok(num_seqs, num_kv_heads, num_heads, head_dim, max_blocks_per_seq,
+                       block_size) ||
+      !valid_partition(partition_tokens) || shared_blocks < 0 ||
+      shared_blocks > max_blocks_per_seq)
+    return 0;
+  const pa::SharedPrefix sh = shared_plan(num_seqs, num_heads, num_kv_heads, shared_blocks,
+                                          block_size);
+  const int64_t w = split_waves(num_seqs, num_kv_heads, max_blocks_per_seq, block_size,
+                                partition_tokens, sh.tiles);
+  return (size_t)ws_layout(num_seqs, num_heads, head_dim, w, sh.chunks).total;
 }
 
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
@@ -164,7 +210,7 @@ static int decode_common(void *out, const void *q, const void *k_cache, const vo
                          void *workspace, size_t workspace_bytes, int32_t stages, int fp8,
                          float k_scale, float v_scale, void *stream, int append = 0,
                          const void *k_new = nullptr, const void *v_new = nullptr,
-                         bool use_scratch = false) {
+                         bool use_scratch = false, int32_t shared_blocks = 0) {
   if (dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_DTYPE;
   if (stages < 1 || stages > 3) return PA_ERR_SHAPE;
   if (fp8 && !(valid_scale(k_scale) && valid_scale(v_scale))) return PA_ERR_SHAPE;
@@ -173,17 +219,21 @@ static int decode_common(void *out, const void *q, const void *k_cache, const vo
       num_blocks <= 0 || num_blocks > INT32_MAX || !std::isfinite(scale) ||
       !valid_partition(partition_tokens))
     return PA_ERR_SHAPE;
+  if (shared_blocks < 0 || shared_blocks > max_blocks_per_seq) return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
+  pa::SharedPrefix sh = shared_plan(num_seqs, num_heads, num_kv_heads, shared_blocks,
+                                    block_size);
   const int64_t waves = split_waves(num_seqs, num_kv_heads, max_blocks_per_seq, block_size,
-                                    partition_tokens);
-  if (waves * num_kv_heads > INT32_MAX || waves + num_seqs > INT32_MAX) return PA_ERR_SHAPE;
+                                    partition_tokens, sh.tiles);
+  if ((waves + sh.waves) * num_kv_heads > INT32_MAX || waves + num_seqs > INT32_MAX)
+    return PA_ERR_SHAPE;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (append && (!k_new || !v_new)) return PA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 8) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
       (append && (!aligned(k_new, 4) || !aligned(v_new, 4))))
     return PA_ERR_ALIGN;
-  const WsLayout l = ws_layout(num_seqs, num_heads, head_dim, waves);
+  const WsLayout l = ws_layout(num_seqs, num_heads, head_dim, waves, sh.chunks);
   if (use_scratch) {  // the library's fixed per-GPU array, after every other check
     if ((size_t)l.total > pa::kScratchBytes) return PA_ERR_SCRATCH;
     if (pa::scratch_buffer(&workspace) != 0) return PA_ERR_LAUNCH;
@@ -199,6 +249,11 @@ static int decode_common(void *out, const void *q, const void *k_cache, const vo
                    reinterpret_cast<float *>(ws + l.o), reinterpret_cast<float *>(ws + l.ml),
                    reinterpret_cast<int32_t *>(ws + l.cu), stages, append, k_new, v_new,
                    fp8 ? 1.0f / k_scale : 1.0f, fp8 ? 1.0f / v_scale : 1.0f, stream};
+  if (sh.tiles > 0) {
+    sh.o = reinterpret_cast<float *>(ws + l.sh_o);
+    sh.ml = reinterpret_cast<float *>(ws + l.sh_ml);
+    a.sh = sh;
+  }
   return pa::launch_decode(a) == 0 ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -252,6 +307,26 @@ int paged_attention_decode_append_noalloc(void *out, const void *q, const void *
                        num_kv_heads, num_seqs, num_heads, head_dim, max_blocks_per_seq,
                        num_blocks, dtype, partition_tokens, nullptr, 0, 3, kv_fp8, k_scale,
                        v_scale, stream, 1, k_new, v_new, true);
+}
+
+int paged_attention_decode_shared(void *out, const void *q, const void *k_new,
+                                  const void *v_new, void *k_cache, void *v_cache,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  float scale, float k_scale, float v_scale, int32_t block_size,
+                                  int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                                  int32_t head_dim, int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, int32_t dtype, int32_t kv_fp8,
+                                  int32_t shared_blocks, int32_t partition_tokens,
+                                  void *workspace, size_t workspace_bytes, int32_t stages,
+                                  void *stream) {
+  if (kv_fp8 != 0 && kv_fp8 != 1) return PA_ERR_DTYPE;
+  if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_NULL;
+  const int append = k_new != nullptr;
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                       num_kv_heads, num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                       num_blocks, dtype, partition_tokens, workspace, workspace_bytes, stages,
+                       kv_fp8, k_scale, v_scale, stream, append, k_new, v_new, false,
+                       shared_blocks);
 }
 
 int paged_attention_decode_stages(void *out, const void *q, const void *k_cache,
@@ -386,6 +461,24 @@ int paged_validate_metadata(const int32_t *block_tables, const int32_t *context_
       if (sl >= slots || seen[(size_t)sl]) return PA_ERR_METADATA;
       seen[(size_t)sl] = 1;
     }
+  }
+  return PA_OK;
+}
+
+int paged_validate_shared_prefix(const int32_t *block_tables, const int32_t *context_lens,
+                                 int32_t num_seqs, int32_t max_blocks_per_seq,
+                                 int32_t block_size, int32_t shared_blocks, int32_t append) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || block_size <= 0 || shared_blocks < 0 ||
+      shared_blocks > max_blocks_per_seq)
+    return PA_ERR_SHAPE;
+  if (num_seqs > 0 && (!block_tables || !context_lens)) return PA_ERR_NULL;
+  const int64_t prefix = (int64_t)shared_blocks * block_size;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t len = context_lens[s];
+    if (len < prefix || (append && shared_blocks > 0 && len <= prefix)) return PA_ERR_METADATA;
+    for (int32_t i = 0; i < shared_blocks; ++i)
+      if (block_tables[(int64_t)s * max_blocks_per_seq + i] != block_tables[i])
+        return PA_ERR_METADATA;
   }
   return PA_OK;
 }

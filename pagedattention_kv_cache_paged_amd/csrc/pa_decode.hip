@@ -174,10 +174,219 @@ struct Frag<D, true> {
 // Tiles in flight per wave (register ring depth).
 constexpr int kBuf = 2;
 
+// Lazy rescale slack (log2 units): the reference max is raised only when a
+// tile's max exceeds it by more than this.
+constexpr float kSlack = 8.f;
+
+// Tiles in flight per shared-prefix wavefront.
+constexpr int kSharedBuf = 2;
+
+// One wavefront of a shared prefix ("vLLM framework analysis: how
+// PagedAttention speeds up LLM inference 20x" (intelliparadigm.com), 2.3:
+// sequences hold a common prompt's blocks by reference).  Every sequence's
+// first sh.tiles tiles are the same blocks, so one wavefront streams a chunk
+// of them once for the query heads of kSharedGroups * seqs_per_group
+// sequences: per tile, the K and V fragments are the A operands of the MFMAs
+// of every 16-column group (column c of group gi: sequence
+// (colset * kSharedGroups + gi) * seqs_per_group + c / G, head c % G).  Each
+// (sequence, query head) leaves one partial (o, m, l) per chunk for the
+// merge.  The prefix is read through the caches (other column sets read the
+// same chunk), and every tile is full.
+template <int DT, int D, int BS, bool KV8>
+__device__ __forceinline__ void shared_prefix_wave(
+    const SharedPrefix &sh, int sw, int kvh, const uint16_t *__restrict__ q,
+    const void *__restrict__ k_cache, const void *__restrict__ v_cache,
+    const int32_t *__restrict__ block_tables, float scale_log2, float out_scale,
+    int num_seqs, int num_kv_heads, int num_heads, int group, int64_t num_blocks) {
+  using E = Elem<DT>;
+  using CT = std::conditional_t<KV8, uint8_t, uint16_t>;
+  constexpr int KSTEPS = D / 32;
+  constexpr int DTILES = D / 16;
+  constexpr int NG = kSharedGroups;
+  const int lane = threadIdx.x;
+  const int row = lane & 15;
+  const int grp = lane >> 4;
+  // the column sets of one chunk are adjacent in launch order, so they run
+  // together and share the chunk in the caches
+  const int ch = sw / sh.colsets;
+  const int cs = sw - ch * sh.colsets;
+  const int tbeg = ch * sh.chunk_tiles;
+  const int cnt = min(sh.chunk_tiles, sh.tiles - tbeg);  // >= 1
+
+  // Lane l describes prefix tile tbeg + l (lanes past the chunk repeat its
+  // last tile): its block ids, from sequence 0's row of the table.
+  const int it = tbeg + min(lane, cnt - 1);
+  int b0, b1 = 0, boff = 0;
+  if constexpr (BS == 8) {
+    b0 = block_tables[2 * it];
+    b1 = block_tables[2 * it + 1];
+  } else if constexpr (BS == 16) {
+    b0 = block_tables[it];
+  } else {
+    b0 = block_tables[it >> 1];
+    boff = (it & 1) * kTile;
+  }
+  b0 = (b0 >= 0 && b0 < num_blocks) ? b0 : 0;  // ids outside the pool: stay inside it
+  b1 = (b1 >= 0 && b1 < num_blocks) ? b1 : 0;
+
+  // Query fragments of both column groups, held for the whole chunk (the
+  // dimension order of the private path: E4M3 codes come 16 to a lane).
+  int seq[NG], head[NG];
+  bool valid[NG];
+  u32x4 qf[NG][KSTEPS];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int s0 = (cs * NG + gi) * sh.seqs_per_group;
+    const int sq = s0 + row / group;
+    valid[gi] = row < sh.seqs_per_group * group && sq < num_seqs;
+    seq[gi] = valid[gi] ? sq : min(s0, num_seqs - 1);
+    head[gi] = kvh * group + (valid[gi] ? row % group : 0);
+    const uint16_t *qp = q + ((int64_t)seq[gi] * num_heads + head[gi]) * D;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int d0 = KV8 ? 64 * (ks / 2) + 16 * grp + 8 * (ks % 2) : 32 * ks + 8 * grp;
+      qf[gi][ks] = *(const u32x4 *)(qp + d0);
+    }
+  }
+
+  const int64_t blk_stride = (int64_t)num_kv_heads * BS * D;
+  const CT *kbase = static_cast<const CT *>(k_cache) + (int64_t)kvh * BS * D;
+  const CT *vbase = static_cast<const CT *>(v_cache) + (int64_t)kvh * D * BS;
+  // Loads of one full tile: lane (row, grp) reads token row's K dims and the
+  // four tokens 4 * grp .. +3 of V dimension row (+16 per fragment).
+  auto load = [&](Frag<D, KV8> &f, int idx) {
+    const int ka = __builtin_amdgcn_readlane(b0, idx);
+    const CT *kp, *vp;
+    if constexpr (BS == 8) {
+      const int kz = __builtin_amdgcn_readlane(b1, idx);
+      kp = kbase + (int64_t)(row < 8 ? ka : kz) * blk_stride + (row & 7) * D + grp * (KV8 ? 16 : 8);
+      vp = vbase + (int64_t)(grp < 2 ? ka : kz) * blk_stride + ((grp & 1) * D + row) * 4;
+    } else {
+      const int o = BS == 16 ? 0 : __builtin_amdgcn_readlane(boff, idx);
+      const CT *kblk = kbase + (int64_t)ka * blk_stride + o * D;
+      const CT *vblk = vbase + (int64_t)ka * blk_stride;
+      kp = kblk + (uint32_t)(row * D + grp * (KV8 ? 16 : 8));
+      vp = vblk + (uint32_t)((((o >> 2) + grp) * D + row) * 4);
+    }
+    if constexpr (KV8) {
+#pragma unroll
+      for (int h = 0; h < D / 64; ++h) f.k[h] = *(const u32x4 *)(kp + h * 64);
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt) f.v[dt] = *(const uint32_t *)(vp + dt * 64);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) f.k[ks] = *(const u32x4 *)(kp + ks * 32);
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt) f.v[dt] = *(const u32x2 *)(vp + dt * 64);
+    }
+  };
+
+  float m_ref[NG], l_run[NG];
+  f32x4 acc[NG][DTILES];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    m_ref[gi] = -INFINITY;
+    l_run[gi] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt) acc[gi][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One tile for both column groups: scores, lazy online softmax, P.V.
+  auto step = [&](Frag<D, KV8> &f) {
+    u32x4 kf[KSTEPS];
+    u32x2 vv[DTILES];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if constexpr (KV8) {
+        const u32x4 c = f.k[ks / 2];
+        const u32x2 a = E::from_e4m3(ks % 2 ? c.z : c.x);
+        const u32x2 b = E::from_e4m3(ks % 2 ? c.w : c.y);
+        kf[ks] = u32x4{a.x, a.y, b.x, b.y};
+      } else {
+        kf[ks] = f.k[ks];
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt) {
+      if constexpr (KV8) vv[dt] = E::from_e4m3(f.v[dt]);
+      else vv[dt] = f.v[dt];
+    }
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) sc = E::qk(kf[ks], qf[gi][ks], sc);
+      float sv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = sc[r] * scale_log2;
+      const float mx = rows_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+      if (__ballot(mx > m_ref[gi] + kSlack)) {
+        const float m_new = fmaxf(m_ref[gi], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref[gi] - m_new);
+        l_run[gi] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) acc[gi][dt] *= alpha;
+        m_ref[gi] = m_new;
+      }
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sv[r] - m_ref[gi]);
+      u32x2 ph, pl;
+      ph.x = E::pack(p[0], p[1]);
+      ph.y = E::pack(p[2], p[3]);
+      if constexpr (E::kSplitP) {
+        pl.x = E::pack(p[0] - E::lo(ph.x), p[1] - E::hi(ph.x));
+        pl.y = E::pack(p[2] - E::lo(ph.y), p[3] - E::hi(ph.y));
+        l_run[gi] += (p[0] + p[1]) + (p[2] + p[3]);
+      } else {
+        l_run[gi] += (E::lo(ph.x) + E::hi(ph.x)) + (E::lo(ph.y) + E::hi(ph.y));
+      }
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt) {
+        acc[gi][dt] = E::pv(vv[dt], ph, acc[gi][dt]);
+        if constexpr (E::kSplitP) acc[gi][dt] = E::pv(vv[dt], pl, acc[gi][dt]);
+      }
+    }
+  };
+
+  Frag<D, KV8> f[kSharedBuf];
+#pragma unroll
+  for (int b = 0; b < kSharedBuf - 1; ++b) load(f[b], min(b, cnt - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  for (int t = 0; t < cnt; t += kSharedBuf) {
+#pragma unroll
+    for (int b = 0; b < kSharedBuf; ++b) {
+      load(f[(b + kSharedBuf - 1) % kSharedBuf], min(t + b + kSharedBuf - 1, cnt - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + b < cnt) step(f[b]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // The chunk's partial of each (sequence, query head): lane (row, grp)
+  // holds dims 16 * dt + 4 * grp + 0..3 of column row.
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const float l_tot = rows_sum(l_run[gi]);
+    if (valid[gi]) {
+      const int64_t slot = ((int64_t)head[gi] * num_seqs + seq[gi]) * sh.chunks + ch;
+      const float inv = out_scale / l_tot;
+      float *op = sh.o + slot * D + grp * 4;
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt) *(f32x4 *)(op + dt * 16) = acc[gi][dt] * inv;
+      if (grp == 0) *(f32x2 *)(sh.ml + slot * 2) = f32x2{m_ref[gi], l_tot};
+    }
+  }
+}
+
 // KV8: the caches hold E4M3 codes; scale_log2 then carries k_scale and
 // out_scale is v_scale (1 for 16-bit caches).  APPEND: the fused decode
 // step, whose new tokens come from k_new / v_new (position L - 1).
-template <int DT, int D, int BS, bool KV8, bool APPEND>
+// SHARED: every sequence's first sh.tiles tiles are one shared prefix; the
+// first sh.waves * num_kv_heads workgroups stream it (shared_prefix_wave),
+// the others split only the tiles past it, and every sequence segment
+// leaves a partial for the merge.
+template <int DT, int D, int BS, bool KV8, bool APPEND, bool SHARED>
 __global__ __launch_bounds__(kWave) void decode_split_kernel(
     uint16_t *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml,
     int32_t *__restrict__ ws_cu, const uint16_t *__restrict__ q,
@@ -186,7 +395,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
     const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
     float scale_log2, float out_scale, float k_inv, float v_inv, int num_seqs,
     int num_kv_heads, int num_heads, int group, int max_blocks, int64_t num_blocks,
-    int waves, int slots) {
+    int waves, int slots, SharedPrefix sh) {
   using E = Elem<DT>;
   using CT = std::conditional_t<KV8, uint8_t, uint16_t>;  // cache element
   constexpr int KSTEPS = D / 32;  // 16x16x32 MFMAs per QK tile
@@ -205,15 +414,28 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   CT *kn_lds = KV8 ? reinterpret_cast<CT *>(vn_raw + D) : reinterpret_cast<CT *>(kn_raw);
   CT *vn_lds = KV8 ? kn_lds + D : reinterpret_cast<CT *>(vn_raw);
 
-  const int kvh = blockIdx.x % num_kv_heads;
-  const int j = blockIdx.x / num_kv_heads;
+  int bid = blockIdx.x;
+  if constexpr (SHARED) {
+    const int nsh = sh.waves * num_kv_heads;
+    if (bid < nsh) {
+      shared_prefix_wave<DT, D, BS, KV8>(sh, bid / num_kv_heads, bid % num_kv_heads, q,
+                                         k_cache, v_cache, block_tables, scale_log2,
+                                         out_scale, num_seqs, num_kv_heads, num_heads, group,
+                                         num_blocks);
+      return;
+    }
+    bid -= nsh;
+  }
+  const int kvh = bid % num_kv_heads;
+  const int j = bid / num_kv_heads;
   const int lane = threadIdx.x;
   const int row = lane & 15;  // A-row / B-column / head index inside a tile
   const int grp = lane >> 4;  // quarter of the wave: k-slice and 4-row group
   const int max_len = max_blocks * BS;
 
-  // Tile prefix over all sequences (the same in every wavefront).  Range-0
-  // wavefronts also write the zero rows of sequences with nothing to attend.
+  // Tile prefix over all sequences (the same in every wavefront); with a
+  // shared prefix, over the tiles past it.  Range-0 wavefronts also write the
+  // zero rows of sequences with nothing to attend.
   // With a fused append the last position L - 1 is the new token: the
   // wavefront holding that tile takes its K and V from k_new / v_new
   // instead of the cache and stores them into the cache slot.
@@ -222,13 +444,15 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
     const int s = c + lane;
     int len = s < num_seqs ? context_lens[s] : 0;
     len = min(max(len, 0), max_len);
-    const int incl = wave_incl_scan((len + kTile - 1) / kTile) + carry;
+    const int own = SHARED ? max((len + kTile - 1) / kTile - sh.tiles, 0)
+                           : (len + kTile - 1) / kTile;
+    const int incl = wave_incl_scan(own) + carry;
     if (s < num_seqs) {
       cu[s + 1] = incl;
       lens[s] = len;
     }
     carry = __shfl(incl, kWave - 1);
-    if (j == 0) {
+    if (!SHARED && j == 0) {
       uint64_t zero = __ballot(s < num_seqs && len == 0);
       while (zero) {
         const int zs = c + __builtin_ctzll(zero);
@@ -265,7 +489,8 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   const int sq = lo;
   const int first = cu[sq];
   const int ntiles_sq = cu[sq + 1] - first;
-  const int it = tau - first;
+  const int rel = tau - first;                  // among the sequence's split tiles
+  const int it = rel + (SHARED ? sh.tiles : 0);  // tile index in the sequence
   const int nvalid = min(kTile, lens[sq] - it * kTile);  // >= 1
   const int32_t *tbl = block_tables + (int64_t)sq * max_blocks;
   int b0, b1 = 0, boff = 0;
@@ -281,13 +506,14 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // Fused append: the sequence's last tile holds the new token at row
   // nvalid - 1; nblk is its block (-1 if the id is outside the pool: the
   // token then enters the attention but is not stored).
-  const bool is_new = APPEND && it == ntiles_sq - 1;
+  const bool is_new = APPEND && rel == ntiles_sq - 1;
   const int nraw = (BS == 8 && nvalid > 8) ? b1 : b0;
   const int nblk = (is_new && nraw >= 0 && nraw < num_blocks) ? nraw : -1;
   b0 = (b0 >= 0 && b0 < num_blocks) ? b0 : 0;  // ids outside the pool: stay inside it
   b1 = (b1 >= 0 && b1 < num_blocks) ? b1 : 0;
-  const int seg_end = (it == ntiles_sq - 1 || tau == t1 - 1) ? 1 : 0;
-  const int whole = (first >= t0 && first + ntiles_sq <= t1) ? 1 : 0;
+  const int seg_end = (rel == ntiles_sq - 1 || tau == t1 - 1) ? 1 : 0;
+  // (with a shared prefix no wavefront holds a whole sequence)
+  const int whole = (!SHARED && first >= t0 && first + ntiles_sq <= t1) ? 1 : 0;
   const uint64_t ends = __ballot(seg_end && lane < cnt);  // bit i: a segment ends at tile i
   // The flags of tile t0 + lane in one word, so that one readlane per tile
   // fetches them: bits 0-4 valid tokens, 5 segment end, 6 whole sequence,
@@ -402,7 +628,6 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // most tiles skip the rescale of the accumulators; the weights
   // 2^(s - m_ref) then stay below 2^kSlack, far inside fp32 and bfloat16
   // range.  The softmax is the same for any reference.
-  constexpr float kSlack = 8.f;
   float m_ref = -INFINITY;
   float l_run = 0.f;  // this lane's share of the running sum
   f32x4 acc[DTILES];
@@ -624,12 +849,13 @@ constexpr int kMergeHeads = 4;
 //   M = max_p m_p,  c_p = l_p * 2^(m_p - M),  out = sum_p c_p o_p / sum_p c_p.
 // The partials of sequence s come from wavefronts wave_of(cu[s]) ..
 // wave_of(cu[s+1] - 1), in consecutive slots starting at that first
-// wavefront + s.
-template <int DT, int D>
+// wavefront + s.  SHARED: also the sh.chunks partials of the shared prefix,
+// and a sequence held by one wavefront is merged too.
+template <int DT, int D, bool SHARED>
 __global__ __launch_bounds__(kMergeHeads * kWave) void decode_merge_kernel(
     uint16_t *__restrict__ out, const float *__restrict__ ws_o,
     const float *__restrict__ ws_ml, const int32_t *__restrict__ ws_cu, int num_seqs,
-    int num_heads, int waves, int slots) {
+    int num_heads, int waves, int slots, SharedPrefix sh) {
   using E = Elem<DT>;
   constexpr int PER = D / kWave;  // dims per lane
   const int head = blockIdx.x * (int)(blockDim.x / kWave) + (int)(threadIdx.x / kWave);
@@ -638,35 +864,46 @@ __global__ __launch_bounds__(kMergeHeads * kWave) void decode_merge_kernel(
   if (head >= num_heads) return;
   const int n_tiles = ws_cu[num_seqs];
   const int c0 = ws_cu[seq], c1 = ws_cu[seq + 1];
-  if (c1 <= c0) return;  // nothing to attend: the split pass wrote zeros
-  const int wv = min(waves, n_tiles);  // as in the split pass: all ranges non-empty
-  const int jf = wave_of(c0, n_tiles, wv);
-  const int jl = wave_of(c1 - 1, n_tiles, wv);
-  if (jf == jl) return;  // one wavefront held the sequence and wrote its row
-  const int np = jl - jf + 1;
+  int np = 0, jf = 0;
+  if (c1 > c0) {
+    const int wv = min(waves, n_tiles);  // as in the split pass: all ranges non-empty
+    jf = wave_of(c0, n_tiles, wv);
+    const int jl = wave_of(c1 - 1, n_tiles, wv);
+    if (!SHARED && jf == jl) return;  // one wavefront held the sequence and wrote its row
+    np = jl - jf + 1;
+  } else if (!SHARED) {
+    return;  // nothing to attend: the split pass wrote zeros
+  }
 
-  const int64_t base = (int64_t)head * slots + jf + seq;
-  const f32x2 *ml = (const f32x2 *)(ws_ml + base * 2);
   // One pass with a running maximum, so each partial's (m, l) and o are
   // loaded together: c_p = l_p * 2^(m_p - M) rescaled as M grows.
   float big = -INFINITY, den = 0.f;
   float num[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) num[i] = 0.f;
-  const float *o = ws_o + base * D + lane * PER;
+  auto absorb = [&](const f32x2 *ml, const float *o, int n) {
 #pragma unroll 4
-  for (int p = 0; p < np; ++p) {
-    const f32x2 v = ml[p];
-    float op[PER];
+    for (int p = 0; p < n; ++p) {
+      const f32x2 v = ml[p];
+      float op[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) op[i] = o[(int64_t)p * D + i];
-    const float m_new = fmaxf(big, v.x);
-    const float a = __builtin_amdgcn_exp2f(big - m_new);  // 0 on the first partial
-    const float c = v.y * __builtin_amdgcn_exp2f(v.x - m_new);
-    den = den * a + c;
+      for (int i = 0; i < PER; ++i) op[i] = o[(int64_t)p * D + i];
+      const float m_new = fmaxf(big, v.x);
+      const float a = __builtin_amdgcn_exp2f(big - m_new);  // 0 on the first partial
+      const float c = v.y * __builtin_amdgcn_exp2f(v.x - m_new);
+      den = den * a + c;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) num[i] = num[i] * a + c * op[i];
-    big = m_new;
+      for (int i = 0; i < PER; ++i) num[i] = num[i] * a + c * op[i];
+      big = m_new;
+    }
+  };
+  if constexpr (SHARED) {
+    const int64_t sb = ((int64_t)head * num_seqs + seq) * sh.chunks;
+    absorb((const f32x2 *)(sh.ml + sb * 2), sh.o + sb * D + lane * PER, sh.chunks);
+  }
+  if (np > 0) {
+    const int64_t base = (int64_t)head * slots + jf + seq;
+    absorb((const f32x2 *)(ws_ml + base * 2), ws_o + base * D + lane * PER, np);
   }
   const float inv = 1.0f / den;
   uint16_t *op = out + ((int64_t)seq * num_heads + head) * D + lane * PER;
@@ -684,27 +921,34 @@ int launch_typed(const DecodeArgs &a) {
   const float scale_log2 = (float)((double)a.scale * (double)a.k_scale * 1.4426950408889634);
   hipStream_t st = (hipStream_t)a.stream;
   const int group = a.num_heads / a.num_kv_heads;
+  const bool shared = a.sh.tiles > 0;
   hipError_t e = hipSuccess;
   if (a.stages & 1) {
-    dim3 grid((unsigned)a.num_kv_heads * (unsigned)a.waves);
+    dim3 grid((unsigned)a.num_kv_heads * (unsigned)(a.waves + (shared ? a.sh.waves : 0)));
     // LDS: tile prefix and lengths, query fragments, and for the fused
     // append the new rows (16-bit, plus E4M3 codes).
     const size_t lds = (size_t)((2 * a.num_seqs + 1 + 3) & ~3) * sizeof(int) +
                        (size_t)(D / 32) * kWave * 16 + (a.append ? 6 * D : 0);
-#define PA_SPLIT(KV8, APPEND, OUT_SCALE)                                                      \
-  decode_split_kernel<DT, D, BS, KV8, APPEND><<<grid, kWave, lds, st>>>(                      \
+#define PA_SPLIT(KV8, APPEND, SHARED, OUT_SCALE)                                               \
+  decode_split_kernel<DT, D, BS, KV8, APPEND, SHARED><<<grid, kWave, lds, st>>>(               \
       (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, (const uint16_t *)a.q, (void *)a.k_cache,  \
       (void *)a.v_cache, a.block_tables, a.context_lens, (const uint16_t *)a.k_new,           \
       (const uint16_t *)a.v_new, scale_log2, OUT_SCALE, a.k_inv, a.v_inv, a.num_seqs,         \
       a.num_kv_heads, a.num_heads, group, a.max_blocks_per_seq, a.num_blocks, a.waves,        \
-      a.slots)
+      a.slots, a.sh)
+#define PA_SPLIT_SH(KV8, APPEND, OUT_SCALE)                                                   \
+  do {                                                                                        \
+    if (shared) PA_SPLIT(KV8, APPEND, true, OUT_SCALE);                                       \
+    else PA_SPLIT(KV8, APPEND, false, OUT_SCALE);                                             \
+  } while (0)
     if (a.kv_fp8) {
-      if (a.append) PA_SPLIT(true, true, a.v_scale);
-      else PA_SPLIT(true, false, a.v_scale);
+      if (a.append) PA_SPLIT_SH(true, true, a.v_scale);
+      else PA_SPLIT_SH(true, false, a.v_scale);
     } else {
-      if (a.append) PA_SPLIT(false, true, 1.0f);
-      else PA_SPLIT(false, false, 1.0f);
+      if (a.append) PA_SPLIT_SH(false, true, 1.0f);
+      else PA_SPLIT_SH(false, false, 1.0f);
     }
+#undef PA_SPLIT_SH
 #undef PA_SPLIT
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
@@ -713,9 +957,14 @@ int launch_typed(const DecodeArgs &a) {
     // about waves / num_seqs partials per sequence
     const int mh = a.waves <= 4 * a.num_seqs ? kMergeHeads : 1;
     dim3 g2((unsigned)((a.num_heads + mh - 1) / mh), (unsigned)a.num_seqs);
-    decode_merge_kernel<DT, D><<<g2, mh * kWave, 0, st>>>((uint16_t *)a.out, a.ws_o, a.ws_ml,
-                                                     a.ws_cu, a.num_seqs, a.num_heads,
-                                                     a.waves, a.slots);
+    if (shared)
+      decode_merge_kernel<DT, D, true><<<g2, mh * kWave, 0, st>>>(
+          (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, a.num_seqs, a.num_heads, a.waves,
+          a.slots, a.sh);
+    else
+      decode_merge_kernel<DT, D, false><<<g2, mh * kWave, 0, st>>>(
+          (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, a.num_seqs, a.num_heads, a.waves,
+          a.slots, a.sh);
     e = hipGetLastError();
   }
   return (int)e;

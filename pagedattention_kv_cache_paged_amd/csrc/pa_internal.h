@@ -19,6 +19,25 @@ constexpr int kPrefillMaxBlocks = 4096;  // prefill keeps a sequence's block ids
 // library's code object, one per GPU, held until the process ends.
 constexpr size_t kScratchBytes = (size_t)16 << 20;
 
+// A prefix shared by every sequence of the batch: the first `tiles` 16-token
+// tiles of every sequence are the same blocks (sequence 0's table entries).
+// The split pass then gives that prefix to wavefronts of its own, each taking
+// `chunk_tiles` tiles of it for the query heads of several sequences at once
+// (kSharedGroups groups of 16 MFMA columns: seqs_per_group sequences of G
+// heads per group), and splits only the tiles past the prefix the usual way.
+constexpr int kSharedGroups = 2;       // 16-column MFMA groups per shared wavefront
+constexpr int kSharedChunkTiles = 32;  // prefix tiles per shared wavefront, at most
+struct SharedPrefix {
+  int32_t tiles = 0;           // shared tiles per sequence (0: no shared path)
+  int32_t chunk_tiles = 0;
+  int32_t chunks = 0;          // ceil(tiles / chunk_tiles)
+  int32_t seqs_per_group = 0;  // 16 / G
+  int32_t colsets = 0;         // wavefronts per chunk and KV head
+  int32_t waves = 0;           // shared wavefronts per KV head: chunks * colsets
+  float *o = nullptr;          // [num_heads][num_seqs][chunks][head_dim]
+  float *ml = nullptr;         // [num_heads][num_seqs][chunks][2]
+};
+
 struct DecodeArgs {
   void *out;
   const void *q;
@@ -54,6 +73,7 @@ struct DecodeArgs {
   float k_inv;         // float32(1 / k_scale): E4M3 quantisation of k_new
   float v_inv;
   void *stream;
+  SharedPrefix sh;     // tiles == 0: no shared prefix
 };
 
 struct WriteArgs {

@@ -32,12 +32,13 @@ def test_library_exports_every_declared_symbol():
             "paged_attention_split_waves", "paged_validate_metadata", "pa_strerror",
             "pa_abi_version", "paged_kv_write_fp8", "paged_attention_decode_fp8",
             "paged_attention_decode_append", "paged_attention_decode_append_stages",
-            "paged_attention_decode_append_noalloc",
+            "paged_attention_decode_append_noalloc", "paged_attention_decode_shared",
+            "paged_attention_workspace_bytes_shared", "paged_validate_shared_prefix",
             "paged_attention_prefill",
             "paged_validate_prefill", "paged_attention_prefill_fp8"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pa_abi_version() == 8
+    assert lib.pa_abi_version() == 9
 
 
 def test_single_hip_runtime():
@@ -232,6 +233,61 @@ def test_append_rejects_before_launch(kw, code):
 
 def test_append_zero_sequences_is_noop():
     assert _append(B=0, out=None, q=None, kn=None, vn=None) == 0
+
+
+def _shared(**kw):
+    a = dict(out=FAKE, q=FAKE, kn=None, vn=None, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE,
+             scale=0.125, ks=1.0, vs=1.0, bs=16, hkv=8, B=4, hq=32, d=128, mb=128, nb=1000,
+             dtype=1, fp8=0, sb=64, pt=0, ws=FAKE, wsb=1 << 30, stages=3, stream=None)
+    a.update(kw)
+    return B.load().paged_attention_decode_shared(
+        a["out"], a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["bt"], a["cl"], a["scale"],
+        a["ks"], a["vs"], a["bs"], a["hkv"], a["B"], a["hq"], a["d"], a["mb"], a["nb"],
+        a["dtype"], a["fp8"], a["sb"], a["pt"], a["ws"], a["wsb"], a["stages"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sb=-1), -3), (dict(sb=129), -3),          # outside the table
+    (dict(kn=FAKE), -1), (dict(vn=FAKE), -1),       # one of the new rows only
+    (dict(fp8=2), -2), (dict(stages=4), -3), (dict(d=96), -3),
+    (dict(wsb=16), -4), (dict(ws=None), -4),
+])
+def test_shared_rejects_before_launch(kw, code):
+    assert _shared(**kw) == code
+
+
+def test_shared_workspace_sizes():
+    """Hand-worked: the prefix workload (128 sequences, 32 q / 8 kv heads,
+    D 128, 96-entry tables, 64 shared blocks of 16).  Private tiles at most
+    128 x 32 = 4096 per KV head: 128 waves (1024 / 8), 256 slots per query
+    head; the 64 shared tiles are 2 chunks of 32, partials 32 x 128 x 2."""
+    slots = 128 + 128
+    private = 32 * slots * 128 * 4 + 32 * slots * 2 * 4 + 768  # prefix of 129 int32 -> 768 B
+    shared = 32 * 128 * 2 * 128 * 4 + 32 * 128 * 2 * 2 * 4
+    assert B.workspace_bytes_shared(128, 32, 8, 128, 96, 16, 64) == private + shared
+    # no shared blocks: the plain decode's workspace
+    assert B.workspace_bytes_shared(64, 32, 8, 128, 128, 16, 0) == \
+        B.workspace_bytes(64, 32, 8, 128, 128, 16)
+    assert B.workspace_bytes_shared(128, 32, 8, 128, 96, 16, 97) == 0
+
+
+def test_validate_shared_prefix():
+    w = W.prefix()
+    bt, cl = w.block_tables.copy(), w.context_lens.copy()
+    assert B.validate_shared_prefix(bt, cl, 16, 64) == 0
+    assert B.validate_shared_prefix(bt, cl, 16, 64, append=True) == 0
+    assert B.validate_shared_prefix(bt, cl, 16, 0) == 0
+    assert B.validate_shared_prefix(bt, cl, 16, 65) == -6   # block 64 is private
+    bt2 = bt.copy()
+    bt2[7, 13] = bt2[7, 70]
+    assert B.validate_shared_prefix(bt2, cl, 16, 64) == -6
+    cl2 = cl.copy()
+    cl2[3] = 1024
+    assert B.validate_shared_prefix(bt, cl2, 16, 64) == 0   # the prefix alone
+    assert B.validate_shared_prefix(bt, cl2, 16, 64, append=True) == -6
+    cl2[3] = 1023
+    assert B.validate_shared_prefix(bt, cl2, 16, 64) == -6
+    assert B.validate_shared_prefix(bt, cl, 16, -1) == -3
 
 
 def _noalloc(**kw):
