@@ -162,12 +162,12 @@ def cpu_model() -> str:
 
 def cpu_baseline(w, seconds: float, fp8: bool = False):
     """The fp64 oracle on the first n sequences, all heads; n grows until
-    about `seconds` of single-thread work.  The same n sequences are then run
-    again with one sequence per task on a pool of host threads (the C oracle
-    runs outside the GIL), at most 16.  Rates in KV GB/s of the same
-    accounting as the GPU figure; the pooled run is the headline figure."""
+    about `seconds` of single-thread work.  The same rows are then run again
+    shared out over a pool of host threads (the C oracle runs outside
+    Python's lock), one GPU's share of the host: at most 16 threads, fewer
+    if there are fewer rows.  Rates in KV GB/s of the same accounting as the
+    GPU figure; the pooled run is the headline figure."""
     import oracle
-    from concurrent.futures import ThreadPoolExecutor
     kc, vc = w.nan_caches_fp8() if fp8 else w.nan_caches()
     for which in ("hist", "new"):
         k, v, s = w.write_batch(which)
@@ -177,34 +177,35 @@ def cpu_baseline(w, seconds: float, fp8: bool = False):
         else:
             oracle.kv_write(k, v, s, kc, vc, w.block_size)
 
-    def one(n):
-        rows = np.array([(n, h) for h in range(w.num_heads)], dtype=np.int32)
+    def run(rows, threads):
         if fp8:
             oracle.decode_fp8_rows(rows, w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
-                                   w.block_size, w.dtype, FP8_K_SCALE, FP8_V_SCALE)
+                                   w.block_size, w.dtype, FP8_K_SCALE, FP8_V_SCALE,
+                                   threads=threads)
         else:
             oracle.decode_rows(rows, w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
-                               w.block_size, w.dtype)
+                               w.block_size, w.dtype, threads=threads)
 
     done_tokens, t_total, n = 0, 0.0, 0
     while n < w.num_seqs and t_total < seconds:
+        rows = np.array([(n, h) for h in range(w.num_heads)], dtype=np.int32)
         t0 = time.perf_counter()
-        one(n)
+        run(rows, 1)
         t_total += time.perf_counter() - t0
         done_tokens += int(w.context_lens[n])
         n += 1
-    # one GPU's share of the host: at most 16 threads, whatever the host has
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    rows = oracle.all_rows(n, w.num_heads)
+    threads = min(oracle.host_threads(), rows.shape[0])
     t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(one, range(n)))
+    run(rows, threads)
     t_pool = time.perf_counter() - t0
     kvb = done_tokens * kv_bytes_per_token(w, fp8)
     sample = (f"first {n} of {w.num_seqs} sequences, all {w.num_heads} query heads "
               f"({done_tokens} context tokens), fp64 C oracle")
     return {"value": round(kvb / t_pool / 1e9, 6), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{sample}, one sequence per task on {threads} threads, {t_pool:.2f} s",
+            "sample": f"{sample}, (sequence, head) rows shared out over {threads} threads, "
+                      f"{t_pool:.2f} s",
             "seq_tokens_per_s": round(done_tokens / t_pool, 1), "cpu": cpu_model(),
             "host_cpus": os.cpu_count(), "cpus_usable": len(os.sched_getaffinity(0)),
             "single_thread": {"value": round(kvb / t_total / 1e9, 6), "unit": "GB/s",
