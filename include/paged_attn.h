@@ -371,10 +371,15 @@ int paged_attention_decode_append_noalloc(void *out, const void *q, const void *
  * workgroup keeps its sequence's block ids on chip), else PA_ERR_SHAPE.
  * Numerics: scores and the softmax in fp32; P.V in binary16 weights times
  * binary16 V with fp32 accumulation.  With bfloat16 caches, V is converted
- * to binary16 on chip: exact for magnitudes 2^-17 .. 65504, rounded by less
- * than 2^-24 below, saturated at +-65504 above.  NaN in q, K or V gives
- * unspecified values in the rows that see it.  No workspace; out rows of
- * the chunks are the only writes.  Asynchronous on `stream`.
+ * to binary16 on chip: exact for magnitudes 2^-17 .. 65280, rounded by less
+ * than 2^-24 below.  A workgroup (64 rows of one sequence, up to 4 heads of
+ * one KV head) that meets a bfloat16 V of magnitude 65536 or more instead
+ * recomputes its rows with bfloat16 V (scaled by 2^-40 on chip, exact down
+ * to 2^-86) and the weights split into bfloat16 hi + lo parts: no finite V
+ * is clamped, at about twice that workgroup's time.  Infinite V and NaN in
+ * q, K or V give unspecified values in the rows that see them.  No
+ * workspace; out rows of the chunks are the only writes.  Asynchronous on
+ * `stream`.
  */
 int paged_attention_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
                             const int32_t *block_tables, const int32_t *context_lens,

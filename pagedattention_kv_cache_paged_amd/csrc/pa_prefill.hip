@@ -28,7 +28,8 @@
 //     MFMA wrote: the k index of both operands runs over the same eight keys
 //     per lane, so no shuffle is needed).
 // Online softmax per (head, token) with a lazily raised reference max, as in
-// decode; P.V runs in binary16 (see Elem below); the causal mask runs only
+// decode; P.V runs in binary16 (see Elem below, and the exact mode for
+// bfloat16 V beyond binary16's range); the causal mask runs only
 // on tiles that reach past a wave's first position.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -56,13 +57,14 @@ constexpr int kKT = 64;          // keys per tile
 constexpr int kRB = kKT / 16;    // 16-key row blocks per tile (QK)
 constexpr int kNH = kKT / 32;    // 32-key halves per tile (PV)
 
-// QK runs in the caches' own 16-bit type; P.V always runs in binary16: the
-// weights lie in [0, 2^8] (the reference max lags by at most kSlack), where
-// binary16 keeps 11 significant bits, and a bfloat16 V tile is converted to
-// binary16 as it is stored to LDS.  That conversion is exact for every
-// bfloat16 value of magnitude 2^-17 .. 65504 (8 significant bits fit in 11),
-// rounds smaller ones by less than 2^-24, and saturates larger ones at
-// +-65504 (round toward zero never overflows).
+// QK runs in the caches' own 16-bit type; P.V runs in binary16: the weights
+// lie in [0, 2^8] (the reference max lags by at most kSlack), where binary16
+// keeps 11 significant bits, and a bfloat16 V tile is converted to binary16
+// as it is stored to LDS.  That conversion is exact for every bfloat16 value
+// of magnitude 2^-17 .. 65280 (8 significant bits fit in 11) and rounds
+// smaller ones by less than 2^-24.  Larger ones (65536 and up) would
+// saturate: a workgroup that stages one recomputes its rows in an exact mode
+// (bfloat16 V, weights split into bfloat16 hi + lo), so no V is clamped.
 // Elem<DT>: the QK product and the output in the caches' type.
 template <int DT>
 struct Elem;
@@ -275,9 +277,20 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
       else st_v[stage][j] = Piece{lo.x, lo.y, hi.x, hi.y};
     }
   };
+  // bfloat16 V beyond binary16's range (magnitude 65536 and up: the largest
+  // bfloat16 value below it is 65280) would saturate in the conversion, so
+  // the conversion keeps the largest magnitude it met in vmax; a workgroup
+  // that met one reruns its keys in the exact mode (see below).
+  constexpr bool kCheckV = DT == 1 && !KV8;
+  float vmax = 0.f;
   // Into LDS; V of keys past the workgroup's last position is zeroed there
   // (those keys are not loaded, or lie past the context, and meet weight 0).
-  auto stash = [&](int stage, int buf, int tile) {
+  // exact (bfloat16 caches only, for the exact mode below): V stays
+  // bfloat16, scaled by 2^-40 (exact down to magnitude 2^-86), so that the
+  // fp32 accumulators of up to 2^17 keys times weights up to 2^8 stay finite
+  // for every finite bfloat16 V.
+  auto stash = [&](auto exact, int stage, int buf, int tile) {
+    constexpr bool EXACT = decltype(exact)::value;
     uint16_t *kl = lds + buf * T::elems;
     uint16_t *vl = kl + T::kElems;
 #pragma unroll
@@ -296,16 +309,25 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
         v = e4m3x8_to<0>(st_v[stage][j]);  // binary16, exact
       } else {
         v = st_v[stage][j];
-        if constexpr (DT == 1) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
-        }
       }
+      // (zeroing before or after the conversion gives the same bits)
       if (valid < 8) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int c = valid - 2 * e;
           v[e] &= c >= 2 ? 0xffffffffu : (c == 1 ? 0x0000ffffu : 0u);
+        }
+      }
+      if constexpr (kCheckV) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __uint_as_float(v[e] << 16), hi = __uint_as_float(v[e] & 0xffff0000u);
+          if constexpr (EXACT) {
+            v[e] = Elem<1>::pack(lo * 0x1p-40f, hi * 0x1p-40f);
+          } else {
+            vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
+            v[e] = bf16x2_to_f16x2(v[e]);
+          }
         }
       }
       uint16_t *vd = vl + (p % D) * T::vRow + k8;
@@ -321,6 +343,8 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
   constexpr float kSlack = 8.f;
   float m_ref[HW], l_run[HW];
   f32x4 acc[HW][DTILES];
+
+  float out_mul = out_scale;  // multiplies the normalised rows
 #pragma unroll
   for (int c = 0; c < HW; ++c) {
     m_ref[c] = -INFINITY;
@@ -332,7 +356,7 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
   // Tiles go LDS buffer (tile % 2); tile t's registers sit in stage t % kStages.
 #pragma unroll
   for (int b = 0; b < kStages - 1; ++b) fetch(b, min(b, ntiles - 1));
-  stash(0, 0, 0);
+  stash(std::false_type{}, 0, 0, 0);
   __syncthreads();
   for (int tb = 0; tb < ntiles; tb += kStages) {
 #pragma unroll
@@ -439,18 +463,111 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
           // barrier, so it can be filled now; the barrier after makes the
           // fill visible before anyone reads it (and keeps any wave from
           // refilling this buffer while another still reads it).
-          stash((b + 1) % kStages, buf ^ 1, tile + 1);
+          stash(std::false_type{}, (b + 1) % kStages, buf ^ 1, tile + 1);
           __syncthreads();
         }
       }
     }
   }
-
+  if constexpr (kCheckV) {
+    // Exact mode, for the rare workgroup that staged a bfloat16 V beyond
+    // binary16's range: the walk again from the first key, one tile at a
+    // time (no load ring: this path is short of registers, not of time).
+    // The reduction is a barrier, so every wave has left the walk above.
+    if (__syncthreads_or(vmax >= 65536.f)) {
+      out_mul = 0x1p40f;  // undoes the scaling of V
+#pragma unroll
+      for (int c = 0; c < HW; ++c) {
+        m_ref[c] = -INFINITY;
+        l_run[c] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) acc[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      for (int tile = 0; tile < ntiles; ++tile) {
+        fetch(0, tile);
+        stash(std::true_type{}, 0, 0, tile);
+        __syncthreads();
+        const int t0 = tile * kKT;
+        if (t0 <= wave_hi) {
+          const uint16_t *kl = lds;
+          const uint16_t *vl = kl + T::kElems;
+          f32x4 sc[kRB][HW];
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+            for (int c = 0; c < HW; ++c) sc[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb) {
+              const u32x4 ka = *(const u32x4 *)(kl + (rb * 16 + col) * T::kRow + ks * 32 + grp * 8);
+#pragma unroll
+              for (int c = 0; c < HW; ++c) sc[rb][c] = E::mfma(ka, qf[c][ks], sc[rb][c]);
+            }
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const bool ok = t0 + rb * 16 + grp * 4 + r <= pos;
+#pragma unroll
+              for (int c = 0; c < HW; ++c) sc[rb][c][r] = ok ? sc[rb][c][r] : -INFINITY;
+            }
+#pragma unroll
+          for (int c = 0; c < HW; ++c) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb)
+              mx = fmaxf(mx, fmaxf(fmaxf(sc[rb][c][0], sc[rb][c][1]), fmaxf(sc[rb][c][2], sc[rb][c][3])));
+            mx = rows_max(mx) * scale_log2;
+            if (__ballot(mx > m_ref[c] + kSlack)) {
+              const float m_new = fmaxf(m_ref[c], mx);
+              const float alpha = __builtin_amdgcn_exp2f(m_ref[c] - m_new);
+              l_run[c] *= alpha;
+#pragma unroll
+              for (int dt = 0; dt < DTILES; ++dt) acc[c][dt] *= alpha;
+              m_ref[c] = m_new;
+            }
+            float lsum = 0.f;
+#pragma unroll
+            for (int h = 0; h < kNH; ++h) {
+              // weights of keys 32h+4grp..+3 and 32h+16+4grp..+3 as
+              // bfloat16 hi + lo (16 significant bits)
+              float p[8];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                p[r] = __builtin_amdgcn_exp2f(fmaf(sc[2 * h][c][r], scale_log2, -m_ref[c]));
+                p[4 + r] = __builtin_amdgcn_exp2f(fmaf(sc[2 * h + 1][c][r], scale_log2, -m_ref[c]));
+              }
+              u32x4 w, lo;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                w[e] = Elem<1>::pack(p[2 * e], p[2 * e + 1]);
+                lo[e] = Elem<1>::pack(p[2 * e] - __uint_as_float(w[e] << 16),
+                                      p[2 * e + 1] - __uint_as_float(w[e] & 0xffff0000u));
+              }
+              lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+#pragma unroll
+              for (int dt = 0; dt < DTILES; ++dt) {
+                const uint16_t *vr = vl + (dt * 16 + col) * T::vRow + 32 * h + grp * 4;
+                const u32x2 a = *(const u32x2 *)vr;
+                const u32x2 b = *(const u32x2 *)(vr + 16);
+                const u32x4 va = {a.x, a.y, b.x, b.y};
+                acc[c][dt] = Elem<1>::mfma(va, w, acc[c][dt]);
+                acc[c][dt] = Elem<1>::mfma(va, lo, acc[c][dt]);
+              }
+            }
+            l_run[c] += lsum;
+          }
+        }
+        __syncthreads();  // before the next tile overwrites the buffer
+      }
+    }
+  }
   // rows of this lane: token col of the wave, heads c; lane holds dims
   // 16*dt + 4*grp + 0..3
   float inv[HW];
 #pragma unroll
-  for (int c = 0; c < HW; ++c) inv[c] = out_scale / rows_sum(l_run[c]);  // whole wave
+  for (int c = 0; c < HW; ++c) inv[c] = out_mul / rows_sum(l_run[c]);  // whole wave
   const int row = wt0 + col;
   if (row < n) {
 #pragma unroll

@@ -3,7 +3,8 @@ against oracle_prefill: |gpu - oracle| <= 2e-3 + 1e-2 * |oracle| element by
 element, on ragged batches mixing whole prompts, chunks after a cached
 prefix (prefix and chunk lengths off tile and block edges), one-row chunks
 and empty chunks, over head_dim, block size, GQA group (1 to 16) and dtype;
-and a Llama-3-8B-shaped chunk batch (sampled rows).  Rows outside the
+and a Llama-3-8B-shaped chunk batch (sampled rows); bfloat16 V beyond
+binary16's range, which takes the kernel's exact mode.  Rows outside the
 chunks are never written.  paged_attention_prefill_fp8 is held to the same
 bar against oracle_prefill_fp8 on E4M3 caches that paged_kv_write_fp8
 filled (the reading of "vLLM framework analysis: how PagedAttention speeds
@@ -39,12 +40,17 @@ def dev_bits(bits, dtype):
 
 
 def run(lengths, chunks, G, hkv, d, bs, dtype, seed, rows=None, v_scale=None, kv8=None,
-        **wkw):
-    """kv8 = (k_scale, v_scale): E4M3 caches and paged_attention_prefill_fp8."""
+        v_map=None, **wkw):
+    """kv8 = (k_scale, v_scale): E4M3 caches and paged_attention_prefill_fp8.
+    v_map: a function of the tokens' V values [N, Hkv, D] (float64) giving
+    the V values to store (rounded to the cache type)."""
     w = W.build("pf", lengths, num_heads=G * hkv, num_kv_heads=hkv, head_dim=d,
                 block_size=bs, dtype=dtype, seed=seed, **wkw)
     if v_scale is not None:  # V values times v_scale, kept inside +-65000
         v = np.clip(f64(w.token_v, dtype) * v_scale, -65000.0, 65000.0)
+        w.token_v = W.to_bits(v.astype(np.float32), dtype).reshape(w.token_v.shape)
+    if v_map is not None:
+        v = v_map(f64(w.token_v, dtype))
         w.token_v = W.to_bits(v.astype(np.float32), dtype).reshape(w.token_v.shape)
     ksh, vsh = w.cache_shapes()
     if kv8 is None:
@@ -165,6 +171,41 @@ def test_prefill_bf16_v_range(log2s):
     got, ref, _ = run([300, 77, 129], [300, 40, 1], 4, 2, 128, 16, W.BF16, 91 + log2s,
                       v_scale=s)
     check(got, ref, W.BF16, f"v x 2^{log2s}", atol=ATOL * max(s, 1.0))
+
+
+@pytest.mark.parametrize("log2s", [17, 60, 125])
+def test_prefill_bf16_v_beyond_binary16(log2s):
+    """bfloat16 V beyond binary16's range (unit-normal V times 2^17, 2^60,
+    2^125; 2^125 reaches within a factor 2 of bfloat16's largest value):
+    every workgroup stages such values and recomputes its rows in the exact
+    mode (bfloat16 V, weights as bfloat16 hi + lo), so the tolerance holds in
+    units of V's scale, where saturation at 65504 would miss by orders of
+    magnitude."""
+    s = 2.0 ** log2s
+    got, ref, _ = run([300, 77, 129], [300, 40, 1], 4, 2, 128, 16, W.BF16, 191 + log2s,
+                      v_map=lambda v: v * s)
+    check(got, ref, W.BF16, f"v x 2^{log2s}", atol=ATOL * s)
+
+
+@pytest.mark.parametrize("G,d", [(4, 128), (1, 64), (2, 128)])
+def test_prefill_bf16_v_mixed_magnitudes(G, d):
+    """Among unit-normal V, six tokens carry V of 2^100 times a unit normal's
+    magnitude.  Workgroups that stage one of them take the exact mode, also
+    for their rows that attend only to unit-scale V (those before the huge
+    token, or in another head), which must keep the absolute tolerance of
+    unit V; rows that see a huge token are dominated by it (relative
+    tolerance).  Workgroups that stage none keep the binary16 path."""
+    g = np.random.default_rng(40 + G)
+
+    def v_map(v):
+        idx = g.choice(v.shape[0], 6, replace=False)
+        v = v.copy()
+        v[idx] = np.abs(v[idx]) * 2.0 ** 100
+        return v
+
+    got, ref, _ = run([300, 150, 129, 64], [300, 100, 1, 64], G, 2, d, 16, W.BF16, 300 + G,
+                      v_map=v_map)
+    check(got, ref, W.BF16, f"mixed G={G} d={d}")
 
 
 def test_prefill_leaves_other_rows():
