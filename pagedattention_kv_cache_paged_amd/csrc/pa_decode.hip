@@ -163,16 +163,70 @@ struct Frag;
 template <int D>
 struct Frag<D, false> {
   u32x4 k[D / 32];  // one 16x16x32 A fragment per k-step
-  u32x2 v[D / 16];  // 4 tokens of one dimension per 16-dim tile
+  u32x2 v[D / 16];  // 4 tokens of one dimension per fragment (see vdim)
 };
 template <int D>
 struct Frag<D, true> {
   u32x4 k[D / 64];     // 16 codes = two k-steps
-  uint32_t v[D / 16];  // 4 token codes of one dimension per 16-dim tile
+  uint32_t v[D / 16];  // 4 token codes of one dimension per fragment (see vdim)
 };
+
+// V fragment layout.  Each lane loads 16 bytes of one 4-token group per
+// load, VG adjacent dimensions (VG = 16 / (4 tokens x element bytes): 4
+// for E4M3 codes, 2 for 16-bit values), so that the 16 lanes of a quarter
+// read one contiguous 256-byte run of the cache's [D][4] group.  V^T
+// fragment dt (one 16x16 MFMA A operand, rows i = 0..15) then holds dims
+// 16*VG*(dt/VG) + VG*i + dt%VG, and the output lanes hold 4*VG adjacent
+// dims per group of VG fragments (see vdim).
+template <bool KV8>
+struct VLayout {
+  static constexpr int VG = KV8 ? 4 : 2;
+};
+// dimension of row i of V fragment dt
+template <bool KV8>
+__device__ __forceinline__ constexpr int vdim(int dt, int i) {
+  constexpr int VG = VLayout<KV8>::VG;
+  return 16 * VG * (dt / VG) + VG * i + dt % VG;
+}
 
 // Tiles in flight per wave (register ring depth).
 constexpr int kBuf = 2;
+
+// V registers of one tile from 16-byte loads: group g (fragments VG*g ..
+// VG*g + VG-1) at element offset 64*VG*g from vp, which points at this
+// lane's first dimension (VG*row) of its 4-token group.
+template <int D, bool KV8, bool NT, typename CT>
+__device__ __forceinline__ void load_v(Frag<D, KV8> &f, const CT *vp) {
+  constexpr int VG = VLayout<KV8>::VG;
+#pragma unroll
+  for (int g = 0; g < D / 16 / VG; ++g) {
+    const u32x4 *src = (const u32x4 *)(vp + 64 * VG * g);
+    const u32x4 w = NT ? __builtin_nontemporal_load(src) : *src;
+    if constexpr (KV8) {
+      f.v[4 * g] = w.x; f.v[4 * g + 1] = w.y; f.v[4 * g + 2] = w.z; f.v[4 * g + 3] = w.w;
+    } else {
+      f.v[2 * g] = u32x2{w.x, w.y}; f.v[2 * g + 1] = u32x2{w.z, w.w};
+    }
+  }
+}
+
+// One (sequence, head) row of results, scaled: acc[dt][r] holds the
+// fragment layout's dim vdim(dt, 4*grp + r); lane (., grp) writes its 4*VG
+// adjacent dims of each group g, at 16*VG*g + 4*VG*grp.
+template <int D, bool KV8, typename F>
+__device__ __forceinline__ void row_values(const f32x4 (&acc)[D / 16], int g, F &&emit) {
+  constexpr int VG = VLayout<KV8>::VG;
+#pragma unroll
+  for (int c = 0; c < VG; ++c) {  // f32x4 chunk c: elements 4c .. 4c+3
+    f32x4 v;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int e = 4 * c + t;  // element e = VG*r + j
+      v[t] = acc[VG * g + e % VG][e / VG];
+    }
+    emit(c, v);
+  }
+}
 
 // Lazy rescale slack (log2 units): the reference max is raised only when a
 // tile's max exceeds it by more than this.
@@ -253,32 +307,30 @@ __device__ __forceinline__ void shared_prefix_wave(
   const CT *kbase = static_cast<const CT *>(k_cache) + (int64_t)kvh * BS * D;
   const CT *vbase = static_cast<const CT *>(v_cache) + (int64_t)kvh * D * BS;
   // Loads of one full tile: lane (row, grp) reads token row's K dims and the
-  // four tokens 4 * grp .. +3 of V dimension row (+16 per fragment).
+  // four tokens 4 * grp .. +3 of V dimensions vdim(dt, row).
   auto load = [&](Frag<D, KV8> &f, int idx) {
     const int ka = __builtin_amdgcn_readlane(b0, idx);
     const CT *kp, *vp;
     if constexpr (BS == 8) {
       const int kz = __builtin_amdgcn_readlane(b1, idx);
       kp = kbase + (int64_t)(row < 8 ? ka : kz) * blk_stride + (row & 7) * D + grp * (KV8 ? 16 : 8);
-      vp = vbase + (int64_t)(grp < 2 ? ka : kz) * blk_stride + ((grp & 1) * D + row) * 4;
+      vp = vbase + (int64_t)(grp < 2 ? ka : kz) * blk_stride +
+           ((grp & 1) * D + VLayout<KV8>::VG * row) * 4;
     } else {
       const int o = BS == 16 ? 0 : __builtin_amdgcn_readlane(boff, idx);
       const CT *kblk = kbase + (int64_t)ka * blk_stride + o * D;
       const CT *vblk = vbase + (int64_t)ka * blk_stride;
       kp = kblk + (uint32_t)(row * D + grp * (KV8 ? 16 : 8));
-      vp = vblk + (uint32_t)((((o >> 2) + grp) * D + row) * 4);
+      vp = vblk + (uint32_t)((((o >> 2) + grp) * D + VLayout<KV8>::VG * row) * 4);
     }
     if constexpr (KV8) {
 #pragma unroll
       for (int h = 0; h < D / 64; ++h) f.k[h] = *(const u32x4 *)(kp + h * 64);
-#pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt) f.v[dt] = *(const uint32_t *)(vp + dt * 64);
     } else {
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) f.k[ks] = *(const u32x4 *)(kp + ks * 32);
-#pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt) f.v[dt] = *(const u32x2 *)(vp + dt * 64);
     }
+    load_v<D, KV8, false>(f, vp);
   };
 
   float m_ref[NG], l_run[NG];
@@ -364,16 +416,20 @@ __device__ __forceinline__ void shared_prefix_wave(
   }
 
   // The chunk's partial of each (sequence, query head): lane (row, grp)
-  // holds dims 16 * dt + 4 * grp + 0..3 of column row.
+  // holds dims vdim(dt, 4 * grp + 0..3) of column row.
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     const float l_tot = rows_sum(l_run[gi]);
     if (valid[gi]) {
       const int64_t slot = ((int64_t)head[gi] * num_seqs + seq[gi]) * sh.chunks + ch;
       const float inv = out_scale / l_tot;
-      float *op = sh.o + slot * D + grp * 4;
+      constexpr int VG = VLayout<KV8>::VG;
+      float *op = sh.o + slot * D + grp * 4 * VG;
 #pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt) *(f32x4 *)(op + dt * 16) = acc[gi][dt] * inv;
+      for (int g = 0; g < DTILES / VG; ++g)
+        row_values<D, KV8>(acc[gi], g, [&](int c, f32x4 v) {
+          *(f32x4 *)(op + 16 * VG * g + 4 * c) = v * inv;
+        });
       if (grp == 0) *(f32x2 *)(sh.ml + slot * 2) = f32x2{m_ref[gi], l_tot};
     }
   }
@@ -597,30 +653,26 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
     if constexpr (BS == 8) {  // the tile's two blocks: per-lane choice
       const int kz = __builtin_amdgcn_readlane(b1, idx);
       kp = kbase + (int64_t)(ktok < 8 ? ka : kz) * blk_stride + (ktok & 7) * D + grp * (KV8 ? 16 : 8);
-      vp = vbase + (int64_t)(vtok < 8 ? ka : kz) * blk_stride + (((vtok & 7) >> 2) * D + row) * 4;
+      vp = vbase + (int64_t)(vtok < 8 ? ka : kz) * blk_stride +
+           (((vtok & 7) >> 2) * D + VLayout<KV8>::VG * row) * 4;
     } else {
       // block base in scalar registers, 32-bit lane offsets
       const int o = BS == 16 ? 0 : __builtin_amdgcn_readlane(boff, idx);
       const CT *kblk = kbase + (int64_t)ka * blk_stride + o * D;
       const CT *vblk = vbase + (int64_t)ka * blk_stride;
       kp = kblk + (uint32_t)(ktok * D + grp * (KV8 ? 16 : 8));
-      vp = vblk + (uint32_t)((((o + vtok) >> 2) * D + row) * 4);
+      vp = vblk + (uint32_t)((((o + vtok) >> 2) * D + VLayout<KV8>::VG * row) * 4);
     }
     if constexpr (KV8) {
 #pragma unroll
       for (int h = 0; h < D / 64; ++h)
         f.k[h] = __builtin_nontemporal_load((const u32x4 *)(kp + h * 64));
-#pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt)
-        f.v[dt] = __builtin_nontemporal_load((const uint32_t *)(vp + dt * 64));
     } else {
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks)
         f.k[ks] = __builtin_nontemporal_load((const u32x4 *)(kp + ks * 32));
-#pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt)
-        f.v[dt] = __builtin_nontemporal_load((const u32x2 *)(vp + dt * 64));
     }
+    load_v<D, KV8, true>(f, vp);
   };
 
   // Reference max per head in log2 units, reset at each sequence segment.
@@ -667,7 +719,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
       if (grp == (r >> 2)) {
 #pragma unroll
         for (int dt = 0; dt < DTILES; ++dt) {
-          const uint32_t x = vn_lds[dt * 16 + row];
+          const uint32_t x = vn_lds[vdim<KV8>(dt, row)];
           if constexpr (KV8) {
             f.v[dt] = (f.v[dt] & ~(0xffu << (8 * e))) | (x << (8 * e));
           } else if (e >> 1) {
@@ -695,11 +747,14 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
         }
         if (grp == (r >> 2)) {
           const int g4 = ((BS == 8 ? (grp * 4) & 7 : bo + grp * 4) >> 2);  // group in the block
+          constexpr int VG = VLayout<KV8>::VG;
 #pragma unroll
-          for (int dt = 0; dt < DTILES; ++dt) {
-            CT *vp = vd + (g4 * D + dt * 16 + row) * 4;
-            if constexpr (KV8) *(uint32_t *)vp = f.v[dt];
-            else *(u32x2 *)vp = f.v[dt];
+          for (int g = 0; g < DTILES / VG; ++g) {
+            CT *vp = vd + (g4 * D + 16 * VG * g + VG * row) * 4;
+            if constexpr (KV8)
+              *(u32x4 *)vp = u32x4{f.v[4 * g], f.v[4 * g + 1], f.v[4 * g + 2], f.v[4 * g + 3]};
+            else
+              *(u32x4 *)vp = u32x4{f.v[2 * g].x, f.v[2 * g].y, f.v[2 * g + 1].x, f.v[2 * g + 1].y};
           }
         }
       }
@@ -780,21 +835,24 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
       if (row < group) {
         const int head = kvh * group + row;
         const float inv = out_scale / l_tot;
+        constexpr int VG = VLayout<KV8>::VG;
         if (mt & kWhole) {
-          // lane (row, grp) holds dims 16*dt + 4*grp + 0..3 of head row
-          uint16_t *op = out + ((int64_t)sqn * num_heads + head) * D + grp * 4;
+          // lane (row, grp) holds dims 16*VG*g + 4*VG*grp .. +4*VG of head row
+          uint16_t *op = out + ((int64_t)sqn * num_heads + head) * D + grp * 4 * VG;
 #pragma unroll
-          for (int dt = 0; dt < DTILES; ++dt) {
-            u32x2 w;
-            w.x = E::pack(acc[dt][0] * inv, acc[dt][1] * inv);
-            w.y = E::pack(acc[dt][2] * inv, acc[dt][3] * inv);
-            *(u32x2 *)(op + dt * 16) = w;
-          }
+          for (int g = 0; g < DTILES / VG; ++g)
+            row_values<D, KV8>(acc, g, [&](int c, f32x4 v) {
+              const u32x2 w = {E::pack(v[0] * inv, v[1] * inv), E::pack(v[2] * inv, v[3] * inv)};
+              *(u32x2 *)(op + 16 * VG * g + 4 * c) = w;
+            });
         } else {
           const int64_t slot = (int64_t)head * slots + j + sqn;
-          float *op = ws_o + slot * D + grp * 4;
+          float *op = ws_o + slot * D + grp * 4 * VG;
 #pragma unroll
-          for (int dt = 0; dt < DTILES; ++dt) *(f32x4 *)(op + dt * 16) = acc[dt] * inv;
+          for (int g = 0; g < DTILES / VG; ++g)
+            row_values<D, KV8>(acc, g, [&](int c, f32x4 v) {
+              *(f32x4 *)(op + 16 * VG * g + 4 * c) = v * inv;
+            });
           if (grp == 0) *(f32x2 *)(ws_ml + slot * 2) = f32x2{m_ref, l_tot};
         }
       }

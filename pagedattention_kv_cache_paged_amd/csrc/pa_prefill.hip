@@ -206,8 +206,10 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
   const int pos = first_pos + tok;                    // its context position
   const int wave_lo = first_pos + min(wt0, n - 1);    // wave's first / last positions
   const int wave_hi = first_pos + min(wt0 + kQT - 1, n - 1);
-  const int wg_hi = first_pos + min(qb * kQB + kQB - 1, n - 1);
-  const int ntiles = wg_hi / kKT + 1;                 // keys 0 .. wg_hi
+  // (workgroup-uniform: read back as scalars, so the address and mask
+  // arithmetic built on them stays on the scalar unit)
+  const int wg_hi = __builtin_amdgcn_readfirstlane(first_pos + min(qb * kQB + kQB - 1, n - 1));
+  const int ntiles = __builtin_amdgcn_readfirstlane(wg_hi / kKT + 1);  // keys 0 .. wg_hi
   const int32_t *tbl = block_tables + (int64_t)seq * max_blocks;
   const int nent = (wg_hi >> log2_bs) + 1;  // table entries of keys 0 .. wg_hi
   for (int i = tid; i < nent; i += kThreads) {
@@ -258,7 +260,8 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
       const int pw = min(wv * kWave + j * kThreads, PIECES - kWave);  // first piece (uniform)
       // the load's keys; past the rows' reach it rereads the group of the
       // last key seen (same block, in bounds)
-      const int key0 = min(tile * kKT + pw / KPR, wg_hi & ~(KPL - 1));
+      const int key0 =
+          __builtin_amdgcn_readfirstlane(min(tile * kKT + pw / KPR, wg_hi & ~(KPL - 1)));
       const int blk = __builtin_amdgcn_readfirstlane(tbl_lds[key0 >> log2_bs]);
       const char *src = kbase + blk * blk_bytes + (int64_t)((key0 & (bs - 1)) * D * EB);
       st_k[stage][j] = __builtin_nontemporal_load((const Piece *)(src + koff));
@@ -266,7 +269,8 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       const int pw = min(wv * kWave + j * kThreads, PIECES - kWave);
-      const int key0 = min(tile * kKT + (pw / D) * 8, wg_hi & ~7);  // the load's key octet
+      // the load's key octet
+      const int key0 = __builtin_amdgcn_readfirstlane(min(tile * kKT + (pw / D) * 8, wg_hi & ~7));
       const int blk = __builtin_amdgcn_readfirstlane(tbl_lds[key0 >> log2_bs]);
       const char *src = vbase + blk * blk_bytes +
                         (int64_t)((((key0 & (bs - 1)) >> 2) * D + pw % D) * 4 * EB) + voff;
@@ -303,7 +307,8 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
       else kv = st_k[stage][j];
       *(u32x4 *)(kl + (p / KPR) * T::kRow + (p % KPR) * 8) = kv;
       const int k8 = (pw / D) * 8;
-      const int valid = wg_hi + 1 - (tile * kKT + k8);  // keys the rows can see
+      // keys the rows can see
+      const int valid = __builtin_amdgcn_readfirstlane(wg_hi + 1 - (tile * kKT + k8));
       u32x4 v;
       if constexpr (KV8) {
         v = e4m3x8_to<0>(st_v[stage][j]);  // binary16, exact
