@@ -731,8 +731,8 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
       }
       // Store the token: its K row, and its V as part of its whole 4-token
       // group (the lanes of quarter r / 4 hold that group's [D][4] run, the
-      // other three positions with the bytes they held), so the V store
-      // writes whole cache lines rather than a few bytes of each.
+      // other three positions with the bytes they held), so that both
+      // stores write whole cache lines rather than a few bytes of each.
       const int nb = __builtin_amdgcn_readlane(nblk, idx);
       if (nb >= 0) {
         const int bo = BS == 32 ? __builtin_amdgcn_readlane(boff, idx) : 0;
@@ -740,11 +740,11 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
         const int64_t bh = (int64_t)nb * num_kv_heads + kvh;
         CT *kd = static_cast<CT *>(k_cache) + (bh * BS + off) * D;
         CT *vd = static_cast<CT *>(v_cache) + bh * D * BS;
-        if (row == r) {
-#pragma unroll
-          for (int h = 0; h < (KV8 ? D / 64 : KSTEPS); ++h)
-            *(u32x4 *)(kd + (KV8 ? 64 * h + 16 * grp : 32 * h + 8 * grp)) = f.k[h];
-        }
+        // the K row from LDS, where it sits in dimension order: 16 bytes per
+        // lane, so that one store instruction writes the whole row
+        constexpr int KL = D * (int)sizeof(CT) / 16;  // lanes that store
+        if (lane < KL) *(u32x4 *)(kd + lane * (16 / (int)sizeof(CT))) =
+            *(const u32x4 *)(kn_lds + lane * (16 / (int)sizeof(CT)));
         if (grp == (r >> 2)) {
           const int g4 = ((BS == 8 ? (grp * 4) & 7 : bo + grp * 4) >> 2);  // group in the block
           constexpr int VG = VLayout<KV8>::VG;
