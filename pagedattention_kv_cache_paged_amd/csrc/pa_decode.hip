@@ -253,6 +253,9 @@ __device__ __forceinline__ void shared_prefix_wave(
     const int32_t *__restrict__ block_tables, float scale_log2, float out_scale,
     int num_seqs, int num_kv_heads, int num_heads, int group, int64_t num_blocks) {
   using E = Elem<DT>;
+  // P.V over E4M3 caches in binary16 (every code value is one; weights
+  // keep 11 significant bits), otherwise in the caches' type
+  using PE = std::conditional_t<KV8, Elem<kF16>, E>;
   using CT = std::conditional_t<KV8, uint8_t, uint16_t>;
   constexpr int KSTEPS = D / 32;
   constexpr int DTILES = D / 16;
@@ -360,7 +363,7 @@ __device__ __forceinline__ void shared_prefix_wave(
     }
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) {
-      if constexpr (KV8) vv[dt] = E::from_e4m3(f.v[dt]);
+      if constexpr (KV8) vv[dt] = PE::from_e4m3(f.v[dt]);
       else vv[dt] = f.v[dt];
     }
 #pragma unroll
@@ -384,19 +387,19 @@ __device__ __forceinline__ void shared_prefix_wave(
 #pragma unroll
       for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sv[r] - m_ref[gi]);
       u32x2 ph, pl;
-      ph.x = E::pack(p[0], p[1]);
-      ph.y = E::pack(p[2], p[3]);
-      if constexpr (E::kSplitP) {
-        pl.x = E::pack(p[0] - E::lo(ph.x), p[1] - E::hi(ph.x));
-        pl.y = E::pack(p[2] - E::lo(ph.y), p[3] - E::hi(ph.y));
+      ph.x = PE::pack(p[0], p[1]);
+      ph.y = PE::pack(p[2], p[3]);
+      if constexpr (PE::kSplitP) {
+        pl.x = PE::pack(p[0] - PE::lo(ph.x), p[1] - PE::hi(ph.x));
+        pl.y = PE::pack(p[2] - PE::lo(ph.y), p[3] - PE::hi(ph.y));
         l_run[gi] += (p[0] + p[1]) + (p[2] + p[3]);
       } else {
-        l_run[gi] += (E::lo(ph.x) + E::hi(ph.x)) + (E::lo(ph.y) + E::hi(ph.y));
+        l_run[gi] += (PE::lo(ph.x) + PE::hi(ph.x)) + (PE::lo(ph.y) + PE::hi(ph.y));
       }
 #pragma unroll
       for (int dt = 0; dt < DTILES; ++dt) {
-        acc[gi][dt] = E::pv(vv[dt], ph, acc[gi][dt]);
-        if constexpr (E::kSplitP) acc[gi][dt] = E::pv(vv[dt], pl, acc[gi][dt]);
+        acc[gi][dt] = PE::pv(vv[dt], ph, acc[gi][dt]);
+        if constexpr (PE::kSplitP) acc[gi][dt] = PE::pv(vv[dt], pl, acc[gi][dt]);
       }
     }
   };
@@ -453,6 +456,9 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
     int num_kv_heads, int num_heads, int group, int max_blocks, int64_t num_blocks,
     int waves, int slots, SharedPrefix sh) {
   using E = Elem<DT>;
+  // P.V over E4M3 caches in binary16 (every code value is one; weights
+  // keep 11 significant bits), otherwise in the caches' type
+  using PE = std::conditional_t<KV8, Elem<kF16>, E>;
   using CT = std::conditional_t<KV8, uint8_t, uint16_t>;  // cache element
   constexpr int KSTEPS = D / 32;  // 16x16x32 MFMAs per QK tile
   constexpr int DTILES = D / 16;  // 16x16x16 MFMAs per PV tile
@@ -810,24 +816,24 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(s[r] - m_ref);
     u32x2 ph, pl;
-    ph.x = E::pack(p[0], p[1]);
-    ph.y = E::pack(p[2], p[3]);
-    if constexpr (E::kSplitP) {
+    ph.x = PE::pack(p[0], p[1]);
+    ph.y = PE::pack(p[2], p[3]);
+    if constexpr (PE::kSplitP) {
       // residuals are exact in fp32; the sum is taken over the full weights
-      pl.x = E::pack(p[0] - E::lo(ph.x), p[1] - E::hi(ph.x));
-      pl.y = E::pack(p[2] - E::lo(ph.y), p[3] - E::hi(ph.y));
+      pl.x = PE::pack(p[0] - PE::lo(ph.x), p[1] - PE::hi(ph.x));
+      pl.y = PE::pack(p[2] - PE::lo(ph.y), p[3] - PE::hi(ph.y));
       l_run += (p[0] + p[1]) + (p[2] + p[3]);
     } else {
       // the sum uses the rounded weights the MFMA multiplies with
-      l_run += (E::lo(ph.x) + E::hi(ph.x)) + (E::lo(ph.y) + E::hi(ph.y));
+      l_run += (PE::lo(ph.x) + PE::hi(ph.x)) + (PE::lo(ph.y) + PE::hi(ph.y));
     }
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) {
       u32x2 vv;
-      if constexpr (KV8) vv = E::from_e4m3(f.v[dt]);
+      if constexpr (KV8) vv = PE::from_e4m3(f.v[dt]);
       else vv = f.v[dt];
-      acc[dt] = E::pv(vv, ph, acc[dt]);
-      if constexpr (E::kSplitP) acc[dt] = E::pv(vv, pl, acc[dt]);
+      acc[dt] = PE::pv(vv, ph, acc[dt]);
+      if constexpr (PE::kSplitP) acc[dt] = PE::pv(vv, pl, acc[dt]);
     }
     if (mt & kEnd) {
       const float l_tot = rows_sum(l_run);
