@@ -350,9 +350,12 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
   f32x4 acc[HW][DTILES];
 
   float out_mul = out_scale;  // multiplies the normalised rows
+  float thr[HW];  // m_ref + kSlack in units of raw scores
+  const float inv_scale = 1.0f / scale_log2;
 #pragma unroll
   for (int c = 0; c < HW; ++c) {
     m_ref[c] = -INFINITY;
+    thr[c] = -INFINITY;
     l_run[c] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) acc[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -417,18 +420,23 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
           u32x4 pb[kNH][HW];
     #pragma unroll
           for (int c = 0; c < HW; ++c) {
-            float mx = -INFINITY;
+            // The reference max moves only when a score passes m_ref + kSlack:
+            // each lane checks its own 16 raw scores against that bound (thr,
+            // in raw units), and only then is the row max reduced over the
+            // row's four lanes (a row whose keys all lie past it gives -inf).
+            float lm = -INFINITY;
     #pragma unroll
             for (int rb = 0; rb < kRB; ++rb)
-              mx = fmaxf(mx, fmaxf(fmaxf(sc[rb][c][0], sc[rb][c][1]), fmaxf(sc[rb][c][2], sc[rb][c][3])));
-            mx = rows_max(mx) * scale_log2;  // a row whose keys all lie past it gives -inf
-            if (__ballot(mx > m_ref[c] + kSlack)) {
+              lm = fmaxf(lm, fmaxf(fmaxf(sc[rb][c][0], sc[rb][c][1]), fmaxf(sc[rb][c][2], sc[rb][c][3])));
+            if (__ballot(lm > thr[c])) {
+              const float mx = rows_max(lm) * scale_log2;
               const float m_new = fmaxf(m_ref[c], mx);
               const float alpha = __builtin_amdgcn_exp2f(m_ref[c] - m_new);
               l_run[c] *= alpha;
     #pragma unroll
               for (int dt = 0; dt < DTILES; ++dt) acc[c][dt] *= alpha;
               m_ref[c] = m_new;
+              thr[c] = (m_new + kSlack) * inv_scale;
             }
             float lsum = 0.f;
     #pragma unroll
