@@ -337,10 +337,13 @@ __device__ __forceinline__ void shared_prefix_wave(
   };
 
   float m_ref[NG], l_run[NG];
+  float thr[NG];  // m_ref + kSlack in units of raw scores
+  const float inv_scale = 1.0f / scale_log2;
   f32x4 acc[NG][DTILES];
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     m_ref[gi] = -INFINITY;
+    thr[gi] = -INFINITY;
     l_run[gi] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) acc[gi][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -371,21 +374,22 @@ __device__ __forceinline__ void shared_prefix_wave(
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) sc = E::qk(kf[ks], qf[gi][ks], sc);
-      float sv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = sc[r] * scale_log2;
-      const float mx = rows_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
-      if (__ballot(mx > m_ref[gi] + kSlack)) {
+      // raw scores, checked lane by lane against thr before any reduction
+      // (as in the split pass); the scale joins in the exponent's FMA
+      const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      if (__ballot(lm > thr[gi])) {
+        const float mx = rows_max(lm) * scale_log2;
         const float m_new = fmaxf(m_ref[gi], mx);
         const float alpha = __builtin_amdgcn_exp2f(m_ref[gi] - m_new);
         l_run[gi] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DTILES; ++dt) acc[gi][dt] *= alpha;
         m_ref[gi] = m_new;
+        thr[gi] = (m_new + kSlack) * inv_scale;
       }
       float p[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sv[r] - m_ref[gi]);
+      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -m_ref[gi]));
       u32x2 ph, pl;
       ph.x = PE::pack(p[0], p[1]);
       ph.y = PE::pack(p[2], p[3]);
@@ -687,6 +691,8 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // 2^(s - m_ref) then stay below 2^kSlack, far inside fp32 and bfloat16
   // range.  The softmax is the same for any reference.
   float m_ref = -INFINITY;
+  float thr = -INFINITY;  // m_ref + kSlack in units of raw scores
+  const float inv_scale = 1.0f / scale_log2;
   float l_run = 0.f;  // this lane's share of the running sum
   f32x4 acc[DTILES];
 #pragma unroll
@@ -782,9 +788,10 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
       }
       sc = E::qk(kf, qf[ks], sc);
     }
+    // raw scores; the scale (> 0, log2 units) joins in the exponent's FMA
     float s[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = sc[r] * scale_log2;
+    for (int r = 0; r < 4; ++r) s[r] = sc[r];
     if (n < kTile) {
       const int c = n - grp * 4;  // valid tokens among this lane's four
 #pragma unroll
@@ -803,18 +810,23 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
         }
       }
     }
-    const float mx = rows_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
-    if (__ballot(mx > m_ref + kSlack)) {  // always on a segment's first tile
+    // The reference moves only when a score passes m_ref + kSlack: each
+    // lane checks its own four raw scores against that bound (thr, in raw
+    // units), and only then is the max reduced over the column's lanes.
+    const float lm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    if (__ballot(lm > thr)) {  // always on a segment's first tile
+      const float mx = rows_max(lm) * scale_log2;
       const float m_new = fmaxf(m_ref, mx);  // finite: every tile has a valid token
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DTILES; ++dt) acc[dt] *= alpha;
       m_ref = m_new;
+      thr = (m_new + kSlack) * inv_scale;
     }
     float p[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(s[r] - m_ref);
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m_ref));
     u32x2 ph, pl;
     ph.x = PE::pack(p[0], p[1]);
     ph.y = PE::pack(p[2], p[3]);
@@ -863,6 +875,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
         }
       }
       m_ref = -INFINITY;
+      thr = -INFINITY;
       l_run = 0.f;
 #pragma unroll
       for (int dt = 0; dt < DTILES; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
