@@ -200,9 +200,11 @@ int paged_kv_write_fp8(const void *k, const void *v, const int64_t *slot_mapping
 
 /*
  * paged_attention_decode_stages over E4M3 caches: the same attention with
- * K_t = code * k_scale and V_t = code * v_scale.  The codes are converted to
- * the q type exactly in registers; k_scale joins the score scale and v_scale
- * the output.  Workspace as for the 16-bit caches.
+ * K_t = code * k_scale and V_t = code * v_scale.  The codes are converted
+ * exactly in registers, K to the q type and V to binary16; P.V then runs
+ * with binary16 weights (11 significant bits) whatever the q type.  k_scale
+ * joins the score scale and v_scale the output.  Workspace as for the
+ * 16-bit caches.
  */
 int paged_attention_decode_fp8(void *out, const void *q, const void *k_cache,
                                const void *v_cache, const int32_t *block_tables,

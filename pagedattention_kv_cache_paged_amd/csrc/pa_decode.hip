@@ -27,13 +27,16 @@
 //   O^T[D x 16 head]     += V^T[D x 16 tok] * P^T[16 tok x 16 head]
 //        -> D/16 MFMA 16x16x16; A = V^T read straight from the V cache,
 //           whose (block, head) slice is block_size/4 groups of [D][4]
-//           (8 contiguous bytes = 4 tokens of one dim per lane),
+//           (4 tokens of one dim adjacent; each lane loads 16 bytes, the
+//           4 tokens of VG adjacent dims, see VLayout),
 //           B = P exactly as the QK MFMA left it in registers (lane l holds
 //           head l%16, tokens 4*(l/16)+0..3), so no shuffle is needed.
-//           For bfloat16, P goes in as a hi and a lo bfloat16 part (two
-//           MFMAs) so the weights keep ~16 significant bits.
+//           For bfloat16 caches, P goes in as a hi and a lo bfloat16 part
+//           (two MFMAs) so the weights keep ~16 significant bits; over
+//           binary16 and E4M3 caches it is one binary16 MFMA.
 // Every lane's softmax state and accumulators belong to head l%16, so the
-// rescale by exp(m_old - m_new) is lane-local; only the tile max and the
+// rescale by exp(m_old - m_new) is lane-local; only the tile max (when a
+// lane's own scores pass the current reference by the slack) and the
 // final sum cross the wave's four 16-lane rows (permlane16/32 swaps).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -688,8 +691,9 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // Reference max per head in log2 units, reset at each sequence segment.
   // It is raised only when a tile's max exceeds it by more than kSlack, so
   // most tiles skip the rescale of the accumulators; the weights
-  // 2^(s - m_ref) then stay below 2^kSlack, far inside fp32 and bfloat16
-  // range.  The softmax is the same for any reference.
+  // 2^(s - m_ref) then stay below 2^kSlack, far inside the range of every
+  // weight type (bfloat16, binary16).  The softmax is the same for any
+  // reference.
   float m_ref = -INFINITY;
   float thr = -INFINITY;  // m_ref + kSlack in units of raw scores
   const float inv_scale = 1.0f / scale_log2;

@@ -380,7 +380,8 @@ __global__ __launch_bounds__(kWave * kTG * NWH) void prefill_kernel(
           const uint16_t *kl = lds + buf * T::elems;
           const uint16_t *vl = kl + T::kElems;
           // raw scores q.k: kRB 16-key row blocks x HW heads; the scale (> 0,
-          // in log2 units) joins in the exponent's FMA and on the tile max
+          // in log2 units) joins in the exponent's FMA (the max check below
+          // runs on raw scores)
           // k-step outer: the four row blocks' fragments of one k-step are
           // read together, then feed kRB * HW independent accumulations, so
           // no MFMA waits on the one before it or on a read just issued.
