@@ -23,7 +23,8 @@
 // Per 16-token tile, with G <= 16 query heads padded to 16:
 //   S^T[16 tok x 16 head] = K[16 tok x D] * Q^T[D x 16 head]
 //        -> D/32 MFMA 16x16x32; A = K rows as stored (token-major cache),
-//           each lane loading 16 contiguous bytes of one token's row.
+//           each lane loading 16 contiguous bytes of one token's row (E4M3
+//           at D = 128: loaded as whole lines and rearranged through LDS).
 //   O^T[D x 16 head]     += V^T[D x 16 tok] * P^T[16 tok x 16 head]
 //        -> D/16 MFMA 16x16x16; A = V^T read straight from the V cache,
 //           whose (block, head) slice is block_size/4 groups of [D][4]
@@ -482,6 +483,11 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   uint16_t *vn_raw = kn_raw + D;
   CT *kn_lds = KV8 ? reinterpret_cast<CT *>(vn_raw + D) : reinterpret_cast<CT *>(kn_raw);
   CT *vn_lds = KV8 ? kn_lds + D : reinterpret_cast<CT *>(vn_raw);
+  // E4M3 at D = 128: one tile's K codes, 16 token rows of 144 bytes (128
+  // + 16 of padding, so that the fragment reads spread over the banks)
+  constexpr bool kKT = KV8 && D == 128;
+  constexpr int kKTRow = 144;
+  uint8_t *kt_lds = reinterpret_cast<uint8_t *>(q_lds + KSTEPS * kWave) + (APPEND ? 6 * D : 0);
 
   int bid = blockIdx.x;
   if constexpr (SHARED) {
@@ -676,7 +682,23 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
       kp = kblk + (uint32_t)(ktok * D + grp * (KV8 ? 16 : 8));
       vp = vblk + (uint32_t)((((o + vtok) >> 2) * D + VLayout<KV8>::VG * row) * 4);
     }
-    if constexpr (KV8) {
+    if constexpr (kKT) {
+      // whole lines: load h reads tokens 8h .. 8h+7, lane l 16 codes of
+      // token 8h + l/8 (clamped to the valid ones) at 16 * (l % 8)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = min(8 * h + (lane >> 3), n - 1);
+        const CT *src;
+        if constexpr (BS == 8) {
+          const int kz = __builtin_amdgcn_readlane(b1, idx);
+          src = kbase + (int64_t)(t < 8 ? ka : kz) * blk_stride + (t & 7) * D + (lane & 7) * 16;
+        } else {
+          const int o = BS == 16 ? 0 : __builtin_amdgcn_readlane(boff, idx);
+          src = kbase + (int64_t)ka * blk_stride + o * D + (uint32_t)(t * D + (lane & 7) * 16);
+        }
+        f.k[h] = __builtin_nontemporal_load((const u32x4 *)src);
+      }
+    } else if constexpr (KV8) {
 #pragma unroll
       for (int h = 0; h < D / 64; ++h)
         f.k[h] = __builtin_nontemporal_load((const u32x4 *)(kp + h * 64));
@@ -710,6 +732,14 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   auto step = [&](Frag<D, KV8> &f, int idx) {
     const int mt = __builtin_amdgcn_readlane(meta, idx);
     const int n = mt & 31;
+    if constexpr (kKT) {  // K as loaded -> LDS -> the MFMA layout (token row, codes 64h + 16grp)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *(u32x4 *)(kt_lds + (8 * h + (lane >> 3)) * kKTRow + (lane & 7) * 16) = f.k[h];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        f.k[h] = *(const u32x4 *)(kt_lds + row * kKTRow + (4 * h + grp) * 16);
+    }
     if (APPEND && (mt & kNew)) {
       // The new token (row r of the tile) comes from k_new / v_new, not
       // from its cache slot, which this wavefront now fills.  Lanes of A-row
@@ -1009,7 +1039,8 @@ int launch_typed(const DecodeArgs &a) {
     // LDS: tile prefix and lengths, query fragments, and for the fused
     // append the new rows (16-bit, plus E4M3 codes).
     const size_t lds = (size_t)((2 * a.num_seqs + 1 + 3) & ~3) * sizeof(int) +
-                       (size_t)(D / 32) * kWave * 16 + (a.append ? 6 * D : 0);
+                       (size_t)(D / 32) * kWave * 16 + (a.append ? 6 * D : 0) +
+                       (a.kv_fp8 && D == 128 ? 16 * 144 : 0);
 #define PA_SPLIT(KV8, APPEND, SHARED, OUT_SCALE)                                               \
   decode_split_kernel<DT, D, BS, KV8, APPEND, SHARED><<<grid, kWave, lds, st>>>(               \
       (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, (const uint16_t *)a.q, (void *)a.k_cache,  \
