@@ -20,7 +20,9 @@
  * Every call validates its arguments on the host before launching anything;
  * on error nothing is enqueued and no memory is touched.  A return of PA_OK
  * means the work was enqueued on `stream` (the calls are asynchronous).
- * The library holds no state and may be called from several threads.
+ * The library may be called from several threads.  Its only state is the
+ * fixed per-GPU scratch array of paged_attention_decode_append_noalloc and
+ * that array's device address, looked up once per device under a lock.
  *
  * Element type: q, k, v, both caches and out share one 16-bit type, IEEE
  * binary16 (PA_F16) or bfloat16 (PA_BF16); arithmetic is fp32.
