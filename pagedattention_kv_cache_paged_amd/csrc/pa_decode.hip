@@ -143,14 +143,18 @@ __device__ __forceinline__ float rows_sum(float x) {
 
 
 
-// Inclusive prefix sum over the wave's 64 lanes.
+// Inclusive prefix sum over the wave's 64 lanes, by DPP: shifts by 1, 2, 4
+// and 8 within each row of 16 lanes (sources outside the row read 0), then
+// row 0's total joins row 1 and row 2's joins row 3 (broadcast of lanes 15
+// and 47), then lane 31's (rows 0-1) joins rows 2 and 3.  Rows that a
+// broadcast does not enable keep their value.  No LDS round trips.
 __device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
 }
 
@@ -514,26 +518,43 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // With a fused append the last position L - 1 is the new token: the
   // wavefront holding that tile takes its K and V from k_new / v_new
   // instead of the cache and stores them into the cache slot.
+  // The lengths of kScanChunks chunks of 64 sequences are loaded together,
+  // so that they cost one round trip, and their scans are independent until
+  // the chunks' totals are added in.
+  constexpr int kScanChunks = 4;
   int carry = 0;
-  for (int c = 0; c < num_seqs; c += kWave) {
-    const int s = c + lane;
-    int len = s < num_seqs ? context_lens[s] : 0;
-    len = min(max(len, 0), max_len);
-    const int own = SHARED ? max((len + kTile - 1) / kTile - sh.tiles, 0)
-                           : (len + kTile - 1) / kTile;
-    const int incl = wave_incl_scan(own) + carry;
-    if (s < num_seqs) {
-      cu[s + 1] = incl;
-      lens[s] = len;
+  for (int c0 = 0; c0 < num_seqs; c0 += kScanChunks * kWave) {
+    int len[kScanChunks], incl[kScanChunks];
+#pragma unroll
+    for (int b = 0; b < kScanChunks; ++b) {
+      const int s = c0 + b * kWave + lane;
+      len[b] = s < num_seqs ? context_lens[s] : 0;
     }
-    carry = __shfl(incl, kWave - 1);
-    if (!SHARED && j == 0) {
-      uint64_t zero = __ballot(s < num_seqs && len == 0);
-      while (zero) {
-        const int zs = c + __builtin_ctzll(zero);
-        zero &= zero - 1;
-        uint16_t *op = out + ((int64_t)zs * num_heads + kvh * group) * D;
-        for (int e = lane * 4; e < group * D; e += kWave * 4) *(u32x2 *)(op + e) = u32x2{0, 0};
+#pragma unroll
+    for (int b = 0; b < kScanChunks; ++b) {
+      len[b] = min(max(len[b], 0), max_len);
+      const int own = SHARED ? max((len[b] + kTile - 1) / kTile - sh.tiles, 0)
+                             : (len[b] + kTile - 1) / kTile;
+      incl[b] = wave_incl_scan(own);
+    }
+#pragma unroll
+    for (int b = 0; b < kScanChunks; ++b) {
+      const int c = c0 + b * kWave;
+      const int s = c + lane;
+      const int total = __builtin_amdgcn_readlane(incl[b], kWave - 1);
+      if (s < num_seqs) {
+        cu[s + 1] = incl[b] + carry;
+        lens[s] = len[b];
+      }
+      carry += total;
+      if (!SHARED && j == 0) {
+        uint64_t zero = __ballot(s < num_seqs && len[b] == 0);
+        while (zero) {
+          const int zs = c + __builtin_ctzll(zero);
+          zero &= zero - 1;
+          uint16_t *op = out + ((int64_t)zs * num_heads + kvh * group) * D;
+          for (int e = lane * 4; e < group * D; e += kWave * 4) *(u32x2 *)(op + e) = u32x2{0, 0};
+        }
       }
     }
   }

@@ -200,6 +200,29 @@ def test_max_batch():
         check_close(c.decode(partition_tokens=pt), ref, w.dtype, f"max batch pt{pt}")
 
 
+@pytest.mark.parametrize("pt", [0, 16])
+def test_scan_chunks_with_empty_sequences(pt):
+    """600 sequences: the split pass reads their lengths 64 at a time in
+    groups of four chunks, so the tile prefix carries across lanes 63/64,
+    across chunks and across the 256-sequence group edge.  Empty sequences
+    sit on those edges, first and last."""
+    g = np.random.default_rng(17)
+    lens = g.integers(1, 60, size=600)
+    for s in (0, 63, 64, 127, 255, 256, 257, 511, 512, 599):
+        lens[s] = 0
+    w = W.build("scan", [max(int(L), 1) for L in lens], num_heads=4, num_kv_heads=2,
+                head_dim=64, block_size=16, dtype=W.F16, seed=321)
+    c = Case(w)
+    cl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    say(f"scan chunks pt={pt}")
+    got = c.decode(partition_tokens=pt, cl=cl)
+    kc, vc = oracle_caches(w)
+    ref = oracle.decode(w.q, kc, vc, w.block_tables, lens.astype(np.int32), w.scale, 16,
+                        w.dtype)
+    assert np.all(f64(got, w.dtype)[lens == 0] == 0)
+    check_close(got, ref, w.dtype, f"scan chunks pt{pt}")
+
+
 # ---- invariants -----------------------------------------------------------------------------
 
 def test_partition_size_invariance():
