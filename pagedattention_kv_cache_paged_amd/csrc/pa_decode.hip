@@ -520,19 +520,19 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // instead of the cache and stores them into the cache slot.
   // The lengths of kScanChunks chunks of 64 sequences are loaded together,
   // so that they cost one round trip, and their scans are independent until
-  // the chunks' totals are added in.
+  // the chunks' totals are added in.  The loads take no branch (lanes past
+  // the last sequence read its length again and drop it), which would make
+  // each of them wait for its own data.
   constexpr int kScanChunks = 4;
   int carry = 0;
   for (int c0 = 0; c0 < num_seqs; c0 += kScanChunks * kWave) {
     int len[kScanChunks], incl[kScanChunks];
 #pragma unroll
-    for (int b = 0; b < kScanChunks; ++b) {
-      const int s = c0 + b * kWave + lane;
-      len[b] = s < num_seqs ? context_lens[s] : 0;
-    }
+    for (int b = 0; b < kScanChunks; ++b)
+      len[b] = context_lens[min(c0 + b * kWave + lane, num_seqs - 1)];
 #pragma unroll
     for (int b = 0; b < kScanChunks; ++b) {
-      len[b] = min(max(len[b], 0), max_len);
+      len[b] = c0 + b * kWave + lane < num_seqs ? min(max(len[b], 0), max_len) : 0;
       const int own = SHARED ? max((len[b] + kTile - 1) / kTile - sh.tiles, 0)
                              : (len[b] + kTile - 1) / kTile;
       incl[b] = wave_incl_scan(own);
@@ -993,9 +993,13 @@ __global__ __launch_bounds__(kMergeHeads * kWave) void decode_merge_kernel(
   const int head = blockIdx.x * (int)(blockDim.x / kWave) + (int)(threadIdx.x / kWave);
   const int seq = blockIdx.y;
   const int lane = threadIdx.x % kWave;
-  if (head >= num_heads) return;
+  // The three tile-prefix entries go out together, before any branch: each
+  // is a round trip to memory that the split pass wrote, and a test that
+  // needs all three (c1 <= n_tiles always holds) keeps the compiler from
+  // moving one of them behind the wait for the others.
   const int n_tiles = ws_cu[num_seqs];
   const int c0 = ws_cu[seq], c1 = ws_cu[seq + 1];
+  if (head >= num_heads || c1 > n_tiles) return;
   int np = 0, jf = 0;
   if (c1 > c0) {
     const int wv = min(waves, n_tiles);  // as in the split pass: all ranges non-empty
