@@ -465,8 +465,10 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
     float scale_log2, float out_scale, float k_inv, float v_inv, int num_seqs,
-    int num_kv_heads, int num_heads, int group, int max_blocks, int64_t num_blocks,
-    int waves, int slots, SharedPrefix sh) {
+    int num_kv_heads, int num_heads, int group, int max_blocks, int waves, int slots,
+    int64_t num_blocks, SharedPrefix sh) {
+  // (waves sits next to the other sizes, in the argument line that the first
+  // scalar loads fetch: it is needed right after the length scan)
   using E = Elem<DT>;
   // P.V over E4M3 caches in binary16 (every code value is one; weights
   // keep 11 significant bits), otherwise in the caches' type
@@ -525,7 +527,8 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // each of them wait for its own data.
   constexpr int kScanChunks = 4;
   int carry = 0;
-  for (int c0 = 0; c0 < num_seqs; c0 += kScanChunks * kWave) {
+  int c0 = 0;
+  do {  // num_seqs >= 1: no test before the first group's loads
     int len[kScanChunks], incl[kScanChunks];
 #pragma unroll
     for (int b = 0; b < kScanChunks; ++b)
@@ -557,7 +560,8 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
         }
       }
     }
-  }
+    c0 += kScanChunks * kWave;
+  } while (c0 < num_seqs);
   if (lane == 0) cu[0] = 0;
   __syncthreads();
   const int n_tiles = __builtin_amdgcn_readfirstlane(carry);  // uniform: scalar loop control
@@ -1059,6 +1063,7 @@ int launch_typed(const DecodeArgs &a) {
   const int group = a.num_heads / a.num_kv_heads;
   const bool shared = a.sh.tiles > 0;
   hipError_t e = hipSuccess;
+  if (a.num_seqs < 1) return (int)hipErrorInvalidValue;  // the split pass reads lengths[0]
   if (a.stages & 1) {
     dim3 grid((unsigned)a.num_kv_heads * (unsigned)(a.waves + (shared ? a.sh.waves : 0)));
     // LDS: tile prefix and lengths, query fragments, and for the fused
@@ -1071,8 +1076,8 @@ int launch_typed(const DecodeArgs &a) {
       (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, (const uint16_t *)a.q, (void *)a.k_cache,  \
       (void *)a.v_cache, a.block_tables, a.context_lens, (const uint16_t *)a.k_new,           \
       (const uint16_t *)a.v_new, scale_log2, OUT_SCALE, a.k_inv, a.v_inv, a.num_seqs,         \
-      a.num_kv_heads, a.num_heads, group, a.max_blocks_per_seq, a.num_blocks, a.waves,        \
-      a.slots, a.sh)
+      a.num_kv_heads, a.num_heads, group, a.max_blocks_per_seq, a.waves, a.slots,             \
+      a.num_blocks, a.sh)
 #define PA_SPLIT_SH(KV8, APPEND, OUT_SCALE)                                                   \
   do {                                                                                        \
     if (shared) PA_SPLIT(KV8, APPEND, true, OUT_SCALE);                                       \
