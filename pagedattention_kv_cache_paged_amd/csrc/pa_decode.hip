@@ -788,15 +788,24 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
           f.k[h] = *(const u32x4 *)(kn_lds + (KV8 ? 64 * h + 16 * grp : 32 * h + 8 * grp));
       }
       if (grp == (r >> 2)) {
+        // all eight reads first, then selects: a branch per fragment on the
+        // (uniform) position e made each read wait for its own LDS round trip
+        uint32_t x[DTILES];
 #pragma unroll
-        for (int dt = 0; dt < DTILES; ++dt) {
-          const uint32_t x = vn_lds[vdim<KV8>(dt, row)];
-          if constexpr (KV8) {
-            f.v[dt] = (f.v[dt] & ~(0xffu << (8 * e))) | (x << (8 * e));
-          } else if (e >> 1) {
-            f.v[dt].y = (e & 1) ? ((f.v[dt].y & 0xffffu) | (x << 16)) : ((f.v[dt].y & 0xffff0000u) | x);
-          } else {
-            f.v[dt].x = (e & 1) ? ((f.v[dt].x & 0xffffu) | (x << 16)) : ((f.v[dt].x & 0xffff0000u) | x);
+        for (int dt = 0; dt < DTILES; ++dt) x[dt] = vn_lds[vdim<KV8>(dt, row)];
+        if constexpr (KV8) {
+          const uint32_t keep = ~(0xffu << (8 * e));
+#pragma unroll
+          for (int dt = 0; dt < DTILES; ++dt) f.v[dt] = (f.v[dt] & keep) | (x[dt] << (8 * e));
+        } else {
+          const int sh = 16 * (e & 1);
+          const uint32_t keep = ~(0xffffu << sh);
+          const bool upper = (e >> 1) != 0;  // token in the second dword of the fragment
+#pragma unroll
+          for (int dt = 0; dt < DTILES; ++dt) {
+            const uint32_t w = ((upper ? f.v[dt].y : f.v[dt].x) & keep) | (x[dt] << sh);
+            f.v[dt].x = upper ? f.v[dt].x : w;
+            f.v[dt].y = upper ? w : f.v[dt].y;
           }
         }
       }
