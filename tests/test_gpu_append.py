@@ -255,7 +255,9 @@ def test_append_fp8_named(name, make):
 
 @pytest.mark.parametrize("bs", [8, 32])
 def test_append_fp8_edges(bs):
-    lens = [0, 1, 17, 1, 300, 32, 0, 5]
+    # the new token at each of the four places in its 4-token V group, and on
+    # block and tile edges
+    lens = [0, 1, 17, 1, 300, 32, 0, 5, 2, 3, 4, 18, 19, 20, 31, 33]
     w = W.build("a8edges", [max(L, 1) for L in lens], num_heads=8, num_kv_heads=2,
                 head_dim=128, block_size=bs, dtype=W.BF16, seed=120 + bs,
                 max_blocks_per_seq=(320 + bs - 1) // bs)
