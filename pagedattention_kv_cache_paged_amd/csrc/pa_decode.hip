@@ -522,9 +522,9 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // instead of the cache and stores them into the cache slot.
   // The lengths of kScanChunks chunks of 64 sequences are loaded together,
   // so that they cost one round trip, and their scans are independent until
-  // the chunks' totals are added in.  The loads take no branch (lanes past
-  // the last sequence read its length again and drop it), which would make
-  // each of them wait for its own data.
+  // the chunks' totals are added in.  The loads take no branch: lanes past
+  // the last sequence read its length again and drop it (a branch around
+  // each load made each one wait for its own data).
   constexpr int kScanChunks = 4;
   int carry = 0;
   int c0 = 0;
@@ -788,7 +788,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
           f.k[h] = *(const u32x4 *)(kn_lds + (KV8 ? 64 * h + 16 * grp : 32 * h + 8 * grp));
       }
       if (grp == (r >> 2)) {
-        // all eight reads first, then selects: a branch per fragment on the
+        // all reads first, then selects: a branch per fragment on the
         // (uniform) position e made each read wait for its own LDS round trip
         uint32_t x[DTILES];
 #pragma unroll
