@@ -494,6 +494,9 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   constexpr bool kKT = KV8 && D == 128;
   constexpr int kKTRow = 144;
   uint8_t *kt_lds = reinterpret_cast<uint8_t *>(q_lds + KSTEPS * kWave) + (APPEND ? 6 * D : 0);
+  // The partial result of the wavefront's first segment (group rows of D
+  // floats, then group (m, l) pairs), kept here until the tile loop is done.
+  float *stg = reinterpret_cast<float *>(kt_lds + (kKT ? 16 * kKTRow : 0));
 
   int bid = blockIdx.x;
   if constexpr (SHARED) {
@@ -649,6 +652,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // With APPEND the new token's K and V rows go the same way, PER elements
   // per lane.
   uint32_t knx[PER], vnx[PER];
+  int first_sq = -1;  // sequence of a first-segment partial waiting in LDS
   auto load_new = [&](int idx) {
     if constexpr (APPEND) {
       const int s = __builtin_amdgcn_readlane(sq, idx);
@@ -931,6 +935,17 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
               const u32x2 w = {E::pack(v[0] * inv, v[1] * inv), E::pack(v[2] * inv, v[3] * inv)};
               *(u32x2 *)(op + 16 * VG * g + 4 * c) = w;
             });
+        } else if ((ends & ((1ull << idx) - 1)) == 0) {
+          // The first segment continues a sequence from the previous
+          // wavefront.  Its partial waits in LDS and is stored after the tile
+          // loop: stored here, it would hold up this wavefront's next waits.
+          float *sp = stg + row * D + grp * 4 * VG;
+#pragma unroll
+          for (int g = 0; g < DTILES / VG; ++g)
+            row_values<D, KV8>(acc, g, [&](int c, f32x4 v) {
+              *(f32x4 *)(sp + 16 * VG * g + 4 * c) = v * inv;
+            });
+          if (grp == 0) *(f32x2 *)(stg + group * D + row * 2) = f32x2{m_ref, l_tot};
         } else {
           const int64_t slot = (int64_t)head * slots + j + sqn;
           float *op = ws_o + slot * D + grp * 4 * VG;
@@ -942,6 +957,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
           if (grp == 0) *(f32x2 *)(ws_ml + slot * 2) = f32x2{m_ref, l_tot};
         }
       }
+      if (!(mt & kWhole) && (ends & ((1ull << idx) - 1)) == 0) first_sq = sqn;
       m_ref = -INFINITY;
       thr = -INFINITY;
       l_run = 0.f;
@@ -979,6 +995,16 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
       if (t + b < cnt) step(f[b], t + b);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  if (first_sq >= 0) {  // the deferred partial, 16 bytes per lane and store
+    for (int e = lane * 4; e < group * D; e += kWave * 4) {
+      const int r = e / D;
+      *(f32x4 *)(ws_o + ((int64_t)(kvh * group + r) * slots + j + first_sq) * D + (e - r * D)) =
+          *(const f32x4 *)(stg + e);
+    }
+    if (lane < group)
+      *(f32x2 *)(ws_ml + ((int64_t)(kvh * group + lane) * slots + j + first_sq) * 2) =
+          *(const f32x2 *)(stg + group * D + lane * 2);
   }
 }
 
@@ -1079,7 +1105,8 @@ int launch_typed(const DecodeArgs &a) {
     // append the new rows (16-bit, plus E4M3 codes).
     const size_t lds = (size_t)((2 * a.num_seqs + 1 + 3) & ~3) * sizeof(int) +
                        (size_t)(D / 32) * kWave * 16 + (a.append ? 6 * D : 0) +
-                       (a.kv_fp8 && D == 128 ? 16 * 144 : 0);
+                       (a.kv_fp8 && D == 128 ? 16 * 144 : 0) +
+                       (size_t)group * (D + 2) * sizeof(float);
 #define PA_SPLIT(KV8, APPEND, SHARED, OUT_SCALE)                                               \
   decode_split_kernel<DT, D, BS, KV8, APPEND, SHARED><<<grid, kWave, lds, st>>>(               \
       (uint16_t *)a.out, a.ws_o, a.ws_ml, a.ws_cu, (const uint16_t *)a.q, (void *)a.k_cache,  \
