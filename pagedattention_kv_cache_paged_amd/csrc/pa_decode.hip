@@ -772,11 +772,10 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
     if (APPEND && (mt & kNew)) {
       // The new token (row r of the tile) comes from k_new / v_new, not
       // from its cache slot, which this wavefront now fills.  Lanes of A-row
-      // r hold the token's K pieces; lanes of quarter r / 4 hold element
-      // r % 4 of each V^T fragment.  E4M3 caches: the wave first quantises
-      // the rows, PER elements per lane (the lane's own LDS writes).
+      // r hold the token's K pieces (its V follows after the QK MFMAs).
+      // E4M3 caches: the wave first quantises the rows, PER elements per lane
+      // (the lane's own LDS writes).
       const int r = n - 1;
-      const int e = r & 3;
       if constexpr (KV8) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -791,6 +790,31 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
         for (int h = 0; h < (KV8 ? D / 64 : KSTEPS); ++h)
           f.k[h] = *(const u32x4 *)(kn_lds + (KV8 ? 64 * h + 16 * grp : 32 * h + 8 * grp));
       }
+    }
+    u32x4 qf[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = q_lds[ks * kWave + lane];
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4 kf;
+      if constexpr (KV8) {  // codes 8*(ks%2) .. +8 of the 16 loaded for ks/2
+        const u32x4 c = f.k[ks / 2];
+        const u32x2 a = E::from_e4m3(ks % 2 ? c.z : c.x);
+        const u32x2 b = E::from_e4m3(ks % 2 ? c.w : c.y);
+        kf = u32x4{a.x, a.y, b.x, b.y};
+      } else {
+        kf = f.k[ks];
+      }
+      sc = E::qk(kf, qf[ks], sc);
+    }
+    if (APPEND && (mt & kNew)) {
+      // V of the new token, and the stores, after the QK MFMAs are issued (as
+      // in any tile, V is first waited for here) and before the mask below
+      // zeroes the group's later positions, which go back as they were.
+      // Lanes of quarter r / 4 hold element r % 4 of each V^T fragment.
+      const int r = n - 1;
+      const int e = r & 3;
       if (grp == (r >> 2)) {
         // all reads first, then selects: a branch per fragment on the
         // (uniform) position e made each read wait for its own LDS round trip
@@ -842,23 +866,6 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
           }
         }
       }
-    }
-    u32x4 qf[KSTEPS];
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = q_lds[ks * kWave + lane];
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      u32x4 kf;
-      if constexpr (KV8) {  // codes 8*(ks%2) .. +8 of the 16 loaded for ks/2
-        const u32x4 c = f.k[ks / 2];
-        const u32x2 a = E::from_e4m3(ks % 2 ? c.z : c.x);
-        const u32x2 b = E::from_e4m3(ks % 2 ? c.w : c.y);
-        kf = u32x4{a.x, a.y, b.x, b.y};
-      } else {
-        kf = f.k[ks];
-      }
-      sc = E::qk(kf, qf[ks], sc);
     }
     // raw scores; the scale (> 0, log2 units) joins in the exponent's FMA
     float s[4];
