@@ -480,7 +480,8 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
   // LDS: cu[num_seqs + 1], lens[num_seqs], then (16-byte aligned) the
   // current segment's query fragments, lane-major per k-step; with APPEND
   // also the new token's K and V rows of the current segment's sequence
-  // (16-bit), and for KV8 their E4M3 codes.
+  // (16-bit), and for KV8 their E4M3 codes; for KV8 at D = 128 one tile's K
+  // codes; last, the first segment's partial result.
   extern __shared__ __align__(16) int lds[];
   int *cu = lds;
   int *lens = lds + num_seqs + 1;
@@ -942,7 +943,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(
               const u32x2 w = {E::pack(v[0] * inv, v[1] * inv), E::pack(v[2] * inv, v[3] * inv)};
               *(u32x2 *)(op + 16 * VG * g + 4 * c) = w;
             });
-        } else if ((ends & ((1ull << idx) - 1)) == 0) {
+        } else if ((ends & ((1ull << idx) - 1)) == 0) {  // no earlier segment end
           // The first segment continues a sequence from the previous
           // wavefront.  Its partial waits in LDS and is stored after the tile
           // loop: stored here, it would hold up this wavefront's next waits.
@@ -1108,8 +1109,9 @@ int launch_typed(const DecodeArgs &a) {
   if (a.num_seqs < 1) return (int)hipErrorInvalidValue;  // the split pass reads lengths[0]
   if (a.stages & 1) {
     dim3 grid((unsigned)a.num_kv_heads * (unsigned)(a.waves + (shared ? a.sh.waves : 0)));
-    // LDS: tile prefix and lengths, query fragments, and for the fused
-    // append the new rows (16-bit, plus E4M3 codes).
+    // LDS: tile prefix and lengths, query fragments, for the fused append
+    // the new rows (16-bit, plus E4M3 codes), for E4M3 at D = 128 one K
+    // tile, and the first segment's partial (group x (D + 2) floats).
     const size_t lds = (size_t)((2 * a.num_seqs + 1 + 3) & ~3) * sizeof(int) +
                        (size_t)(D / 32) * kWave * 16 + (a.append ? 6 * D : 0) +
                        (a.kv_fp8 && D == 128 ? 16 * 144 : 0) +
