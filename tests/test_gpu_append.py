@@ -268,3 +268,21 @@ def test_append_fp8_edges(bs):
     assert np.all(f64(got, w.dtype)[cl == 0] == 0)
     ref = oracle.decode_fp8(w.q, rk, rv, w.block_tables, cl, w.scale, bs, w.dtype, KS, VS)
     check_close(got, ref, w.dtype, f"fp8 edges bs{bs}")
+
+
+def test_append_fp8_max_lds():
+    """The largest LDS request of the decode pass: 8192 sequences (lengths
+    and tile prefix), group 16 at head_dim 128 (the first segment's partial),
+    the new rows of the fused step and the E4M3 K tile.  Codes bit-exact,
+    every output row against the oracle."""
+    g = np.random.default_rng(9)
+    w = W.build("maxlds", g.integers(1, 25, size=8192), num_heads=32, num_kv_heads=2,
+                head_dim=128, block_size=16, dtype=W.BF16, seed=126)
+    say("append fp8 max LDS B=8192 G=16 D=128")
+    got, kc, vc = run_append(w, fp8=True)
+    rk, rv = oracle_state(w, fp8=True)
+    assert np.array_equal(kc, rk) and np.array_equal(vc, rv), "E4M3 caches differ"
+    rows = oracle.all_rows(w.num_seqs, w.num_heads)
+    ref = oracle.decode_fp8_rows(rows, w.q, rk, rv, w.block_tables, w.context_lens, w.scale,
+                                 w.block_size, w.dtype, KS, VS, threads=oracle.host_threads())
+    check_close(got, ref.reshape(got.shape), w.dtype, "fp8 max LDS")
