@@ -286,3 +286,20 @@ def test_append_fp8_max_lds():
     ref = oracle.decode_fp8_rows(rows, w.q, rk, rv, w.block_tables, w.context_lens, w.scale,
                                  w.block_size, w.dtype, KS, VS, threads=oracle.host_threads())
     check_close(got, ref.reshape(got.shape), w.dtype, "fp8 max LDS")
+
+
+def test_append_fp8_many_whole_sequences_per_wave():
+    """The fused step over E4M3 caches at group 16 and head_dim 128 where
+    most wavefronts finish several whole sequences (up to seven), each with
+    its new token: codes bit-exact, every output row against the oracle."""
+    g = np.random.default_rng(10)
+    w = W.build("wholea", g.integers(1, 41, size=2048), num_heads=32, num_kv_heads=2,
+                head_dim=128, block_size=16, dtype=W.BF16, seed=127)
+    say("append fp8 many whole sequences B=2048 G=16 D=128")
+    got, kc, vc = run_append(w, fp8=True)
+    rk, rv = oracle_state(w, fp8=True)
+    assert np.array_equal(kc, rk) and np.array_equal(vc, rv), "E4M3 caches differ"
+    rows = oracle.all_rows(w.num_seqs, w.num_heads)
+    ref = oracle.decode_fp8_rows(rows, w.q, rk, rv, w.block_tables, w.context_lens, w.scale,
+                                 w.block_size, w.dtype, KS, VS, threads=oracle.host_threads())
+    check_close(got, ref.reshape(got.shape), w.dtype, "fp8 whole seqs")

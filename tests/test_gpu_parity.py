@@ -200,6 +200,26 @@ def test_max_batch():
         check_close(c.decode(partition_tokens=pt), ref, w.dtype, f"max batch pt{pt}")
 
 
+@pytest.mark.parametrize("pt", [0, 32])
+def test_many_whole_sequences_per_wave(pt):
+    """2048 sequences of 1-40 tokens at group 16 and head_dim 128: by
+    default (512 wavefronts per KV head, about seven tiles each) most
+    wavefronts finish several whole sequences (up to seven) and store their
+    rows mid-loop; with 32-token partitions (3072 wavefronts per KV head)
+    most sequences are split and merged.  Every output row against the
+    oracle."""
+    g = np.random.default_rng(8)
+    w = W.build("whole", g.integers(1, 41, size=2048), num_heads=32, num_kv_heads=2,
+                head_dim=128, block_size=16, dtype=W.BF16, seed=125)
+    say(f"many whole sequences pt={pt}")
+    got = Case(w).decode(partition_tokens=pt)
+    kc, vc = oracle_caches(w)
+    rows = oracle.all_rows(w.num_seqs, w.num_heads)
+    ref = oracle.decode_rows(rows, w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                             w.block_size, w.dtype, threads=oracle.host_threads())
+    check_close(got, ref.reshape(got.shape), w.dtype, f"whole seqs pt{pt}")
+
+
 @pytest.mark.parametrize("pt", [0, 16])
 def test_scan_chunks_with_empty_sequences(pt):
     """600 sequences: the split pass reads their lengths 64 at a time in
