@@ -13,7 +13,9 @@ all its blocks by reference), so the next append of either copies their
 shared, partly filled last block first (pool copy-on-write plus
 paged_copy_blocks).  After every step both caches equal the oracle's bit
 for bit, and every output row is within |gpu - oracle| <= 2e-3 + 1e-2 *
-|oracle| of the oracle's attention over the same block tables.
+|oracle| of the oracle's attention over the same block tables.  Run over
+16-bit caches and over E4M3 caches (quantising writes, the E4M3 prefill
+and decode).
 """
 import numpy as np
 import pytest
@@ -29,6 +31,7 @@ DEV = "cuda:0"
 ATOL, RTOL = 2e-3, 1e-2
 HKV, HQ, D, BS, NB, MAXB = 4, 16, 128, 16, 160, 24
 DT, TDT = W.BF16, torch.bfloat16
+KS, VS = 0.02, 0.03
 
 
 def say(msg):
@@ -61,7 +64,12 @@ def table_array(tables):
     return bt
 
 
-def test_serving_loop_with_fork_and_copy_on_write():
+def cache_bits(t):
+    return t.cpu().numpy() if t.dtype == torch.uint8 else host_bits(t)
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "e4m3"])
+def test_serving_loop_with_fork_and_copy_on_write(fp8):
     g = np.random.default_rng(51)
     pool = B.BlockPool(NB, order=g.permutation(NB))
     lens = [int(x) for x in g.integers(5, 120, size=6)]
@@ -71,29 +79,52 @@ def test_serving_loop_with_fork_and_copy_on_write():
     scale = 1.0 / np.sqrt(D)
 
     # caches: NaN in every slot, on the device and in the oracle
-    nan = W.NAN_BITS[DT]
-    kh = np.full((NB, HKV, BS, D), nan, np.uint16)
-    vh = np.full((NB, HKV, BS // 4, D, 4), nan, np.uint16)
-    kc, vc = dev_bits(kh), dev_bits(vh)
+    if fp8:
+        kh = np.full((NB, HKV, BS, D), W.FP8_NAN, np.uint8)
+        vh = np.full((NB, HKV, BS // 4, D, 4), W.FP8_NAN, np.uint8)
+        kc, vc = torch.from_numpy(kh).to(DEV), torch.from_numpy(vh).to(DEV)
+    else:
+        kh = np.full((NB, HKV, BS, D), W.NAN_BITS[DT], np.uint16)
+        vh = np.full((NB, HKV, BS // 4, D, 4), W.NAN_BITS[DT], np.uint16)
+        kc, vc = dev_bits(kh), dev_bits(vh)
+
+    def write(k, v, sl):  # the same tokens into both sides
+        if fp8:
+            oracle.kv_write_fp8(k, v, sl, kh, vh, BS, DT, KS, VS)
+            B.paged_kv_write_fp8(dev_bits(k), dev_bits(v), torch.from_numpy(sl).to(DEV), kc, vc,
+                                 KS, VS)
+        else:
+            oracle.kv_write(k, v, sl, kh, vh, BS)
+            B.paged_kv_write(dev_bits(k), dev_bits(v), torch.from_numpy(sl).to(DEV), kc, vc)
+
+    def attend(q, bt, cl):
+        if fp8:
+            return oracle.decode_fp8(q, kh, vh, bt, cl, scale, BS, DT, KS, VS)
+        return oracle.decode(q, kh, vh, bt, cl, scale, BS, DT)
+
+    fs = dict(k_scale=KS, v_scale=VS) if fp8 else {}
 
     # prompts: written, then prefilled as one chunk per sequence
     slots = np.array([tables[s][p // BS] * BS + p % BS for s, L in enumerate(lens)
                       for p in range(L)], np.int64)
     pk = W.normal_bits(g, (slots.size, HKV, D), DT)
     pv = W.normal_bits(g, (slots.size, HKV, D), DT)
-    oracle.kv_write(pk, pv, slots, kh, vh, BS)
-    B.paged_kv_write(dev_bits(pk), dev_bits(pv), torch.from_numpy(slots).to(DEV), kc, vc)
+    write(pk, pv, slots)
     bt = table_array(tables)
     cl = np.array(lens, np.int32)
     qs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     qp = W.normal_bits(g, (int(qs[-1]), HQ, D), DT)
     outp = torch.empty((int(qs[-1]), HQ, D), dtype=TDT, device=DEV)
-    say("prefill of the prompts")
-    B.paged_attention_prefill(outp, dev_bits(qp), kc, vc, torch.from_numpy(bt).to(DEV),
-                              torch.from_numpy(cl).to(DEV), torch.from_numpy(qs).to(DEV),
-                              scale, BS, HKV, max(lens))
+    say(f"prefill of the prompts, fp8={fp8}")
+    pargs = (outp, dev_bits(qp), kc, vc, torch.from_numpy(bt).to(DEV),
+             torch.from_numpy(cl).to(DEV), torch.from_numpy(qs).to(DEV), scale)
+    if fp8:
+        B.paged_attention_prefill_fp8(*pargs, KS, VS, BS, HKV, max(lens))
+        ref = oracle.prefill_fp8(qp, kh, vh, bt, cl, qs, scale, BS, DT, KS, VS)
+    else:
+        B.paged_attention_prefill(*pargs, BS, HKV, max(lens))
+        ref = oracle.prefill(qp, kh, vh, bt, cl, qs, scale, BS, DT)
     torch.cuda.synchronize()
-    ref = oracle.prefill(qp, kh, vh, bt, cl, qs, scale, BS, DT)
     check_close(host_bits(outp), ref, "prefill")
 
     for step in range(6):
@@ -134,13 +165,15 @@ def test_serving_loop_with_fork_and_copy_on_write():
         say(f"decode step {step}: {n} sequences, lengths {lens}")
         B.paged_attention_decode_append(out, dev_bits(q), dev_bits(kn), dev_bits(vn), kc, vc,
                                         torch.from_numpy(bt).to(DEV),
-                                        torch.from_numpy(cl).to(DEV), scale, BS, HKV)
+                                        torch.from_numpy(cl).to(DEV), scale, BS, HKV, **fs)
         torch.cuda.synchronize()
-        oracle.kv_write(kn, vn, np.array(new_slots, np.int64), kh, vh, BS)
-        assert np.array_equal(host_bits(kc), kh), f"K cache, step {step}"
-        assert np.array_equal(host_bits(vc), vh), f"V cache, step {step}"
-        check_close(host_bits(out), oracle.decode(q, kh, vh, bt, cl, scale, BS, DT),
-                    f"step {step}")
+        if fp8:
+            oracle.kv_write_fp8(kn, vn, np.array(new_slots, np.int64), kh, vh, BS, DT, KS, VS)
+        else:
+            oracle.kv_write(kn, vn, np.array(new_slots, np.int64), kh, vh, BS)
+        assert np.array_equal(cache_bits(kc), kh), f"K cache, step {step}"
+        assert np.array_equal(cache_bits(vc), vh), f"V cache, step {step}"
+        check_close(host_bits(out), attend(q, bt, cl), f"step {step}")
 
     # the fork and its source still share their two full blocks; every other
     # block has one holder
