@@ -11,7 +11,10 @@ prompts are written with paged_kv_write and prefilled as one chunk each
 its last one is full; at step 2 sequence 0 forks (a second sequence holds
 all its blocks by reference), so the next append of either copies their
 shared, partly filled last block first (pool copy-on-write plus
-paged_copy_blocks).  After every step both caches equal the oracle's bit
+paged_copy_blocks); at step 3 sequence 3 is preempted (its blocks swapped
+out to a pinned host pool with paged_swap_blocks and released to the
+pool, where other sequences may take them) and at step 5 it resumes in
+freshly allocated blocks (swapped back in).  After every step both caches equal the oracle's bit
 for bit, and every output row is within |gpu - oracle| <= 2e-3 + 1e-2 *
 |oracle| of the oracle's attention over the same block tables.  Run over
 16-bit caches and over E4M3 caches (quantising writes, the E4M3 prefill
@@ -103,6 +106,13 @@ def test_serving_loop_with_fork_and_copy_on_write(fp8):
         return oracle.decode(q, kh, vh, bt, cl, scale, BS, DT)
 
     fs = dict(k_scale=KS, v_scale=VS) if fp8 else {}
+    # pinned host pool for swapped-out blocks, and the oracle's copy of it
+    NH = 16
+    hdt, ndt = (torch.uint8, np.uint8) if fp8 else (TDT, np.uint16)
+    hk_t = torch.zeros((NH, HKV, BS, D), dtype=hdt).pin_memory()
+    hv_t = torch.zeros((NH, HKV, BS // 4, D, 4), dtype=hdt).pin_memory()
+    hkh = np.zeros((NH, HKV, BS, D), ndt)
+    hvh = np.zeros((NH, HKV, BS // 4, D, 4), ndt)
 
     # prompts: written, then prefilled as one chunk per sequence
     slots = np.array([tables[s][p // BS] * BS + p % BS for s, L in enumerate(lens)
@@ -127,16 +137,34 @@ def test_serving_loop_with_fork_and_copy_on_write(fp8):
     torch.cuda.synchronize()
     check_close(host_bits(outp), ref, "prefill")
 
+    active = [True] * len(lens)
     for step in range(6):
         if step == 2:  # sequence 0 forks: the new sequence holds its blocks by reference
             for b in tables[0]:
                 pool.incref(b)
             tables.append(list(tables[0]))
             lens.append(lens[0])
+            active.append(True)
+        if step == 3:  # sequence 3 is preempted: its blocks go to the host pool
+            sp = np.array([(b, i) for i, b in enumerate(tables[3])], np.int64)
+            oracle.swap_blocks(sp, hkh, hvh, kh, vh, BS)
+            B.paged_swap_blocks(torch.from_numpy(sp).pin_memory(), hk_t, hv_t, kc, vc)
+            for b in tables[3]:
+                pool.decref(b)
+            active[3] = False
+        if step == 5:  # and resumes in fresh blocks
+            fresh = [pool.alloc() for _ in tables[3]]
+            assert all(b >= 0 for b in fresh)
+            sp = np.array([(i, b) for i, b in enumerate(fresh)], np.int64)
+            oracle.swap_blocks(sp, kh, vh, hkh, hvh, BS)
+            B.paged_swap_blocks(torch.from_numpy(sp).pin_memory(), kc, vc, hk_t, hv_t)
+            tables[3] = fresh
+            active[3] = True
+        run = [s for s in range(len(lens)) if active[s]]
         # position L of each sequence takes the new token: a new block when the
         # last one is full, else the last block, copied first if it is shared
         pairs, new_slots = [], []
-        for s in range(len(lens)):
+        for s in run:
             L = lens[s]
             if L % BS == 0:
                 b = pool.alloc()
@@ -155,14 +183,14 @@ def test_serving_loop_with_fork_and_copy_on_write(fp8):
             pa = np.array(pairs, np.int64)
             oracle.copy_blocks(pa, kh, vh, BS)
             B.paged_copy_blocks(torch.from_numpy(pa).to(DEV), kc, vc)
-        bt = table_array(tables)
-        cl = np.array(lens, np.int32)
-        n = len(lens)
+        bt = table_array([tables[s] for s in run])
+        cl = np.array([lens[s] for s in run], np.int32)
+        n = len(run)
         q = W.normal_bits(g, (n, HQ, D), DT)
         kn = W.normal_bits(g, (n, HKV, D), DT)
         vn = W.normal_bits(g, (n, HKV, D), DT)
         out = torch.empty((n, HQ, D), dtype=TDT, device=DEV)
-        say(f"decode step {step}: {n} sequences, lengths {lens}")
+        say(f"decode step {step}: sequences {run}, lengths {cl.tolist()}")
         B.paged_attention_decode_append(out, dev_bits(q), dev_bits(kn), dev_bits(vn), kc, vc,
                                         torch.from_numpy(bt).to(DEV),
                                         torch.from_numpy(cl).to(DEV), scale, BS, HKV, **fs)
